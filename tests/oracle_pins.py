@@ -1,0 +1,300 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each pin takes the oracle module as its argument and raises AssertionError
+when the module disagrees with the pages, a closed form, a library routine,
+finite differences or an invariant. The same pins run against copies of the
+oracle with planted mistakes, to show that a plausible slip fails one of them.
+No pin retypes an oracle formula.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import scipy.special as sps
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BETAS = (0.0, 0.1, 0.5, 0.9, 1.0)
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _logits(seed, R, V, scale=1.0):
+    return _rng(seed).standard_normal((R, V)) * scale
+
+
+def _h(beta):
+    """Binary entropy in nats: the value of JSD_beta at disjoint supports."""
+    return -beta * math.log(beta) - (1 - beta) * math.log(1 - beta)
+
+
+def pin_log_softmax_library(o):
+    """log_softmax equals scipy's routine, also at large offsets; shift invariant."""
+    a = _logits(1, 5, 37, 3.0) + 800.0      # exp(800) overflows without a max shift
+    ref = sps.log_softmax(a, axis=-1)
+    got = o.log_softmax(a)
+    assert np.all(np.isfinite(got)), "log_softmax overflowed"
+    assert np.allclose(got, ref, rtol=0, atol=1e-12), "log_softmax != scipy"
+    assert np.allclose(o.log_softmax(a - 1234.5), got, rtol=0, atol=1e-12), "not shift invariant"
+
+
+def pin_batchmean_scale_golden(o):
+    """PR #1374's tie table fixes batchmean = 1/rows."""
+    g = _golden("tvd_tie_batchmean.json")
+    rows, vocab = g["rows"], g["vocab"]
+    assert rows * vocab == g["elements"]
+    page_scale = g["gradient_at_tie_before_fix"] / g["per_element_slope_before_fix"]
+    assert abs(o.reduction_scale("batchmean", rows, vocab) - page_scale) < 1e-15
+    assert o.reduction_scale("sum", rows, vocab) == 1.0
+
+
+def pin_self_distillation_exact_zero(o):
+    """Student == teacher: loss exactly 0 and every gradient exactly 0 (PR #1374)."""
+    z = _logits(2, 6, 50, 2.0)
+    for beta in BETAS:
+        for T in (1.0, 2.0):
+            for red in ("batchmean", "sum", "mean"):
+                loss, grad = o.generalized_jsd(z, z.copy(), beta, T, red)
+                assert loss == 0.0, f"self loss {loss} at beta={beta}"
+                assert np.all(grad == 0.0), f"self grad nonzero at beta={beta}, T={T}"
+    X = _rng(3).standard_normal((5, 7))
+    W = _rng(4).standard_normal((11, 7)) * 0.3
+    for beta in BETAS:
+        loss, gX, gW = o.fused_linear_jsd(X, W, X.copy(), W.copy(), beta, 1.5, "batchmean", block_rows=2)
+        assert loss == 0.0 and np.all(gX == 0.0) and np.all(gW == 0.0), f"fused self beta={beta}"
+
+
+def pin_disjoint_support_closed_form(o):
+    """Disjoint supports give JSD_beta = h(beta) exactly (ln 2 at beta = 0.5)."""
+    V = 8
+    zs = np.full((2, V), -1e4)
+    zt = np.full((2, V), -1e4)
+    zs[0, 0] = 0.0
+    zt[0, 5] = 0.0
+    zs[1, :4] = 0.0      # uniform over the first half
+    zt[1, 4:] = 0.0      # uniform over the second half
+    for beta in (0.1, 0.5, 0.9):
+        loss, _ = o.generalized_jsd(zs, zt, beta, 1.0, "none")
+        assert np.allclose(loss, _h(beta), rtol=1e-12, atol=0), f"beta={beta}: {loss} vs {_h(beta)}"
+    loss, _ = o.generalized_jsd(zs, zt, 0.5, 1.0, "none")
+    assert np.allclose(loss, math.log(2.0), rtol=1e-12)
+
+
+def pin_bounds(o):
+    """0 <= JSD_beta <= h(beta) per row; JSD_0.5 <= ln 2."""
+    zs = _logits(5, 40, 30, 4.0)
+    zt = _logits(6, 40, 30, 4.0)
+    for beta in (0.1, 0.5, 0.9):
+        loss, _ = o.generalized_jsd(zs, zt, beta, 1.0, "none")
+        assert np.all(loss >= 0) and np.all(loss <= _h(beta) + 1e-12), f"bounds beta={beta}"
+
+
+def pin_role_swap(o):
+    """Swapping student and teacher maps beta to 1-beta (symmetric at 0.5)."""
+    zs = _logits(7, 4, 25, 2.0)
+    zt = _logits(8, 4, 25, 2.0)
+    for beta in (0.1, 0.3, 0.5):
+        a, _ = o.generalized_jsd(zs, zt, beta, 1.0, "none")
+        b, _ = o.generalized_jsd(zt, zs, 1.0 - beta, 1.0, "none")
+        assert np.allclose(a, b, rtol=1e-12, atol=1e-15), f"role swap beta={beta}"
+    a, _ = o.generalized_jsd(zs, zt, 0.5, 1.0, "sum")
+    b, _ = o.generalized_jsd(zt, zs, 0.5, 1.0, "sum")
+    assert abs(a - b) <= 1e-12 * abs(a)
+
+
+def _kl_rows(p, q):
+    return np.sum(sps.rel_entr(p, q), axis=-1)
+
+
+def pin_kl_endpoints_library(o):
+    """beta=0 is KL(teacher||student), beta=1 is KL(student||teacher) (PR #1352)."""
+    g = _golden("beta_branches.json")
+    kinds = {b["beta"]: b["kind"] for b in g["branches"]}
+    zs = _logits(9, 6, 33, 2.0)
+    zt = _logits(10, 6, 33, 2.0)
+    for T in (1.0, 3.0):
+        Q = sps.softmax(zs / T, axis=-1)
+        P = sps.softmax(zt / T, axis=-1)
+        assert kinds[0.0] == "forward_kl" and kinds[1.0] == "reverse_kl"
+        fwd, _ = o.generalized_jsd(zs, zt, 0.0, T, "none")
+        rev, _ = o.generalized_jsd(zs, zt, 1.0, T, "none")
+        assert np.allclose(fwd, _kl_rows(P, Q), rtol=1e-10, atol=1e-14), "beta=0 != KL(P||Q)"
+        assert np.allclose(rev, _kl_rows(Q, P), rtol=1e-10, atol=1e-14), "beta=1 != KL(Q||P)"
+
+
+def pin_kl_limits(o):
+    """JSD_b / b -> KL(P||Q) as b -> 0 and JSD_b / (1-b) -> KL(Q||P) as b -> 1."""
+    zs = _logits(11, 3, 20, 1.5)
+    zt = _logits(12, 3, 20, 1.5)
+    Q = sps.softmax(zs, axis=-1)
+    P = sps.softmax(zt, axis=-1)
+    eps = 1e-7
+    lo, _ = o.generalized_jsd(zs, zt, eps, 1.0, "none")
+    hi, _ = o.generalized_jsd(zs, zt, 1.0 - eps, 1.0, "none")
+    assert np.allclose(lo / eps, _kl_rows(P, Q), rtol=1e-5), "beta->0 limit"
+    assert np.allclose(hi / eps, _kl_rows(Q, P), rtol=1e-5), "beta->1 limit"
+
+
+def _fd_grad_logits(o, zs, zt, beta, T, red, h=1e-6):
+    g = np.zeros_like(zs)
+    for idx in np.ndindex(*zs.shape):
+        zp = zs.copy()
+        zm = zs.copy()
+        zp[idx] += h
+        zm[idx] -= h
+        lp, _ = o.generalized_jsd(zp, zt, beta, T, red)
+        lm, _ = o.generalized_jsd(zm, zt, beta, T, red)
+        g[idx] = (lp - lm) / (2 * h)
+    return g
+
+
+def pin_finite_differences_logits(o):
+    """Gradient w.r.t. student logits equals central differences of the loss."""
+    zs = _logits(13, 3, 9, 1.5)
+    zt = _logits(14, 3, 9, 1.5)
+    for beta in BETAS:
+        for T in (1.0, 2.0):
+            for red in ("batchmean", "sum", "mean"):
+                _, grad = o.generalized_jsd(zs, zt, beta, T, red)
+                fd = _fd_grad_logits(o, zs, zt, beta, T, red)
+                err = np.max(np.abs(grad - fd))
+                assert err <= 1e-7 * max(1.0, np.max(np.abs(fd))), \
+                    f"FD logits beta={beta} T={T} {red}: err {err}"
+
+
+def pin_finite_differences_fused(o):
+    """grad_input and grad_W equal central differences of the fused loss."""
+    rng = _rng(15)
+    BT, H, V = 3, 4, 7
+    X_s = rng.standard_normal((BT, H))
+    W_s = rng.standard_normal((V, H)) * 0.7
+    X_t = rng.standard_normal((BT, H + 1))
+    W_t = rng.standard_normal((V, H + 1)) * 0.7
+    h = 1e-6
+    for beta in (0.0, 0.5, 1.0):
+        for T in (1.0, 2.0):
+            _, gX, gW = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, T, "batchmean", block_rows=2)
+            for name, M, G in (("X_s", X_s, gX), ("W_s", W_s, gW)):
+                fd = np.zeros_like(M)
+                for idx in np.ndindex(*M.shape):
+                    Mp = M.copy()
+                    Mm = M.copy()
+                    Mp[idx] += h
+                    Mm[idx] -= h
+                    if name == "X_s":
+                        lp = o.fused_linear_jsd(Mp, W_s, X_t, W_t, beta, T, "batchmean")[0]
+                        lm = o.fused_linear_jsd(Mm, W_s, X_t, W_t, beta, T, "batchmean")[0]
+                    else:
+                        lp = o.fused_linear_jsd(X_s, Mp, X_t, W_t, beta, T, "batchmean")[0]
+                        lm = o.fused_linear_jsd(X_s, Mm, X_t, W_t, beta, T, "batchmean")[0]
+                    fd[idx] = (lp - lm) / (2 * h)
+                err = np.max(np.abs(G - fd))
+                assert err <= 1e-7 * max(1.0, np.max(np.abs(fd))), \
+                    f"FD {name} beta={beta} T={T}: err {err}"
+
+
+def pin_temperature_identity(o):
+    """loss(z, T) == loss(z/T, 1); grad(z, T) == grad(z/T, 1) / T."""
+    zs = _logits(16, 4, 21, 3.0)
+    zt = _logits(17, 4, 21, 3.0)
+    for beta in BETAS:
+        for T in (0.5, 2.0, 3.0):
+            la, ga = o.generalized_jsd(zs, zt, beta, T, "batchmean")
+            lb, gb = o.generalized_jsd(zs / T, zt / T, beta, 1.0, "batchmean")
+            assert abs(la - lb) <= 1e-12 * max(1.0, abs(lb)), f"T loss beta={beta} T={T}"
+            assert np.allclose(ga, gb / T, rtol=1e-10, atol=1e-15), f"T grad beta={beta} T={T}"
+
+
+def pin_gradient_rows_sum_to_zero(o):
+    """Softmax shift invariance: each row of the logit gradient sums to zero."""
+    zs = _logits(18, 5, 40, 2.0)
+    zt = _logits(19, 5, 40, 2.0)
+    for beta in BETAS:
+        _, g = o.generalized_jsd(zs, zt, beta, 1.7, "sum")
+        assert np.all(np.abs(g.sum(axis=-1)) <= 1e-14 * 40), f"row sums beta={beta}"
+
+
+def pin_block_invariance_and_reductions(o):
+    """Row blocking changes nothing; none/sum/mean/batchmean scale consistently."""
+    rng = _rng(20)
+    BT, H, V = 7, 5, 13
+    X_s, X_t = rng.standard_normal((BT, H)), rng.standard_normal((BT, H))
+    W_s, W_t = rng.standard_normal((V, H)) * 0.5, rng.standard_normal((V, H)) * 0.5
+    for beta in (0.0, 0.4, 1.0):
+        ref = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.3, "batchmean", block_rows=BT)
+        for br in (1, 3):
+            got = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.3, "batchmean", block_rows=br)
+            for a, b in zip(got, ref):
+                assert np.allclose(a, b, rtol=1e-12, atol=1e-15), f"block_rows={br} beta={beta}"
+        l_none, gX_none, gW_none = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.3, "none", block_rows=3)
+        l_sum, gX_sum, gW_sum = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.3, "sum", block_rows=3)
+        l_mean, gX_mean, _ = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.3, "mean", block_rows=3)
+        assert l_none.shape == (BT,)
+        assert abs(l_none.sum() - l_sum) <= 1e-12 * abs(l_sum)
+        assert abs(ref[0] * BT - l_sum) <= 1e-12 * abs(l_sum)
+        assert abs(l_mean * BT * V - l_sum) <= 1e-12 * abs(l_sum)
+        assert np.allclose(gX_none, gX_sum, rtol=1e-13, atol=0)
+        assert np.allclose(gW_none, gW_sum, rtol=1e-13, atol=0)
+        assert np.allclose(gX_mean * BT * V, gX_sum, rtol=1e-12, atol=1e-15)
+        rows = [0, 4, 6]
+        lr, gXr = o.fused_linear_jsd_rows(X_s, W_s, X_t, W_t, rows, beta, 1.3, "batchmean")
+        assert np.allclose(lr, l_none[rows], rtol=1e-12, atol=1e-15)
+        assert np.allclose(gXr, ref[1][rows], rtol=1e-12, atol=1e-15)
+
+
+def pin_padded_slots_exact_zero(o):
+    """Slots with zero mass in both distributions get exactly zero gradient."""
+    rng = _rng(21)
+    BT, H, V, pad = 4, 6, 20, 5
+    X_s, X_t = rng.standard_normal((BT, H)), rng.standard_normal((BT, H))
+    W_s, W_t = rng.standard_normal((V, H)) * 0.5, rng.standard_normal((V, H)) * 0.5
+    for X in (X_s, X_t):
+        X[:, H - 1] = 1.0
+    for W in (W_s, W_t):
+        W[V - pad:, :] = 0.0
+        W[V - pad:, H - 1] = -9984.0
+    for beta in (0.5, 0.1):
+        _, gX, gW = o.fused_linear_jsd(X_s, W_s, X_t, W_t, beta, 1.0, "batchmean")
+        assert np.all(gW[V - pad:] == 0.0), f"padded grad_W rows beta={beta}"
+        zs, zt = X_s @ W_s.T, X_t @ W_t.T
+        _, g = o.generalized_jsd(zs, zt, beta, 1.0, "batchmean")
+        assert np.all(g[:, V - pad:] == 0.0), f"padded logit grads beta={beta}"
+
+
+ALL_PINS = [
+    pin_log_softmax_library,
+    pin_batchmean_scale_golden,
+    pin_self_distillation_exact_zero,
+    pin_disjoint_support_closed_form,
+    pin_bounds,
+    pin_role_swap,
+    pin_kl_endpoints_library,
+    pin_kl_limits,
+    pin_finite_differences_logits,
+    pin_finite_differences_fused,
+    pin_temperature_identity,
+    pin_gradient_rows_sum_to_zero,
+    pin_block_invariance_and_reductions,
+    pin_padded_slots_exact_zero,
+]
+
+
+def failing_pins(module):
+    """Names of the pins the module fails (any exception counts as a failure)."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(module)
+        except Exception:   # noqa: BLE001 - any failure marks the pin
+            failed.append(pin.__name__)
+    return failed
