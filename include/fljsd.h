@@ -1,0 +1,192 @@
+/*
+ * fljsd.h - C ABI of the fused-linear generalized Jensen-Shannon distillation
+ * pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Liger-Kernel PR #1352 "Fuse log-softmax into
+ * fused_linear_jsd kernel", Summary and Details; PR #1429 "write the
+ * weight-gradient product directly into grad_weight", Summary):
+ *
+ *   Z_s = X_s W_s^T,  Z_t = X_t W_t^T                 (lm_head products)
+ *   Q = softmax(Z_s / T),  P = softmax(Z_t / T)        (student, teacher)
+ *   JSD_beta = beta KL(P||M) + (1-beta) KL(Q||M),  M = beta P + (1-beta) Q
+ *     beta == 0 is forward KL(P||Q), beta == 1 is reverse KL(Q||P)
+ *     (PR #1352, Testing Done: the four beta branches)
+ *   loss = scale * sum over rows and vocabulary of the per-element terms
+ *   dZ_s = d loss / d Z_s  (log-softmax chain rule, 1/T factor, dX_sum term)
+ *   grad_X_s = dZ_s W_s,   grad_W_s = dZ_s^T X_s
+ *
+ * Temperature divides both logits once; there is no T^2 factor (PR #1352,
+ * Open question 2). Exact ties p == q contribute zero (PR #1374 "Fix TVD
+ * gradient at p == q", Summary). The teacher receives no gradient.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, row-major, in device memory, and 16-byte aligned.
+ *  - Floating-point inputs and outputs use `dtype` (FLJSD_F32 or FLJSD_BF16);
+ *    losses are always fp32. All logit-to-loss arithmetic is fp32; GEMMs
+ *    accumulate in fp32 and round once to `dtype`.
+ *  - The caller allocates and owns every buffer, including the workspace.
+ *    The library never allocates device memory, never synchronizes, and
+ *    enqueues work only on `stream` (a hipStream_t; NULL is the null stream).
+ *    Calls return as soon as the work is enqueued.
+ *  - Every argument is checked before anything is enqueued; on error the
+ *    call returns a negative code and leaves every output untouched.
+ *    fljsd_last_error() then describes the failure. NaN or Inf inside the
+ *    data is not checked and propagates.
+ *  - Calls on one stream are ordered. Concurrent calls on different streams
+ *    are safe when their workspaces and outputs do not overlap.
+ */
+#ifndef FLJSD_H
+#define FLJSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of inputs, logits, gradients and weights. */
+typedef enum fljsd_dtype {
+  FLJSD_F32 = 0,
+  FLJSD_BF16 = 1
+} fljsd_dtype;
+
+/* Reduction of the per-element loss terms; `scale` is what multiplies both
+ * the summed loss and the gradient. batchmean divides by the number of rows
+ * (PR #1374's tie table: -0.0625 = -0.5 * 1/8 at 8 rows).
+ *   BATCHMEAN: loss = sum / rows          scale = 1/rows
+ *   SUM:       loss = sum                 scale = 1
+ *   MEAN:      loss = sum / (rows * V)    scale = 1/(rows*V)
+ *   NONE:      loss[r] = row r's sum      scale = 1 (gradient as for SUM) */
+typedef enum fljsd_reduction {
+  FLJSD_BATCHMEAN = 0,
+  FLJSD_SUM = 1,
+  FLJSD_MEAN = 2,
+  FLJSD_NONE = 3
+} fljsd_reduction;
+
+/* Status codes. */
+#define FLJSD_OK 0
+#define FLJSD_EINVAL (-1)      /* null required pointer, size <= 0, beta outside [0,1],
+                                  temperature <= 0 or not finite, ld < V, num_chunks < 0 */
+#define FLJSD_EDTYPE (-2)      /* dtype or reduction value not in the enums */
+#define FLJSD_EWORKSPACE (-3)  /* workspace smaller than the plan needs */
+#define FLJSD_EALIGN (-4)      /* pointer not 16-byte aligned, or H_s / H_t not a multiple
+                                  of 8 elements (bf16) or 4 elements (fp32) */
+#define FLJSD_EHIP (-5)        /* a HIP call or kernel launch failed */
+#define FLJSD_EDEVICE (-6)     /* the current device is not a gfx950 GPU */
+
+/*
+ * fljsd_forward_backward - the whole fused-linear JSD pass, forward and
+ * backward (PR #1352 Details; PR #1429 Summary).
+ *
+ * Inputs (read only):
+ *   X_s [BT, H_s], W_s [V, H_s]   student hidden states and lm_head weight
+ *   X_t [BT, H_t], W_t [V, H_t]   teacher hidden states and lm_head weight
+ *   beta in [0, 1], temperature > 0, reduction (fljsd_reduction).
+ *   num_chunks >= 1: rows are processed in chunks of C = ceil(BT/num_chunks)
+ *     rows, exactly as asked (the last chunk may be shorter, and there may be
+ *     fewer than num_chunks chunks). num_chunks == 0: the library picks the
+ *     smallest count whose workspace fits in workspace_bytes
+ *     (fljsd_plan_num_chunks). Results do not depend on the chunk count
+ *     beyond rounding.
+ * Outputs (every element written; may be uninitialized on entry):
+ *   loss      fp32: 1 value, or BT values for FLJSD_NONE.
+ *   grad_X_s  [BT, H_s] in dtype, or NULL to skip the grad_input product.
+ *   grad_W_s  [V, H_s] in dtype, or NULL to skip the grad_weight product.
+ *             The first chunk overwrites it; later chunks add to it with one
+ *             fp32 add and one rounding per chunk (PR #1429 Summary).
+ * Workspace: device scratch of at least
+ *   fljsd_workspace_size(BT, H_s, H_t, V, dtype, num_chunks) bytes (for
+ *   num_chunks == 0, at least the size for one chunk's worth of rows that
+ *   fits). It holds both logits chunks (the student chunk becomes dZ in
+ *   place, PR #1352 Details), per-row loss, row statistics and split-K
+ *   partial sums. Its contents on entry do not matter.
+ * Errors: FLJSD_EINVAL, FLJSD_EDTYPE, FLJSD_EALIGN, FLJSD_EWORKSPACE (all
+ *   before any work is enqueued), FLJSD_EDEVICE, FLJSD_EHIP.
+ */
+int fljsd_forward_backward(const void* X_s, const void* W_s,
+                           const void* X_t, const void* W_t,
+                           int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                           int dtype, float beta, float temperature,
+                           int reduction, int num_chunks,
+                           float* loss, void* grad_X_s, void* grad_W_s,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * fljsd_generalized_jsd - the loss step alone over given logits: the three
+ * online-softmax passes (PR #1352 Details: statistics m/d for both
+ * distributions; then loss and dX_sum; then dX), without the GEMMs.
+ *
+ *   logits_s, logits_t [BT, ld] in dtype, the first V columns used.
+ *   loss      fp32: 1 value, or BT values for FLJSD_NONE.
+ *   grad_logits_s [BT, ld] in dtype, or NULL for the loss only. It receives
+ *             d loss / d logits_s, including 1/T and the reduction scale. It
+ *             may equal logits_s (in place: the student logits are
+ *             overwritten by their gradient); any other overlap is an error
+ *             the library does not detect.
+ *   Columns V..ld-1 are neither read nor written. Any ld >= V works; rows
+ *             whose stride is a multiple of 16 bytes take the vector path.
+ * Workspace: at least fljsd_generalized_jsd_workspace_size(BT, V, dtype).
+ */
+int fljsd_generalized_jsd(const void* logits_s, const void* logits_t,
+                          int64_t BT, int64_t V, int64_t ld, int dtype,
+                          float beta, float temperature, int reduction,
+                          float* loss, void* grad_logits_s,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes fljsd_forward_backward needs for this shape with
+ * num_chunks >= 1 chunks. Pure host arithmetic; no device is touched.
+ * Returns 0 for invalid arguments (sizes <= 0, num_chunks < 1, bad dtype). */
+size_t fljsd_workspace_size(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                            int dtype, int num_chunks);
+
+/* Workspace bytes fljsd_generalized_jsd needs. Pure host arithmetic. */
+size_t fljsd_generalized_jsd_workspace_size(int64_t BT, int64_t V, int dtype);
+
+/* Chunk policy (a replacement for the cdiv(V, H) heuristic that PR #1352,
+ * Open question 4, calls mis-tuned for JSD): the smallest num_chunks >= 1
+ * whose workspace fits in budget_bytes. Larger chunks keep the GEMMs
+ * compute-bound, and the pages' sweep shows speed rising with chunk size.
+ * Pure host arithmetic. Returns the count, or FLJSD_EINVAL for invalid sizes,
+ * or FLJSD_EWORKSPACE when even one-row chunks do not fit. */
+int fljsd_plan_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                          int dtype, size_t budget_bytes);
+
+/* Static description of a status code. */
+const char* fljsd_strerror(int code);
+
+/* Details of the calling thread's most recent failure ("" if none). */
+const char* fljsd_last_error(void);
+
+/*
+ * Kernel timing for measurement. While enabled, the library brackets every
+ * kernel launch with a pair of HIP events on the launch stream and adds the
+ * elapsed time, the launch count and the launch's algorithmic work to a
+ * per-kernel-class tally. fljsd_profile_read() waits for the recorded events
+ * and fills up to `n` classes (see FLJSD_KCLASS_*): total milliseconds,
+ * launches, algorithmic floating-point operations and algorithmic HBM bytes.
+ * Enabling clears the tally. Not thread safe; intended for a benchmark that
+ * drives one stream. Returns FLJSD_OK or FLJSD_EHIP.
+ */
+#define FLJSD_KCLASS_GEMM_LOGITS 0      /* Z = X W^T (student and teacher) */
+#define FLJSD_KCLASS_JSD_STATS 1        /* pass 1: row max / denominator */
+#define FLJSD_KCLASS_JSD_LOSS 2         /* pass 2: loss and dX_sum partials */
+#define FLJSD_KCLASS_JSD_GRAD 3         /* pass 3: dZ in place, row loss */
+#define FLJSD_KCLASS_GEMM_GRAD_INPUT 4  /* grad_X = dZ W_s */
+#define FLJSD_KCLASS_SPLITK_REDUCE 5    /* split-K partial sums -> grad_X */
+#define FLJSD_KCLASS_GEMM_GRAD_WEIGHT 6 /* grad_W (=|+=) dZ^T X_s */
+#define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss */
+#define FLJSD_KCLASS_COUNT 8
+
+int fljsd_profile_enable(int enable);
+int fljsd_profile_read(double* total_ms, int64_t* launches, double* flops,
+                       double* hbm_bytes, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLJSD_H */

@@ -1,0 +1,464 @@
+// C-ABI entry points: argument checks, planning, and the stream-ordered launch
+// sequence of the fused-linear JSD pass. See include/fljsd.h for the contract.
+//
+// Per chunk of C rows (Liger-Kernel PR #1352, Details; PR #1429, Summary):
+//   Z_s = X_s W_s^T, Z_t = X_t W_t^T             two logits GEMMs
+//   pass 1 / pass 2 / pass 3                      online-softmax JSD, dZ over Z_s
+//   grad_X_s[chunk] = dZ W_s                      (split-K when few output tiles)
+//   grad_W_s = dZ^T X_s[chunk]                    overwrite on chunk 0, else add
+// then one scalar reduction of the per-row losses.
+#include "fljsd.h"
+#include "kernels.h"
+#include "plan.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#define FLJSD_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace fljsd {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(FLJSD_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+double reduction_scale(int reduction, int64_t rows, int64_t V) {
+  switch (reduction) {
+    case FLJSD_BATCHMEAN: return 1.0 / static_cast<double>(rows);
+    case FLJSD_MEAN: return 1.0 / (static_cast<double>(rows) * static_cast<double>(V));
+    default: return 1.0;  // SUM, NONE
+  }
+}
+
+int mode_for(float beta) {
+  if (beta == 0.0f) return kModeForwardKL;
+  if (beta == 1.0f) return kModeReverseKL;
+  return kModeGeneralized;
+}
+
+// ---- device check (once per device) ---------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLJSD_EDEVICE, "device index out of range");
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail_hip(e, "hipGetDeviceProperties");
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_release);
+    if (state == 2) return fail(FLJSD_EDEVICE, std::string("device is ") + prop.gcnArchName);
+  }
+  return state == 1 ? FLJSD_OK : fail(FLJSD_EDEVICE, "device is not gfx950");
+}
+
+// ---- kernel timing ----------------------------------------------------------
+struct ProfRecord {
+  hipEvent_t start, stop;
+  int cls;
+  double flops, bytes;
+};
+
+struct Profiler {
+  bool enabled = false;
+  std::vector<hipEvent_t> pool;
+  size_t next = 0;
+  std::vector<ProfRecord> records;
+  double ms[FLJSD_KCLASS_COUNT] = {};
+  double flops[FLJSD_KCLASS_COUNT] = {};
+  double bytes[FLJSD_KCLASS_COUNT] = {};
+  int64_t launches[FLJSD_KCLASS_COUNT] = {};
+
+  void clear() {
+    records.clear();
+    next = 0;
+    for (int i = 0; i < FLJSD_KCLASS_COUNT; ++i) {
+      ms[i] = flops[i] = bytes[i] = 0.0;
+      launches[i] = 0;
+    }
+  }
+  hipError_t take(hipEvent_t* ev) {
+    if (next == pool.size()) {
+      hipEvent_t e;
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) return err;
+      pool.push_back(e);
+    }
+    *ev = pool[next++];
+    return hipSuccess;
+  }
+};
+
+Profiler g_prof;
+
+// Launch `f` on `s`, bracketed by timing events when profiling is on.
+template <class F>
+hipError_t timed(hipStream_t s, int cls, double flops, double bytes, F&& f) {
+  if (!g_prof.enabled) return f();
+  ProfRecord rec{};
+  rec.cls = cls;
+  rec.flops = flops;
+  rec.bytes = bytes;
+  hipError_t e = g_prof.take(&rec.start);
+  if (e == hipSuccess) e = g_prof.take(&rec.stop);
+  if (e == hipSuccess) e = hipEventRecord(rec.start, s);
+  if (e != hipSuccess) return e;
+  e = f();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(rec.stop, s);
+  if (e == hipSuccess) g_prof.records.push_back(rec);
+  return e;
+}
+
+hipError_t gemm(int dtype, const GemmArgs& g, hipStream_t s) {
+  return dtype == FLJSD_BF16 ? launch_gemm_bf16(g, s) : launch_gemm_f32(g, s);
+}
+
+double gemm_bytes(const GemmArgs& g, int es) {
+  const double in = (static_cast<double>(g.M) * g.K + static_cast<double>(g.N) * g.K) * es;
+  const double out_es = g.epilogue == kEpiPartialF32 ? 4.0 : es;
+  const double out = static_cast<double>(g.M) * g.N * out_es * (g.epilogue == kEpiAccumulate ? 2 : 1);
+  return in + out;
+}
+
+// Checks shared by both compute entry points.
+int check_common(int dtype, float beta, float temperature, int reduction) {
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
+  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
+    return fail(FLJSD_EDTYPE, "unknown reduction");
+  if (!(beta >= 0.0f && beta <= 1.0f)) return fail(FLJSD_EINVAL, "beta must be in [0, 1]");
+  if (!(temperature > 0.0f) || !std::isfinite(temperature))
+    return fail(FLJSD_EINVAL, "temperature must be finite and > 0");
+  return FLJSD_OK;
+}
+
+int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int es,
+                   hipStream_t s) {
+  const double row_bytes = static_cast<double>(ja.rows) * V * es;
+  hipError_t e = timed(s, FLJSD_KCLASS_JSD_STATS, 0.0, 2 * row_bytes,
+                       [&] { return launch_jsd_stats(ja, dtype, s); });
+  if (e != hipSuccess) return fail_hip(e, "launch jsd_stats");
+  e = timed(s, FLJSD_KCLASS_JSD_LOSS, 0.0, 2 * row_bytes,
+            [&] { return launch_jsd_loss(ja, dtype, s); });
+  if (e != hipSuccess) return fail_hip(e, "launch jsd_loss");
+  if (write_grad) {
+    e = timed(s, FLJSD_KCLASS_JSD_GRAD, 0.0, 3 * row_bytes,
+              [&] { return launch_jsd_grad(ja, dtype, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch jsd_grad");
+  } else {
+    e = launch_jsd_row_loss(ja, s);
+    if (e != hipSuccess) return fail_hip(e, "launch jsd_row_loss");
+  }
+  return FLJSD_OK;
+}
+
+}  // namespace
+}  // namespace fljsd
+
+using namespace fljsd;
+
+FLJSD_EXPORT size_t fljsd_workspace_size(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                                         int dtype, int num_chunks) {
+  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0 || num_chunks < 1) return 0;
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
+  return plan_chunks(BT, H_s, H_t, V, dtype, num_chunks).total;
+}
+
+FLJSD_EXPORT size_t fljsd_generalized_jsd_workspace_size(int64_t BT, int64_t V, int dtype) {
+  if (BT <= 0 || V <= 0) return 0;
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
+  return plan_jsd(BT, V).total;
+}
+
+FLJSD_EXPORT int fljsd_plan_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                                       int dtype, size_t budget_bytes) {
+  g_last_error.clear();
+  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0) return fail(FLJSD_EINVAL, "sizes must be > 0");
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
+  const int64_t nc = policy_num_chunks(BT, H_s, H_t, V, dtype, budget_bytes);
+  if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the budget");
+  if (nc > INT32_MAX) return fail(FLJSD_EINVAL, "chunk count overflows int");
+  return static_cast<int>(nc);
+}
+
+FLJSD_EXPORT const char* fljsd_strerror(int code) {
+  switch (code) {
+    case FLJSD_OK: return "success";
+    case FLJSD_EINVAL: return "invalid argument";
+    case FLJSD_EDTYPE: return "unsupported dtype or reduction";
+    case FLJSD_EWORKSPACE: return "workspace too small";
+    case FLJSD_EALIGN: return "misaligned pointer or leading dimension";
+    case FLJSD_EHIP: return "HIP runtime error";
+    case FLJSD_EDEVICE: return "device is not an MI355X (gfx950)";
+    default: return "unknown status code";
+  }
+}
+
+FLJSD_EXPORT const char* fljsd_last_error(void) { return g_last_error.c_str(); }
+
+FLJSD_EXPORT int fljsd_profile_enable(int enable) {
+  g_prof.enabled = enable != 0;
+  g_prof.clear();
+  return FLJSD_OK;
+}
+
+FLJSD_EXPORT int fljsd_profile_read(double* total_ms, int64_t* launches, double* flops,
+                                    double* hbm_bytes, int n) {
+  for (const ProfRecord& r : g_prof.records) {
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+    g_prof.ms[r.cls] += ms;
+    g_prof.flops[r.cls] += r.flops;
+    g_prof.bytes[r.cls] += r.bytes;
+    g_prof.launches[r.cls] += 1;
+  }
+  g_prof.records.clear();
+  g_prof.next = 0;
+  for (int i = 0; i < n && i < FLJSD_KCLASS_COUNT; ++i) {
+    if (total_ms) total_ms[i] = g_prof.ms[i];
+    if (launches) launches[i] = g_prof.launches[i];
+    if (flops) flops[i] = g_prof.flops[i];
+    if (hbm_bytes) hbm_bytes[i] = g_prof.bytes[i];
+  }
+  return FLJSD_OK;
+}
+
+FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const void* X_t,
+                                        const void* W_t, int64_t BT, int64_t H_s, int64_t H_t,
+                                        int64_t V, int dtype, float beta, float temperature,
+                                        int reduction, int num_chunks, float* loss,
+                                        void* grad_X_s, void* grad_W_s, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!X_s || !W_s || !X_t || !W_t || !loss)
+    return fail(FLJSD_EINVAL, "X_s, W_s, X_t, W_t and loss must not be NULL");
+  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0)
+    return fail(FLJSD_EINVAL, "BT, H_s, H_t and V must be > 0");
+  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
+  int rc = check_common(dtype, beta, temperature, reduction);
+  if (rc != FLJSD_OK) return rc;
+  if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
+  const int vec = dtype_vec(dtype);
+  const void* ptrs[] = {X_s, W_s, X_t, W_t, loss, grad_X_s, grad_W_s, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
+  if (H_s % vec != 0 || H_t % vec != 0)
+    return fail(FLJSD_EALIGN, "H_s and H_t must be multiples of 16 bytes of elements");
+
+  int64_t nc = num_chunks;
+  if (nc == 0) {
+    nc = policy_num_chunks(BT, H_s, H_t, V, dtype, workspace_bytes);
+    if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
+  }
+  const ChunkPlan plan = plan_chunks(BT, H_s, H_t, V, dtype, nc);
+  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
+  if (workspace_bytes < plan.total)
+    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
+  rc = check_device();
+  if (rc != FLJSD_OK) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int es = dtype_size(dtype);
+  char* ws = static_cast<char*>(workspace);
+  void* Zs = ws + plan.off_zs;
+  void* Zt = ws + plan.off_zt;
+  float* row_loss = reduction == FLJSD_NONE ? loss : reinterpret_cast<float*>(ws + plan.off_row_loss);
+  const double scale = reduction_scale(reduction, BT, V);
+  const bool write_grad = grad_X_s != nullptr || grad_W_s != nullptr;
+
+  JsdArgs ja;
+  ja.zs = Zs;
+  ja.zt = Zt;
+  ja.grad = Zs;  // dZ replaces the student logits in place
+  ja.ld = plan.ldz;
+  ja.vec_ok = true;  // ldz is a multiple of 8 elements
+  ja.V = V;
+  ja.slice_w = plan.slices.slice_w;
+  ja.S = plan.slices.S;
+  ja.k2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  ja.beta = beta;
+  ja.grad_scale = static_cast<float>(scale / static_cast<double>(temperature));
+  ja.mode = mode_for(beta);
+  ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
+  ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
+
+  const char* Xs = static_cast<const char*>(X_s);
+  const char* Xt = static_cast<const char*>(X_t);
+  for (int64_t ci = 0; ci < plan.n_chunks; ++ci) {
+    const int64_t r0 = ci * plan.C;
+    const int64_t rows = std::min(plan.C, BT - r0);
+
+    for (int who = 0; who < 2; ++who) {
+      GemmArgs g;
+      const int64_t H = who == 0 ? H_s : H_t;
+      g.A = (who == 0 ? Xs : Xt) + r0 * H * es;
+      g.B = who == 0 ? W_s : W_t;
+      g.C = who == 0 ? Zs : Zt;
+      g.M = rows;
+      g.N = V;
+      g.K = H;
+      g.lda = H;
+      g.ldb = H;
+      g.ldc = plan.ldz;
+      g.a_kcontig = true;
+      g.b_kcontig = true;
+      g.epilogue = kEpiStore;
+      g.splitk = 1;
+      g.k_per_split = H;
+      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_LOGITS, 2.0 * rows * V * H, gemm_bytes(g, es),
+                           [&] { return gemm(dtype, g, s); });
+      if (e != hipSuccess) return fail_hip(e, "launch logits GEMM");
+    }
+
+    ja.rows = rows;
+    ja.row_loss = row_loss + r0;
+    rc = run_jsd_passes(ja, dtype, write_grad, V, es, s);
+    if (rc != FLJSD_OK) return rc;
+
+    if (grad_X_s) {
+      GemmArgs g;
+      g.A = Zs;
+      g.B = W_s;
+      g.M = rows;
+      g.N = H_s;
+      g.K = V;
+      g.lda = plan.ldz;
+      g.ldb = H_s;
+      g.a_kcontig = true;
+      g.b_kcontig = false;
+      const bool split = dtype == FLJSD_BF16 && plan.splitk > 1;
+      char* gx = static_cast<char*>(grad_X_s) + r0 * H_s * es;
+      if (split) {
+        g.C = ws + plan.off_partial;
+        g.ldc = H_s;
+        g.epilogue = kEpiPartialF32;
+        g.splitk = plan.splitk;
+        g.k_per_split = plan.k_per_split;
+      } else {
+        g.C = gx;
+        g.ldc = H_s;
+        g.epilogue = kEpiStore;
+        g.splitk = 1;
+        g.k_per_split = V;
+      }
+      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_INPUT, 2.0 * rows * H_s * V,
+                           gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
+      if (e != hipSuccess) return fail_hip(e, "launch grad_input GEMM");
+      if (split) {
+        const double red_bytes = static_cast<double>(rows) * H_s * (4.0 * plan.splitk + es);
+        e = timed(s, FLJSD_KCLASS_SPLITK_REDUCE, 0.0, red_bytes, [&] {
+          return launch_splitk_reduce(static_cast<const float*>(g.C), plan.splitk, rows, H_s,
+                                      gx, H_s, dtype, s);
+        });
+        if (e != hipSuccess) return fail_hip(e, "launch split-K reduce");
+      }
+    }
+
+    if (grad_W_s) {
+      GemmArgs g;
+      g.A = Zs;                       // A(m=v, k=r) = dZ[r, v]
+      g.B = Xs + r0 * H_s * es;       // B(n=h, k=r) = X_s[r, h]
+      g.C = grad_W_s;
+      g.M = V;
+      g.N = H_s;
+      g.K = rows;
+      g.lda = plan.ldz;
+      g.ldb = H_s;
+      g.ldc = H_s;
+      g.a_kcontig = false;
+      g.b_kcontig = false;
+      g.epilogue = ci == 0 ? kEpiStore : kEpiAccumulate;
+      g.splitk = 1;
+      g.k_per_split = rows;
+      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H_s * V,
+                           gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
+      if (e != hipSuccess) return fail_hip(e, "launch grad_weight GEMM");
+    }
+  }
+
+  if (reduction != FLJSD_NONE) {
+    hipError_t e = timed(s, FLJSD_KCLASS_LOSS_REDUCE, 0.0, 4.0 * BT,
+                         [&] { return launch_loss_reduce(row_loss, BT, static_cast<float>(scale), loss, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
+  }
+  return FLJSD_OK;
+}
+
+FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_t, int64_t BT,
+                                       int64_t V, int64_t ld, int dtype, float beta,
+                                       float temperature, int reduction, float* loss,
+                                       void* grad_logits_s, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!logits_s || !logits_t || !loss)
+    return fail(FLJSD_EINVAL, "logits_s, logits_t and loss must not be NULL");
+  if (BT <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT and V must be > 0");
+  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
+  if (ld < V) return fail(FLJSD_EINVAL, "ld must be >= V");
+  int rc = check_common(dtype, beta, temperature, reduction);
+  if (rc != FLJSD_OK) return rc;
+  const void* ptrs[] = {logits_s, logits_t, loss, grad_logits_s, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
+  const JsdPlan plan = plan_jsd(BT, V);
+  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
+  if (workspace_bytes < plan.total)
+    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
+  rc = check_device();
+  if (rc != FLJSD_OK) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const double scale = reduction_scale(reduction, BT, V);
+  float* row_loss = reduction == FLJSD_NONE ? loss : reinterpret_cast<float*>(ws + plan.off_row_loss);
+
+  JsdArgs ja;
+  ja.zs = logits_s;
+  ja.zt = logits_t;
+  ja.grad = grad_logits_s;
+  ja.ld = ld;
+  ja.vec_ok = ld % dtype_vec(dtype) == 0;
+  ja.rows = BT;
+  ja.V = V;
+  ja.slice_w = plan.slices.slice_w;
+  ja.S = plan.slices.S;
+  ja.k2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
+  ja.beta = beta;
+  ja.grad_scale = static_cast<float>(scale / static_cast<double>(temperature));
+  ja.mode = mode_for(beta);
+  ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
+  ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
+  ja.row_loss = row_loss;
+  rc = run_jsd_passes(ja, dtype, grad_logits_s != nullptr, V, dtype_size(dtype), s);
+  if (rc != FLJSD_OK) return rc;
+  if (reduction != FLJSD_NONE) {
+    hipError_t e = timed(s, FLJSD_KCLASS_LOSS_REDUCE, 0.0, 4.0 * BT,
+                         [&] { return launch_loss_reduce(row_loss, BT, static_cast<float>(scale), loss, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
+  }
+  return FLJSD_OK;
+}

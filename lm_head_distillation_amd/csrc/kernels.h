@@ -1,0 +1,70 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace fljsd {
+
+// Which branch of the divergence a launch evaluates (PR #1352, Testing Done:
+// beta 0.0 is forward KL, 1.0 reverse KL, anything between generalized).
+enum JsdMode : int { kModeGeneralized = 0, kModeForwardKL = 1, kModeReverseKL = 2 };
+
+struct JsdArgs {
+  const void* zs = nullptr;     // student logits [rows, ld]
+  const void* zt = nullptr;     // teacher logits [rows, ld]
+  void* grad = nullptr;         // dZ destination [rows, ld]; may equal zs
+  int64_t ld = 0;
+  bool vec_ok = true;           // ld is a whole number of 16-byte vectors
+  int64_t rows = 0;
+  int64_t V = 0;
+  int64_t slice_w = 0;
+  int S = 1;
+  float k2 = 0.f;               // log2(e) / T: base-2 scaled logit factor
+  float beta = 0.f;
+  float grad_scale = 0.f;       // reduction scale / T
+  int mode = kModeGeneralized;
+  float4* stats = nullptr;      // [rows * S] partial (m_s, d_s, m_t, d_t), base 2
+  float2* lg = nullptr;         // [rows * S] partial (loss, dX_sum)
+  float* row_loss = nullptr;    // [rows] per-row loss out
+};
+
+// Loss passes. dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s);
+hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s);
+// Per-row loss only (no gradient written): merges the pass-2 partials.
+hipError_t launch_jsd_row_loss(const JsdArgs& a, hipStream_t s);
+// loss[0] = scale * sum(row_loss[0..n)), deterministic order.
+hipError_t launch_loss_reduce(const float* row_loss, int64_t n, float scale, float* loss,
+                              hipStream_t s);
+// out[m, n] (dtype, ld ldo) = sum over splits of part[split][m][n] (fp32, ld N).
+hipError_t launch_splitk_reduce(const float* part, int splits, int64_t M, int64_t N,
+                                void* out, int64_t ldo, int dtype, hipStream_t s);
+
+// GEMM operand layouts. An operand is "K-contiguous" when its reduction index
+// is the fastest-varying one in memory.
+enum GemmEpilogue : int {
+  kEpiStore = 0,        // C = A B, rounded once to the dtype
+  kEpiAccumulate = 1,   // C = C + A B, added in fp32 and rounded once
+  kEpiPartialF32 = 2,   // fp32 partial sum of one K-split at C + split * M * ldc
+};
+
+struct GemmArgs {
+  const void* A = nullptr;
+  const void* B = nullptr;
+  void* C = nullptr;
+  int64_t M = 0, N = 0, K = 0;
+  int64_t lda = 0, ldb = 0, ldc = 0;
+  bool a_kcontig = true;   // A(m,k) = A[m*lda + k]  else  A[k*lda + m]
+  bool b_kcontig = true;   // B(n,k) = B[n*ldb + k]  else  B[k*ldb + n]
+  int epilogue = kEpiStore;
+  int splitk = 1;
+  int64_t k_per_split = 0; // multiple of the K tile when splitk > 1
+};
+
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
+
+}  // namespace fljsd

@@ -1,0 +1,78 @@
+// Host-side planning for the fused-linear JSD pass: chunk geometry, the
+// V-slicing of the loss kernels, the split-K factor of the grad_input GEMM and
+// the workspace layout. Pure integer arithmetic; no HIP calls.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace fljsd {
+
+// Tile shape of the bf16 MFMA GEMMs (rows x columns of one workgroup's output).
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+constexpr int kGemmBK = 64;
+// Tile shape of the fp32 GEMMs.
+constexpr int kGemmF32BM = 64;
+constexpr int kGemmF32BN = 64;
+
+// The loss kernels' workgroup: 256 threads, 8 elements per thread per step.
+constexpr int kJsdThreads = 256;
+constexpr int kJsdVec = 8;
+// Aim for at least this many workgroups per loss-kernel launch.
+constexpr int64_t kJsdTargetBlocks = 2048;
+// Minimum elements of one row a loss workgroup covers when a row is split.
+constexpr int64_t kJsdMinSlice = 4096;
+// Aim for at least this many workgroups in the grad_input GEMM.
+constexpr int64_t kGemmTargetBlocks = 256;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline int dtype_size(int dtype) { return dtype == 0 ? 4 : 2; }
+// Elements per 16-byte vector for the dtype.
+inline int dtype_vec(int dtype) { return dtype == 0 ? 4 : 8; }
+
+struct SlicePlan {
+  int S = 1;             // slices per row
+  int64_t slice_w = 0;   // elements per slice, a multiple of kJsdVec
+};
+
+// Slices per row for `rows` rows of V columns: enough workgroups to fill the
+// chip when there are few rows, never slices narrower than kJsdMinSlice.
+SlicePlan plan_slices(int64_t rows, int64_t V);
+
+struct ChunkPlan {
+  int64_t BT = 0, H_s = 0, H_t = 0, V = 0;
+  int dtype = 0;
+  int64_t C = 0;          // rows per chunk
+  int64_t n_chunks = 0;   // chunks actually run: ceil(BT / C)
+  int64_t ldz = 0;        // row stride (elements) of the logits chunk buffers
+  SlicePlan slices;       // for C rows
+  int splitk = 1;         // split-K factor of grad_input = dZ W_s
+  int64_t k_per_split = 0;
+  // Workspace layout, byte offsets from the workspace base.
+  size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0,
+         off_partial = 0, total = 0;
+};
+
+// Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).
+ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
+                      int64_t num_chunks);
+
+// Split-K choice for an M x N output with K-dimension K on the bf16 GEMM.
+void plan_splitk(int64_t M, int64_t N, int64_t K, int* splitk, int64_t* k_per_split);
+
+struct JsdPlan {
+  SlicePlan slices;
+  size_t off_row_loss = 0, off_stats = 0, off_lg = 0, total = 0;
+};
+
+JsdPlan plan_jsd(int64_t BT, int64_t V);
+
+// Smallest num_chunks whose workspace fits the budget; 0 if none does.
+int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
+                          size_t budget);
+
+}  // namespace fljsd

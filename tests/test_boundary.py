@@ -1,0 +1,216 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, its
+pure-host planning functions compute what the header promises, and every
+invalid argument is rejected with its status code before any device work.
+
+Every call here carries at least one invalid argument (or is a pure host
+function), so no kernel can be reached even when a GPU is present.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fljsd.h")
+LIB = os.path.join(ROOT, "lm_head_distillation_amd", "libfljsd.so")
+
+OK, EINVAL, EDTYPE, EWORKSPACE, EALIGN, EHIP, EDEVICE = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = 0, 1
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced in these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fljsd_\w+)\s*\(", text, re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libfljsd.so is not built; run `python -m lm_head_distillation_amd.build`")
+    from lm_head_distillation_amd import fljsd
+    return fljsd.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fljsd_forward_backward", "fljsd_generalized_jsd", "fljsd_workspace_size",
+              "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
+              "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fljsd_\w+)", out))
+    for n in declared_functions():
+        assert n in exported, f"{n} declared but not exported"
+        getattr(lib, n)
+    # Nothing else with the prefix leaks out.
+    assert exported == set(declared_functions())
+
+
+def test_header_compiles_as_c():
+    src = ('#include "fljsd.h"\n'
+           'int (*fb)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
+           ' int64_t, int, float, float, int, int, float*, void*, void*, void*, size_t, void*)'
+           ' = fljsd_forward_backward;\n'
+           'int main(void){return fb == 0 && FLJSD_KCLASS_COUNT == 8;}\n')
+    res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-",
+                          "-I", os.path.join(ROOT, "include")], input=src, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+
+
+def test_strerror_and_last_error(lib):
+    for code in (OK, EINVAL, EDTYPE, EWORKSPACE, EALIGN, EHIP, EDEVICE):
+        assert lib.fljsd_strerror(code)
+    assert lib.fljsd_strerror(12345) == b"unknown status code"
+
+
+# ---- pure host planning ------------------------------------------------------------------
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+def a256(x):
+    return (x + 255) // 256 * 256
+
+
+def test_workspace_size_accounts_for_each_buffer(lib):
+    BT, H, V = 1000, 64, 1003
+    ldz = cdiv(V, 8) * 8
+    for dtype, es in ((F32, 4), (BF16, 2)):
+        for nc in (1, 3, 1000):
+            C = cdiv(BT, nc)
+            got = lib.fljsd_workspace_size(BT, H, H, V, dtype, nc)
+            logits = 2 * a256(C * ldz * es)
+            # logits chunks + per-row loss + (stats, partial sums) + optional split-K
+            assert got >= logits + a256(BT * 4) + a256(C * 16) + a256(C * 8)
+            assert got <= logits + a256(BT * 4) + 64 * (a256(C * 16) + a256(C * 8)) + 4096 * C * H * 4 + 4096
+
+
+def test_workspace_size_rejects_bad_arguments(lib):
+    assert lib.fljsd_workspace_size(0, 64, 64, 10, BF16, 1) == 0
+    assert lib.fljsd_workspace_size(8, 64, 64, 10, BF16, 0) == 0
+    assert lib.fljsd_workspace_size(8, 64, 64, 10, 7, 1) == 0
+    assert lib.fljsd_generalized_jsd_workspace_size(8, 0, BF16) == 0
+    assert lib.fljsd_generalized_jsd_workspace_size(8, 100, BF16) >= 8 * 4
+
+
+def test_large_shapes_workspace(lib):
+    # 8192 x 4096 x 128256 bf16 in one chunk: both logits chunks dominate.
+    one = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 1)
+    assert 2 * 8192 * 128256 * 2 <= one < 2 * 8192 * 128256 * 2 + 64 * 2**20
+    eight = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 8)
+    assert eight < one / 4
+
+
+def test_policy_smallest_count_that_fits(lib):
+    BT, H, V = 8192, 4096, 4096 * 31 + 1
+    sizes = {nc: lib.fljsd_workspace_size(BT, H, H, V, BF16, nc) for nc in (1, 2, 3, 8)}
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, sizes[1]) == 1
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, 10**15) == 1
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, sizes[1] - 1) == 2
+    nc = lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, sizes[3])
+    assert nc <= 3 and lib.fljsd_workspace_size(BT, H, H, V, BF16, nc) <= sizes[3]
+    assert lib.fljsd_workspace_size(BT, H, H, V, BF16, nc - 1) > sizes[3] if nc > 1 else True
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, 1000) == EWORKSPACE
+    assert lib.fljsd_plan_num_chunks(0, H, H, V, BF16, 10**12) == EINVAL
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, 5, 10**12) == EDTYPE
+
+
+# ---- argument checks before any device work --------------------------------------------
+
+def fb(lib, **over):
+    """A call to fljsd_forward_backward with fake pointers; callers always
+    override at least one argument to make it invalid."""
+    a = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
+             beta=0.5, T=1.0, reduction=0, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return lib.fljsd_forward_backward(a["X_s"], a["W_s"], a["X_t"], a["W_t"], a["BT"], a["H_s"],
+                                      a["H_t"], a["V"], a["dtype"], a["beta"], a["T"],
+                                      a["reduction"], a["nc"], a["loss"], a["gX"], a["gW"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(X_s=None), EINVAL), (dict(W_t=None), EINVAL), (dict(loss=None), EINVAL),
+    (dict(BT=0), EINVAL), (dict(V=-3), EINVAL), (dict(H_t=0), EINVAL),
+    (dict(beta=1.5), EINVAL), (dict(beta=-0.1), EINVAL), (dict(beta=float("nan")), EINVAL),
+    (dict(T=0.0), EINVAL), (dict(T=-1.0), EINVAL), (dict(T=float("inf")), EINVAL),
+    (dict(T=float("nan")), EINVAL), (dict(nc=-1), EINVAL),
+    (dict(dtype=2), EDTYPE), (dict(reduction=4), EDTYPE), (dict(reduction=-1), EDTYPE),
+    (dict(X_s=FAKE + 2), EALIGN), (dict(gW=FAKE + 8), EALIGN), (dict(ws=FAKE + 4), EALIGN),
+    (dict(H_s=60), EALIGN), (dict(dtype=F32, H_t=66), EALIGN),
+    (dict(ws_bytes=100), EWORKSPACE), (dict(nc=0, ws_bytes=100), EWORKSPACE),
+    (dict(ws=None), EINVAL),
+])
+def test_forward_backward_rejects(lib, over, code):
+    assert fb(lib, **over) == code
+    assert lib.fljsd_last_error()
+
+
+def jsd(lib, **over):
+    a = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
+             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return lib.fljsd_generalized_jsd(a["zs"], a["zt"], a["BT"], a["V"], a["ld"], a["dtype"],
+                                     a["beta"], a["T"], a["reduction"], a["loss"], a["grad"],
+                                     a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
+    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
+    (dict(grad=FAKE + 2), EALIGN), (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
+])
+def test_generalized_jsd_rejects(lib, over, code):
+    assert jsd(lib, **over) == code
+
+
+def test_profile_interface_without_work(lib):
+    n = 8
+    ms = (ctypes.c_double * n)()
+    launches = (ctypes.c_int64 * n)()
+    assert lib.fljsd_profile_enable(1) == OK
+    assert lib.fljsd_profile_read(ms, launches, None, None, n) == OK
+    assert all(x == 0 for x in launches)
+    assert lib.fljsd_profile_enable(0) == OK
+
+
+# ---- the Python binding ----------------------------------------------------------------
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    from lm_head_distillation_amd import fljsd
+    x = torch.zeros(4, 64)
+    w = torch.zeros(10, 64)
+    with pytest.raises(ValueError):
+        fljsd.fljsd_forward_backward(x, w, x, w, 0.5, 1.0)
+    with pytest.raises(ValueError):
+        fljsd.fljsd_generalized_jsd(w, w, 0.5, 1.0)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    code = ("import lm_head_distillation_amd.fljsd as f; f._LIB_PATH = '/nonexistent/libfljsd.so'\n"
+            "try:\n    f.load_library()\nexcept ImportError as e:\n    print('IMPORTERROR', e)\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert "IMPORTERROR" in res.stdout, res.stderr
+
+
+def test_product_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "lm_head_distillation_amd")
+    for dirpath, _dirs, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,256 @@
+"""GPU parity of the whole pass (fljsd_forward_backward) against the oracle.
+
+Workloads and seeds come from workloads.py. The oracle takes the same input
+bits widened to fp64 and keeps every intermediate in fp64; the GPU rounds the
+logits and dZ to the input dtype, which the bf16 tolerances cover.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import (TOL, assert_loss_close, assert_tensor_close, from_device, normwise,
+                            to_device, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lm_head_distillation_amd import fljsd
+    fljsd.load_library()
+    return fljsd
+
+
+@functools.lru_cache(maxsize=4)
+def _inputs(key, BT=None, V=None, H_s=None, H_t=None):
+    w = workloads.WORKLOADS[key]
+    return w, workloads.make_inputs(w, BT=BT, V=V, H_s=H_s, H_t=H_t)
+
+
+@functools.lru_cache(maxsize=8)
+def _oracle(key, beta, T, reduction, BT=None, V=None, H_s=None, H_t=None):
+    w, inp = _inputs(key, BT, V, H_s, H_t)
+    d = w.dtype
+    return oracle.fused_linear_jsd(to_f64(inp["X_s"], d), to_f64(inp["W_s"], d),
+                                   to_f64(inp["X_t"], d), to_f64(inp["W_t"], d),
+                                   beta, T, reduction)
+
+
+def _device_inputs(inp, dtype):
+    return tuple(to_device(inp[k], dtype) for k in ("X_s", "W_s", "X_t", "W_t"))
+
+
+def _run(fl, dev, beta, T, reduction, nc, **kw):
+    loss, gX, gW = fl.fljsd_forward_backward(*dev, beta, T, reduction, nc, **kw)
+    torch.cuda.synchronize()
+    return loss, gX, gW
+
+
+def _compare(dtype, got, ref):
+    loss, gX, gW = got
+    rl, rX, rW = ref
+    tol = TOL[dtype]
+    e0 = assert_loss_close(from_device(loss), rl, tol)
+    e1 = assert_tensor_close(from_device(gX), rX, tol, "grad_input")
+    e2 = assert_tensor_close(from_device(gW), rW, tol, "grad_weight")
+    print(f"loss rel {e0:.2e}  grad_input normwise {e1:.2e}  grad_weight normwise {e2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("T", [1.0, 2.0])
+@pytest.mark.parametrize("reduction", ["batchmean", "sum", "mean", "none"])
+@pytest.mark.parametrize("nc", [1, 3])
+def test_tiny_f32(fl, beta, T, reduction, nc):
+    """8 x 64 x 512 fp32 (the pages' (8, 512) tie-test shape) at the 1e-5 bar."""
+    w, inp = _inputs("tiny_f32")
+    got = _run(fl, _device_inputs(inp, "f32"), beta, T, reduction, nc)
+    _compare("f32", got, _oracle("tiny_f32", beta, T, reduction))
+
+
+@pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])
+@pytest.mark.parametrize("nc", [1, 4])
+def test_multiblock_tail(fl, beta, nc):
+    """64 x 256 x 40960 bf16: the pages' multi-block shape, partial trailing block."""
+    w, inp = _inputs("multiblock_tail")
+    got = _run(fl, _device_inputs(inp, "bf16"), beta, 1.0, "batchmean", nc)
+    _compare("bf16", got, _oracle("multiblock_tail", beta, 1.0, "batchmean"))
+
+
+def test_ties_self_distillation(fl):
+    """Teacher bit-identical to student: loss and every gradient element are 0."""
+    w, inp = _inputs("ties_self")
+    loss, gX, gW = _run(fl, _device_inputs(inp, "bf16"), w.beta, w.temperature, w.reduction, 1)
+    assert from_device(loss) == 0.0
+    assert torch.count_nonzero(gX).item() == 0
+    assert torch.count_nonzero(gW).item() == 0
+
+
+def test_ties_padded_vocabulary(fl):
+    """Padded vocabulary rows carry zero mass in both models: their grad_W rows
+    are exactly 0, and everything else matches the oracle."""
+    w, inp = _inputs("ties_padded")
+    got = _run(fl, _device_inputs(inp, "bf16"), w.beta, w.temperature, w.reduction, 1)
+    gW = from_device(got[2])
+    assert np.all(gW[-workloads.PAD_ROWS:] == 0.0)
+    _compare("bf16", got, _oracle("ties_padded", w.beta, w.temperature, w.reduction))
+
+
+@pytest.fixture(scope="module")
+def llama3_device():
+    w, inp = _inputs("llama3_head")
+    return w, _device_inputs(inp, "bf16")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("nc", [1, 8, 32])
+def test_llama3_head_full(fl, llama3_device, nc):
+    """1024 x 4096 x 128256 bf16 against the full oracle, per chunk count."""
+    w, dev = llama3_device
+    got = _run(fl, dev, w.beta, w.temperature, w.reduction, nc)
+    _compare("bf16", got, _oracle("llama3_head", w.beta, w.temperature, w.reduction))
+
+
+@pytest.fixture(scope="module")
+def large_batch():
+    w, inp = _inputs("large_batch")
+    return w, inp, _device_inputs(inp, "bf16")
+
+
+@pytest.mark.slow
+def test_large_batch_sampled_and_properties(fl, large_batch):
+    """8192 x 4096 x 128256 bf16, T = 2. Sampled rows (chunk edges included)
+    against the oracle one by one; grad_W through chunk-count invariance and the
+    identity <grad_W, W_s> = <dZ, Z_s> = <grad_X, X_s>."""
+    w, inp, dev = large_batch
+    d = w.dtype
+    rows = np.array([0, 1, 255, 256, 1023, 1024, 4097, 8191])
+    Xs = to_f64(inp["X_s"], d)
+    Ws = to_f64(inp["W_s"], d)
+    Xt = to_f64(inp["X_t"], d)
+    Wt = to_f64(inp["W_t"], d)
+    ref_rows_loss, ref_rows_gX = oracle.fused_linear_jsd_rows(Xs, Ws, Xt, Wt, rows, w.beta,
+                                                              w.temperature, w.reduction)
+    del Wt
+    results = {}
+    for nc in (1, 8, 32):
+        loss, gX, gW = _run(fl, dev, w.beta, w.temperature, w.reduction, nc)
+        results[nc] = (from_device(loss), from_device(gX[torch.as_tensor(rows, device=gX.device)]),
+                       gW)
+        # <grad_W, W_s> == <grad_X, X_s>, both in fp64 from the GPU outputs.
+        lhs = float((gW.double() * dev[1].double()).sum())
+        rhs = float((gX.double() * dev[0].double()).sum())
+        assert abs(lhs - rhs) <= 2e-2 * max(abs(lhs), abs(rhs)), f"nc={nc}: {lhs} vs {rhs}"
+        assert torch.isfinite(gW).all() and torch.isfinite(gX).all()
+        assert_tensor_close(results[nc][1], ref_rows_gX, TOL[d], f"grad_input rows nc={nc}")
+    loss_none, _, _ = _run(fl, dev, w.beta, w.temperature, "none", 1, grad_input=False,
+                           grad_weight=False)
+    row_losses = from_device(loss_none)
+    assert_loss_close(row_losses[rows], ref_rows_loss, TOL[d], "per-row loss")
+    for nc in (1, 8, 32):
+        assert_loss_close(results[nc][0], row_losses.mean(), {"loss_rel": 1e-5}, f"loss nc={nc}")
+    ref_gW = results[1][2].double()
+    for nc in (8, 32):
+        nw = float(torch.linalg.vector_norm(results[nc][2].double() - ref_gW) / torch.linalg.vector_norm(ref_gW))
+        assert nw <= TOL[d]["norm"], f"grad_W nc={nc} vs nc=1 normwise {nw:.3e}"
+
+
+# ---- edge cases -------------------------------------------------------------------------
+
+def _adhoc(seed, BT, H_s, H_t, V, dtype):
+    w = workloads.Workload("adhoc", seed, BT, H_s, H_t, V, dtype, 0.5, 1.0, "batchmean", "independent")
+    return workloads.make_inputs(w)
+
+
+def _oracle_of(inp, dtype, beta, T, reduction):
+    return oracle.fused_linear_jsd(*(to_f64(inp[k], dtype) for k in ("X_s", "W_s", "X_t", "W_t")),
+                                   beta, T, reduction)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("BT,H_s,H_t,V,nc", [
+    (1, 64, 64, 100, 1),          # one row
+    (300, 72, 72, 1000, 1),       # ragged M, N and K tiles
+    (300, 72, 72, 1000, 3),       # ragged chunks
+    (300, 72, 72, 1000, 7),
+    (64, 128, 256, 3000, 2),      # teacher hidden size differs
+    (10, 64, 64, 777, 100),       # more chunks asked than rows
+    (513, 264, 136, 5003, 2),     # odd everything
+])
+def test_shapes(fl, dtype, BT, H_s, H_t, V, nc):
+    inp = _adhoc(7, BT, H_s, H_t, V, dtype)
+    for beta, T in ((0.5, 1.0), (0.0, 2.0), (1.0, 1.5)):
+        got = _run(fl, _device_inputs(inp, dtype), beta, T, "batchmean", nc)
+        _compare(dtype, got, _oracle_of(inp, dtype, beta, T, "batchmean"))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_optional_gradients_and_determinism(fl, dtype):
+    inp = _adhoc(8, 200, 128, 128, 4000, dtype)
+    dev = _device_inputs(inp, dtype)
+    full = _run(fl, dev, 0.3, 1.0, "batchmean", 2)
+    again = _run(fl, dev, 0.3, 1.0, "batchmean", 2)
+    for a, b in zip(full, again):
+        assert torch.equal(a, b), "two identical calls differ"
+    only_x = _run(fl, dev, 0.3, 1.0, "batchmean", 2, grad_weight=False)
+    only_w = _run(fl, dev, 0.3, 1.0, "batchmean", 2, grad_input=False)
+    neither = _run(fl, dev, 0.3, 1.0, "batchmean", 2, grad_input=False, grad_weight=False)
+    assert only_x[2] is None and only_w[1] is None
+    assert torch.equal(only_x[1], full[1]) and torch.equal(only_w[2], full[2])
+    for r in (only_x, only_w, neither):
+        assert torch.equal(r[0], full[0])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reduction", ["sum", "mean", "none"])
+def test_reductions(fl, dtype, reduction):
+    inp = _adhoc(9, 96, 64, 64, 2500, dtype)
+    got = _run(fl, _device_inputs(inp, dtype), 0.7, 1.3, reduction, 3)
+    _compare(dtype, got, _oracle_of(inp, dtype, 0.7, 1.3, reduction))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_every_output_element_written(fl, dtype):
+    """Outputs prefilled with NaN come back finite: the first chunk overwrites
+    grad_W and the loop writes every element (PR #1429 Summary)."""
+    inp = _adhoc(10, 130, 64, 64, 1500, dtype)
+    dev = _device_inputs(inp, dtype)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    loss = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    gX = torch.full(dev[0].shape, float("nan"), dtype=tdt, device="cuda")
+    gW = torch.full(dev[1].shape, float("nan"), dtype=tdt, device="cuda")
+    _run(fl, dev, 0.5, 1.0, "batchmean", 4, out=(loss, gX, gW))
+    assert torch.isfinite(loss).all() and torch.isfinite(gX).all() and torch.isfinite(gW).all()
+    _compare(dtype, (loss[0], gX, gW), _oracle_of(inp, dtype, 0.5, 1.0, "batchmean"))
+
+
+def test_policy_picks_chunks_for_workspace(fl):
+    inp = _adhoc(11, 256, 64, 64, 3000, "bf16")
+    dev = _device_inputs(inp, "bf16")
+    need3 = fl.fljsd_workspace_size(256, 64, 64, 3000, fl.BF16, 3)
+    assert fl.fljsd_plan_num_chunks(256, 64, 64, 3000, fl.BF16, need3) == 3
+    ws = torch.empty(need3, dtype=torch.uint8, device="cuda")
+    auto = _run(fl, dev, 0.5, 1.0, "batchmean", 0, workspace=ws)
+    explicit = _run(fl, dev, 0.5, 1.0, "batchmean", 3)
+    for a, b in zip(auto, explicit):
+        assert torch.equal(a, b)
+
+
+def test_status_codes_on_device(fl):
+    inp = _adhoc(12, 16, 64, 64, 300, "bf16")
+    dev = _device_inputs(inp, "bf16")
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fl.FljsdError) as e:
+        fl.fljsd_forward_backward(*dev, 0.5, 1.0, "batchmean", 1, workspace=small)
+    assert e.value.code == -3
+    with pytest.raises(fl.FljsdError) as e:
+        fl.fljsd_forward_backward(*dev, 1.5, 1.0, "batchmean", 1)
+    assert e.value.code == -1

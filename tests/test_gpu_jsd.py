@@ -1,0 +1,137 @@
+"""GPU parity of the loss step alone (fljsd_generalized_jsd) against the oracle.
+
+Inputs are seeded logits drawn by workloads.py; the oracle sees the same
+values widened to fp64. Here the logits are exact on both sides, so the only
+differences are fp32 arithmetic and, for bf16, the rounding of the gradient
+on output; the bounds below are tighter than the pass-level ones.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import assert_loss_close, assert_tensor_close, from_device, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+# Loss: fp32 arithmetic on exact inputs. Gradient: one bf16 rounding (2^-8
+# relative) plus fp32 arithmetic.
+TIGHT = {
+    "f32": {"loss_rel": 1e-5, "norm": 1e-5, "elem_rel": 1e-5, "elem_max": 1e-5, "elem_abs": 0.0},
+    "bf16": {"loss_rel": 1e-5, "norm": 4e-3, "elem_rel": 2 ** -8, "elem_max": 1e-5, "elem_abs": 0.0},
+}
+
+
+@pytest.fixture(scope="module")
+def fl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lm_head_distillation_amd import fljsd
+    fljsd.load_library()
+    return fljsd
+
+
+def _logits(seed, BT, V, scale, dtype, ld=None):
+    a = workloads.make_logits(seed, BT, V, scale, dtype)
+    if ld is not None and ld != V:
+        pad = np.zeros((BT, ld), dtype=a.dtype)
+        pad[:, :V] = a
+        return a, pad
+    return a, a
+
+
+def _run(fl, zs_np, zt_np, V, dtype, beta, T, reduction, **kw):
+    zs = to_device(zs_np, dtype)
+    zt = to_device(zt_np, dtype)
+    if zs_np.shape[1] != V:
+        zs = zs[:, :V]
+        zt = zt[:, :V]
+    loss, grad = fl.fljsd_generalized_jsd(zs, zt, beta, T, reduction, **kw)
+    torch.cuda.synchronize()
+    return loss, grad, zs
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("T", [1.0, 2.0])
+@pytest.mark.parametrize("reduction", ["batchmean", "sum", "mean", "none"])
+def test_tiny_f32_all_branches(fl, beta, T, reduction):
+    zs, _ = _logits(11, 8, 512, 2.0, "f32")
+    zt, _ = _logits(12, 8, 512, 2.0, "f32")
+    loss, grad, _ = _run(fl, zs, zt, 512, "f32", beta, T, reduction)
+    ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, "f32"), to_f64(zt, "f32"), beta, T, reduction)
+    assert_loss_close(from_device(loss), ref_loss, TIGHT["f32"])
+    assert_tensor_close(from_device(grad), ref_grad, TIGHT["f32"], "grad")
+
+
+@pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])
+@pytest.mark.parametrize("V,ld", [(40960, 40960), (40997, 41000)])
+def test_multiblock_tail_bf16(fl, beta, V, ld):
+    """64 rows x 40960 columns (two 32768-wide blocks of the pages' kernel, the
+    second 8192 wide) and a width that leaves a ragged tail in our own slices."""
+    zs, zs_pad = _logits(21, 64, V, 2.0, "bf16", ld)
+    zt, zt_pad = _logits(22, 64, V, 2.0, "bf16", ld)
+    loss, grad, _ = _run(fl, zs_pad, zt_pad, V, "bf16", beta, 1.0, "batchmean")
+    ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, "bf16"), to_f64(zt, "bf16"), beta, 1.0, "batchmean")
+    assert_loss_close(from_device(loss), ref_loss, TIGHT["bf16"])
+    assert_tensor_close(from_device(grad), ref_grad, TIGHT["bf16"], "grad")
+
+
+@pytest.mark.parametrize("BT,V", [(4, 128256), (3000, 1000), (1, 7), (33, 4099)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_row_and_slice_shapes(fl, BT, V, dtype):
+    """Few wide rows (many slices per row), many narrow rows (one slice each),
+    and odd widths."""
+    zs, _ = _logits(31, BT, V, 3.0, dtype)
+    zt, _ = _logits(32, BT, V, 3.0, dtype)
+    for beta in (0.0, 0.5, 1.0):
+        loss, grad, _ = _run(fl, zs, zt, V, dtype, beta, 1.5, "sum")
+        ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, dtype), to_f64(zt, dtype), beta, 1.5, "sum")
+        assert_loss_close(from_device(loss), ref_loss, TIGHT[dtype])
+        assert_tensor_close(from_device(grad), ref_grad, TIGHT[dtype], f"grad beta={beta}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_in_place_matches_out_of_place_and_is_deterministic(fl, dtype):
+    zs, _ = _logits(41, 16, 20000, 2.0, dtype)
+    zt, _ = _logits(42, 16, 20000, 2.0, dtype)
+    loss_a, grad_a, _ = _run(fl, zs, zt, 20000, dtype, 0.3, 1.0, "batchmean")
+    loss_b, grad_b, _ = _run(fl, zs, zt, 20000, dtype, 0.3, 1.0, "batchmean")
+    loss_c, grad_c, zs_dev = _run(fl, zs, zt, 20000, dtype, 0.3, 1.0, "batchmean", in_place=True)
+    assert grad_c.data_ptr() == zs_dev.data_ptr()
+    assert torch.equal(grad_a, grad_b) and torch.equal(loss_a, loss_b)
+    assert torch.equal(grad_a, grad_c) and torch.equal(loss_a, loss_c)
+    loss_d, grad_d, _ = _run(fl, zs, zt, 20000, dtype, 0.3, 1.0, "batchmean", want_grad=False)
+    assert grad_d is None and torch.equal(loss_a, loss_d)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 1.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ties_give_exact_zeros(fl, beta, dtype):
+    """Student == teacher: loss and every gradient element exactly zero; slots
+    carrying no mass in either distribution get exactly zero gradient."""
+    zs, _ = _logits(51, 32, 9000, 3.0, dtype)
+    loss, grad, _ = _run(fl, zs, zs.copy(), 9000, dtype, beta, 1.0, "batchmean")
+    assert from_device(loss) == 0.0
+    assert torch.count_nonzero(grad).item() == 0
+    zt, _ = _logits(52, 32, 9000, 3.0, dtype)
+    pad_bits = workloads.f32_to_bf16_bits(np.array([workloads.PAD_LOGIT], np.float32))[0]
+    pad = np.float32(workloads.PAD_LOGIT) if dtype == "f32" else pad_bits
+    zs[:, -64:] = pad
+    zt[:, -64:] = pad
+    loss, grad, _ = _run(fl, zs, zt, 9000, dtype, beta, 1.0, "batchmean")
+    g = from_device(grad)
+    assert np.all(g[:, -64:] == 0.0)
+    ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, dtype), to_f64(zt, dtype), beta, 1.0, "batchmean")
+    assert_loss_close(from_device(loss), ref_loss, TIGHT[dtype])
+    assert_tensor_close(g, ref_grad, TIGHT[dtype], "grad")
+
+
+def test_single_column(fl):
+    z = np.array([[1.5], [-2.0], [0.0]], dtype=np.float32)
+    loss, grad, _ = _run(fl, z, -z, 1, "f32", 0.5, 1.0, "sum")
+    assert from_device(loss) == 0.0
+    assert np.all(from_device(grad) == 0.0)
