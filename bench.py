@@ -1,0 +1,235 @@
+"""Throughput of the fused-linear generalized-JSD pass (forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--num-chunks NC]
+
+A step is one fljsd_forward_backward call over the 8192-row workload at the
+Llama-3-8B lm_head shape (H = 4096, V = 128256, bf16, beta = 0.5, T = 2,
+batchmean): both logits GEMMs, the three loss passes, grad_input and grad_W.
+Inputs are seeded synthetic draws (workloads.py), resident in HBM before the
+timed region; outputs and the workspace are preallocated. One JSON line on
+stdout; progress goes to stderr.
+
+Fields beyond the throughput:
+  roofline      the kernel class with the most time: algorithmic flops (or
+                bytes) per launch over its average launch time, from HIP
+                events the library records around each launch during the
+                timed steps, against MI355X's published peak.
+  kernels       the same tally for every kernel class.
+  cpu_baseline  the CPU oracle (numpy fp64) timed on the first rows of the
+                same workload, in tokens/s.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-linear-JSD fwd+bwd tokens/s at H=4096,V=128256 bf16; MFMA util"
+WORKLOAD = "large_batch"
+# The pages' H100 80GB figure for this workload (B*T = 8192, num_chunks = 1,
+# H = 4096, V = 128256, bf16): 60.62 ms per full pass, i.e. 135,137 tokens/s.
+PAGES_TOKENS_PER_S = 8192 / 60.62e-3
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+GEMM_CLASSES = ("gemm_logits", "gemm_grad_input", "gemm_grad_weight")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--num-chunks", type=int, default=0,
+                   help="0: the library's policy for the free HBM (one chunk on 288 GB)")
+    p.add_argument("--cpu-rows", type=int, default=2048,
+                   help="rows of the workload the CPU oracle is timed on")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def device_inputs(inp):
+    import numpy as np
+    import torch
+    return [torch.from_numpy(inp[k].view(np.int16)).view(torch.bfloat16).cuda()
+            for k in ("X_s", "W_s", "X_t", "W_t")]
+
+
+def roofline_of(cls, k):
+    """Achieved rate of one kernel class: algorithmic work per launch over the
+    average launch time."""
+    avg_s = k["ms"] / 1e3 / k["launches"]
+    if cls in GEMM_CLASSES:
+        per_launch = k["flops"] / k["launches"]
+        return {"bound": "mfma", "achieved": per_launch / avg_s / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "per_launch": per_launch, "avg_launch_ms": avg_s * 1e3}
+    per_launch = k["bytes"] / k["launches"]
+    return {"bound": "hbm", "achieved": per_launch / avg_s / 1e9, "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "per_launch": per_launch, "avg_launch_ms": avg_s * 1e3}
+
+
+def traffic_for(cls):
+    """Measured HBM bytes per launch for a kernel class, if a counter summary
+    for the current kernel sources is on file; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get("kernels", {}).get(cls)
+    if not entry:
+        return None
+    from lm_head_distillation_amd.build import source_digest
+    if entry.get("source_digest") != source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, rows):
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    import workloads
+    log(f"cpu baseline: oracle on the first {rows} rows (fp64 widening excluded from the time)")
+    X_s = workloads.to_f64(inp["X_s"][:rows], "bf16")
+    X_t = workloads.to_f64(inp["X_t"][:rows], "bf16")
+    W_s = workloads.to_f64(inp["W_s"], "bf16")
+    W_t = workloads.to_f64(inp["W_t"], "bf16")
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    t0 = time.perf_counter()
+    oracle.fused_linear_jsd(X_s, W_s, X_t, W_t, w.beta, w.temperature, w.reduction, block_rows=256)
+    dt = time.perf_counter() - t0
+    del W_s, W_t
+    return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"first {rows} of {w.BT} rows, full H={w.H_s} and V={w.V} weights, "
+                       f"fp64 numpy/OpenBLAS, {dt:.1f} s"),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(every box in this setup has a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from lm_head_distillation_amd import fljsd
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    fljsd.load_library()
+    w = workloads.WORKLOADS[WORKLOAD]
+    t0 = time.perf_counter()
+    inp = workloads.make_inputs(w)
+    log(f"inputs drawn in {time.perf_counter() - t0:.1f} s")
+    X_s, W_s, X_t, W_t = device_inputs(inp)
+    BT, H, V = w.BT, w.H_s, w.V
+    nc = args.num_chunks or fljsd.fljsd_plan_num_chunks(BT, H, w.H_t, V, fljsd.BF16,
+                                                         fljsd.default_budget_bytes())
+    ws = torch.empty(fljsd.fljsd_workspace_size(BT, H, w.H_t, V, fljsd.BF16, nc),
+                     dtype=torch.uint8, device="cuda")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    gX = torch.empty_like(X_s)
+    gW = torch.empty_like(W_s)
+    out = (loss, gX, gW)
+
+    def step():
+        fljsd.fljsd_forward_backward(X_s, W_s, X_t, W_t, w.beta, w.temperature, w.reduction, nc,
+                                     workspace=ws, out=out)
+
+    torch.cuda.reset_peak_memory_stats()
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; num_chunks={nc}, workspace {ws.numel() / 2**20:.0f} MiB")
+
+    fljsd.fljsd_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernels = fljsd.fljsd_profile_read()
+    fljsd.fljsd_profile_enable(False)
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = BT * args.steps / elapsed
+    peak_mb = torch.cuda.max_memory_allocated() / 2**20
+    log(f"timed {args.steps} steps: {ms_per_step:.2f} ms/step, {tokens_per_s:,.0f} tokens/s, "
+        f"loss {float(loss):.6f}")
+
+    per_class = {}
+    for cls, k in kernels.items():
+        if k["launches"]:
+            r = roofline_of(cls, k)
+            r["ms_per_step"] = k["ms"] / args.steps
+            r["launches_per_step"] = k["launches"] / args.steps
+            per_class[cls] = r
+            log(f"  {cls:18s} {r['ms_per_step']:8.3f} ms/step  {r['achieved']:9.1f} {r['unit']}"
+                f"  ({100 * r['achieved'] / r['peak']:.1f}% of peak)")
+    dominant = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
+    d = per_class[dominant]
+    traffic = traffic_for(dominant)
+    roofline = {"bound": d["bound"], "achieved": round(d["achieved"], 2), "peak": d["peak"],
+                "unit": d["unit"], "frac": round(d["achieved"] / d["peak"], 4), "traffic": traffic,
+                "kernel": dominant, "avg_launch_ms": round(d["avg_launch_ms"], 4),
+                "per_launch": d["per_launch"]}
+    gemm_ms = sum(kernels[c]["ms"] for c in GEMM_CLASSES)
+    gemm_flops = sum(kernels[c]["flops"] for c in GEMM_CLASSES)
+    jsd_cls = ("jsd_stats", "jsd_loss", "jsd_grad")
+    jsd_ms = sum(kernels[c]["ms"] for c in jsd_cls)
+    jsd_bytes = sum(kernels[c]["bytes"] for c in jsd_cls)
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(tokens_per_s / PAGES_TOKENS_PER_S, 4),
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{WORKLOAD}: BT={BT} H={H} V={V} bf16 beta={w.beta} "
+                               f"T={w.temperature} {w.reduction}",
+                   "global_batch": BT, "num_chunks": nc, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "mfma_util_gemms": round(gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "jsd_hbm_gbps_algorithmic": round(jsd_bytes / (jsd_ms / 1e3) / 1e9, 1),
+        "peak_hbm_mb": round(peak_mb, 1),
+        "kernels": {c: {"ms_per_step": round(r["ms_per_step"], 4), "achieved": round(r["achieved"], 2),
+                        "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4)}
+                    for c, r in per_class.items()},
+    }
+    if not args.no_cpu_baseline:
+        del X_s, W_s, X_t, W_t, ws, gX, gW
+        torch.cuda.empty_cache()
+        cb = cpu_baseline(inp, w, args.cpu_rows)
+        log(f"cpu baseline: {cb['value']:.1f} tokens/s on {cb['cores']} threads ({cb['seconds']:.1f} s)")
+        cb.pop("seconds")
+        cb["value"] = round(cb["value"], 2)
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,20 @@ SOURCES = ["api.hip", "jsd.hip", "gemm_bf16.hip", "gemm_f32.hip", "plan.cpp"]
 ARCH = "gfx950"
 
 
+def source_digest() -> str:
+    """Short hash of every source the library is built from (kernels, host
+    code, the public header): counter figures taken for one digest do not
+    describe a library built from another."""
+    import hashlib
+    h = hashlib.sha256()
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC))] + [os.path.join(INCLUDE, "fljsd.h")]
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")

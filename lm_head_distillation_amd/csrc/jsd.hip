@@ -7,15 +7,15 @@
 //   pass 3  dX, written over the student logits when the caller asks for it
 //           in place.
 // Everything from the loaded logit onward is fp32 (PR #1352 Details: the cast
-// happens at load). Exponentials are base 2: logits are pre-scaled by
-// log2(e)/T so the hardware exp2 path evaluates e^x (PR #1352 Details, last
-// bullet). A row may be split into S slices, each a workgroup; the slices'
-// partial statistics and sums are merged in a fixed order, so results are
-// deterministic run to run.
+// happens at load). Exponentials are base 2 (PR #1352 Details, last bullet):
+// with k = log2(e)/T, a row's statistics are m = max z (in logit units, so
+// the maximum is exact) and d = sum 2^((z - m) k), and an element's log2
+// probability is a = (z - m) k - log2 d. A row may be split into S slices,
+// each a workgroup; the slices' partial statistics and sums are merged in a
+// fixed order, so results are deterministic run to run.
 //
-// Per element, with a = log2 of a probability (a_s = y_s - L_s, a_t = y_t -
-// L_t, y = z log2(e)/T, L = m + log2 d), Q = 2^a_s (student), P = 2^a_t
-// (teacher) and D = ln P - ln Q = (a_t - a_s) ln 2:
+// Per element, with Q = 2^a_s (student), P = 2^a_t (teacher) and
+// D = ln P - ln Q = (a_t - a_s) ln 2:
 //   generalized: r = ln(beta e^D + 1 - beta), evaluated as
 //                  D <  0: log1p(beta expm1(D))
 //                  D >= 0: D + log1p((1-beta) expm1(-D))
@@ -32,8 +32,11 @@
 // first-order error of the loss. Near D = 0 the terms come from their Taylor
 // series; the generalized divergence needs no such care (its derivative with
 // respect to a normalizer error is itself O(loss)).
-// y = z log2(e)/T is rounded once (no fused multiply-add) so every pass sees
-// the same y; the row maximum then gives a = y - L exactly where d = 1.
+//
+// Transcendentals use the hardware instructions (v_exp_f32 = 2^x, v_log_f32 =
+// log2, v_rcp_f32). expm1 on (-1/2, 0] is a degree-9 Taylor polynomial and
+// log1p on [-1/4, 0] the atanh series, so both keep full relative accuracy as
+// their argument goes to 0.
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -48,6 +51,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ inline float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ inline float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -109,39 +116,33 @@ __device__ inline void store8(uint16_t* p, int64_t v, int n, bool vec, const flo
   }
 }
 
-// y = z * log2(e)/T, rounded to fp32 on its own: contraction into a later
-// subtraction is switched off so every pass computes bit-identical y.
-__device__ inline float scaled_logit(float z, float k2) {
-#pragma clang fp contract(off)
-  return z * k2;
-}
-
-// Merge of two (max, denominator) pairs in base 2. Commutative bit for bit
-// (max and a two-term IEEE sum are), so both butterfly partners agree.
-__device__ inline void md_merge(float& m, float& d, float mo, float dof) {
+// Merge of two (max, denominator) pairs; maxima in logit units, denominators
+// in base 2 with scale k. Commutative bit for bit (max and a two-term IEEE
+// sum are), so both butterfly partners agree.
+__device__ inline void md_merge(float& m, float& d, float mo, float dof, float k) {
   const float M = fmaxf(m, mo);
   if (M == -INFINITY) {
     m = -INFINITY;
     d = 0.f;
     return;
   }
-  d = d * exp2f(m - M) + dof * exp2f(mo - M);
+  d = d * hw_exp2((m - M) * k) + dof * hw_exp2((mo - M) * k);
   m = M;
 }
 
-// Fold 8 scaled logits into a running (max, denominator).
-__device__ inline void md_update8(float& m, float& d, const float* y) {
-  float mx = y[0];
+// Fold 8 logits into a running (max, denominator).
+__device__ inline void md_update8(float& m, float& d, const float* z, float k) {
+  float mx = z[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
   if (mx == -INFINITY) return;
   if (mx > m) {
-    d *= exp2f(m - mx);
+    d *= hw_exp2((m - mx) * k);
     m = mx;
   }
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc += exp2f(y[i] - m);
+  for (int i = 0; i < 8; ++i) acc += hw_exp2((z[i] - m) * k);
   d += acc;
 }
 
@@ -151,13 +152,46 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-__device__ inline void wave_md(float& m, float& d) {
+__device__ inline void wave_md(float& m, float& d, float k) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float mo = __shfl_xor(m, o, 64);
     const float dof = __shfl_xor(d, o, 64);
-    md_merge(m, d, mo, dof);
+    md_merge(m, d, mo, dof, k);
   }
+}
+
+// expm1(w) for w <= 0: Taylor polynomial on (-1/2, 0], 2^(w log2 e) - 1 below.
+// `t` is w / ln 2 (the same value in base 2).
+__device__ inline float expm1_nonpos(float w, float t) {
+  float p = 1.f / 362880.f;
+  p = fmaf(p, w, 1.f / 40320.f);
+  p = fmaf(p, w, 1.f / 5040.f);
+  p = fmaf(p, w, 1.f / 720.f);
+  p = fmaf(p, w, 1.f / 120.f);
+  p = fmaf(p, w, 1.f / 24.f);
+  p = fmaf(p, w, 1.f / 6.f);
+  p = fmaf(p, w, 0.5f);
+  p = fmaf(p, w, 1.f);
+  const float poly = p * w;
+  return w > -0.5f ? poly : hw_exp2(t) - 1.f;
+}
+
+// log1p(x) for x in (-1, 0]. Near 0 (x >= -1/4): 2 atanh(s) with
+// s = x / (2 + x) in [-1/7, 0], an odd series whose truncation error is below
+// 1e-10 relative; further out, ln(1 + x) from the hardware log2, whose result
+// is then at least 0.41 in magnitude.
+__device__ inline float log1p_nonpos(float x) {
+  const float s = x * hw_rcp(2.f + x);
+  const float s2 = s * s;
+  float p = 1.f / 11.f;
+  p = fmaf(p, s2, 1.f / 9.f);
+  p = fmaf(p, s2, 1.f / 7.f);
+  p = fmaf(p, s2, 1.f / 5.f);
+  p = fmaf(p, s2, 1.f / 3.f);
+  p = fmaf(p, s2, 1.f);
+  const float series = 2.f * s * p;
+  return x >= -0.25f ? series : hw_log2(1.f + x) * kLn2;
 }
 
 // D e^D - expm1(D) for |D| < 1/4: sum over k >= 2 of (k-1) D^k / k!.
@@ -184,21 +218,22 @@ __device__ inline float kl_rev_series(float D) {
   return p * D * D;
 }
 
-// Per-element terms of the divergence; see the file comment. Outputs: the
-// probabilities Q and P, the loss term l, the gradient term g (dA = g - Q G)
-// and gacc, the term summed into G.
+// Per-element terms of the divergence; see the file comment. Inputs are the
+// log2 probabilities a_s, a_t. Outputs: Q and P, the loss term l, the
+// gradient term g (dA = g - Q G) and gacc, the term summed into G.
 template <int MODE>
 __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float& P, float& l,
                                  float& g, float& gacc) {
-  Q = exp2f(as);
-  P = exp2f(at);
+  Q = hw_exp2(as);
+  P = hw_exp2(at);
   if (P == Q) {  // exact tie: no loss, no gradient term
     l = 0.f;
     g = 0.f;
     gacc = 0.f;
     return;
   }
-  const float D = (at - as) * kLn2;
+  const float t = at - as;    // log2(P / Q)
+  const float D = t * kLn2;   // ln(P / Q)
   if (MODE == kModeForwardKL) {
     l = fabsf(D) < 0.25f ? Q * kl_fwd_series(D) : P * D - (P - Q);
     g = -P;
@@ -208,15 +243,12 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
     g = -Q * D;
     gacc = l;    // G = KL(Q||P), the row loss
   } else {
-    float r, dmr;
-    if (D >= 0.f) {
-      const float u = log1pf((1.f - beta) * expm1f(-D));
-      r = D + u;
-      dmr = -u;
-    } else {
-      r = log1pf(beta * expm1f(D));
-      dmr = D - r;
-    }
+    // One expm1 of -|D| and one log1p serve both signs of D.
+    const bool neg = D < 0.f;
+    const float e = expm1_nonpos(-fabsf(D), -fabsf(t));
+    const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
+    const float r = neg ? L1 : D + L1;
+    const float dmr = neg ? D - L1 : -L1;
     l = beta * P * dmr - (1.f - beta) * Q * r;
     g = -(1.f - beta) * Q * r;
     gacc = g;
@@ -224,22 +256,21 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
 }
 
 // Row statistics from the S pass-1 partials, merged in slice order by one
-// thread and broadcast through LDS. Returns L_s = m_s + log2 d_s and L_t.
-__device__ inline void row_log_norms(const JsdArgs& a, int64_t row, float& Ls, float& Lt) {
-  __shared__ float2 sh_L;
+// thread and broadcast through LDS: returns (m_s, log2 d_s, m_t, log2 d_t).
+__device__ inline float4 row_log_norms(const JsdArgs& a, int64_t row) {
+  __shared__ float4 sh_L;
   if (threadIdx.x == 0) {
     const float4* st = a.stats + row * a.S;
     float4 acc = st[0];
     for (int s = 1; s < a.S; ++s) {
       const float4 o = st[s];
-      md_merge(acc.x, acc.y, o.x, o.y);
-      md_merge(acc.z, acc.w, o.z, o.w);
+      md_merge(acc.x, acc.y, o.x, o.y, a.k2);
+      md_merge(acc.z, acc.w, o.z, o.w, a.k2);
     }
-    sh_L = make_float2(acc.x + log2f(acc.y), acc.z + log2f(acc.w));
+    sh_L = make_float4(acc.x, hw_log2(acc.y), acc.z, hw_log2(acc.w));
   }
   __syncthreads();
-  Ls = sh_L.x;
-  Lt = sh_L.y;
+  return sh_L;
 }
 
 template <typename T>
@@ -250,22 +281,18 @@ __global__ __launch_bounds__(kThreads) void jsd_stats_kernel(JsdArgs a) {
   const int64_t v1 = min(a.V, v0 + a.slice_w);
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
+  const float k = a.k2;
   float ms = -INFINITY, ds = 0.f, mt = -INFINITY, dt = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8];
     load8(zs, v, n, a.vec_ok, ys);
     load8(zt, v, n, a.vec_ok, yt);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ys[i] = scaled_logit(ys[i], a.k2);
-      yt[i] = scaled_logit(yt[i], a.k2);
-    }
-    md_update8(ms, ds, ys);
-    md_update8(mt, dt, yt);
+    md_update8(ms, ds, ys, k);
+    md_update8(mt, dt, yt, k);
   }
-  wave_md(ms, ds);
-  wave_md(mt, dt);
+  wave_md(ms, ds, k);
+  wave_md(mt, dt, k);
   __shared__ float4 sh[kWaves];
   const int wave = threadIdx.x / 64;
   if ((threadIdx.x & 63) == 0) sh[wave] = make_float4(ms, ds, mt, dt);
@@ -273,8 +300,8 @@ __global__ __launch_bounds__(kThreads) void jsd_stats_kernel(JsdArgs a) {
   if (threadIdx.x == 0) {
     float4 acc = sh[0];
     for (int w = 1; w < kWaves; ++w) {
-      md_merge(acc.x, acc.y, sh[w].x, sh[w].y);
-      md_merge(acc.z, acc.w, sh[w].z, sh[w].w);
+      md_merge(acc.x, acc.y, sh[w].x, sh[w].y, k);
+      md_merge(acc.z, acc.w, sh[w].z, sh[w].w, k);
     }
     a.stats[row * a.S + s] = acc;
   }
@@ -288,8 +315,8 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   const int64_t v1 = min(a.V, v0 + a.slice_w);
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
-  float Ls, Lt;
-  row_log_norms(a, row, Ls, Lt);
+  const float4 L = row_log_norms(a, row);
+  const float k = a.k2;
   float lsum = 0.f, gsum = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
@@ -300,8 +327,8 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
     for (int i = 0; i < 8; ++i) {
       if (i < n) {
         float Q, P, l, g, gacc;
-        jsd_terms<MODE>(scaled_logit(ys[i], a.k2) - Ls, scaled_logit(yt[i], a.k2) - Lt, a.beta, Q, P,
-                        l, g, gacc);
+        jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
+                        gacc);
         lsum += l;
         gsum += gacc;
       }
@@ -332,15 +359,15 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
   T* gr = static_cast<T*>(a.grad) + row * a.ld;
-  float Ls, Lt;
-  row_log_norms(a, row, Ls, Lt);
+  const float4 L = row_log_norms(a, row);
+  const float k = a.k2;
   __shared__ float sh_G;
   if (threadIdx.x == 0) {
     const float2* lg = a.lg + row * a.S;
     float2 acc = lg[0];
-    for (int k = 1; k < a.S; ++k) {
-      acc.x += lg[k].x;
-      acc.y += lg[k].y;
+    for (int j = 1; j < a.S; ++j) {
+      acc.x += lg[j].x;
+      acc.y += lg[j].y;
     }
     sh_G = acc.y;
     if (s == 0) a.row_loss[row] = acc.x;
@@ -355,8 +382,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
-      jsd_terms<MODE>(scaled_logit(ys[i], a.k2) - Ls, scaled_logit(yt[i], a.k2) - Lt, a.beta, Q, P, l,
-                      g, gacc);
+      jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
       const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
       out[i] = dA * a.grad_scale;
     }
@@ -369,7 +395,7 @@ __global__ __launch_bounds__(64) void jsd_row_loss_kernel(JsdArgs a) {
   if (threadIdx.x == 0) {
     const float2* lg = a.lg + row * a.S;
     float acc = lg[0].x;
-    for (int k = 1; k < a.S; ++k) acc += lg[k].x;
+    for (int j = 1; j < a.S; ++j) acc += lg[j].x;
     a.row_loss[row] = acc;
   }
 }
@@ -411,17 +437,40 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
     }
     const int64_t m = e / N;
     const int64_t c = e % N;   // N is a multiple of 4, so all four share row m
-    float x[4] = {acc.x, acc.y, acc.z, acc.w};
     T* o = out + m * ldo + c;
     if constexpr (sizeof(T) == 4) {
       *reinterpret_cast<float4*>(o) = acc;
     } else {
       uint2 q;
-      q.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-      q.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+      q.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+      q.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
       *reinterpret_cast<uint2*>(o) = q;
     }
   }
+}
+
+template <typename T>
+hipError_t launch_loss_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
+  const dim3 block(kThreads);
+  if (a.mode == kModeForwardKL)
+    hipLaunchKernelGGL((jsd_loss_kernel<T, kModeForwardKL>), grid, block, 0, s, a);
+  else if (a.mode == kModeReverseKL)
+    hipLaunchKernelGGL((jsd_loss_kernel<T, kModeReverseKL>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((jsd_loss_kernel<T, kModeGeneralized>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_grad_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
+  const dim3 block(kThreads);
+  if (a.mode == kModeForwardKL)
+    hipLaunchKernelGGL((jsd_grad_kernel<T, kModeForwardKL>), grid, block, 0, s, a);
+  else if (a.mode == kModeReverseKL)
+    hipLaunchKernelGGL((jsd_grad_kernel<T, kModeReverseKL>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((jsd_grad_kernel<T, kModeGeneralized>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -437,44 +486,12 @@ hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s) {
 
 hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>(a.S));
-  const dim3 block(kThreads);
-  if (dtype == 1) {
-    if (a.mode == kModeForwardKL)
-      hipLaunchKernelGGL((jsd_loss_kernel<uint16_t, kModeForwardKL>), grid, block, 0, s, a);
-    else if (a.mode == kModeReverseKL)
-      hipLaunchKernelGGL((jsd_loss_kernel<uint16_t, kModeReverseKL>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((jsd_loss_kernel<uint16_t, kModeGeneralized>), grid, block, 0, s, a);
-  } else {
-    if (a.mode == kModeForwardKL)
-      hipLaunchKernelGGL((jsd_loss_kernel<float, kModeForwardKL>), grid, block, 0, s, a);
-    else if (a.mode == kModeReverseKL)
-      hipLaunchKernelGGL((jsd_loss_kernel<float, kModeReverseKL>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((jsd_loss_kernel<float, kModeGeneralized>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return dtype == 1 ? launch_loss_t<uint16_t>(a, s, grid) : launch_loss_t<float>(a, s, grid);
 }
 
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>(a.S));
-  const dim3 block(kThreads);
-  if (dtype == 1) {
-    if (a.mode == kModeForwardKL)
-      hipLaunchKernelGGL((jsd_grad_kernel<uint16_t, kModeForwardKL>), grid, block, 0, s, a);
-    else if (a.mode == kModeReverseKL)
-      hipLaunchKernelGGL((jsd_grad_kernel<uint16_t, kModeReverseKL>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((jsd_grad_kernel<uint16_t, kModeGeneralized>), grid, block, 0, s, a);
-  } else {
-    if (a.mode == kModeForwardKL)
-      hipLaunchKernelGGL((jsd_grad_kernel<float, kModeForwardKL>), grid, block, 0, s, a);
-    else if (a.mode == kModeReverseKL)
-      hipLaunchKernelGGL((jsd_grad_kernel<float, kModeReverseKL>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((jsd_grad_kernel<float, kModeGeneralized>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return dtype == 1 ? launch_grad_t<uint16_t>(a, s, grid) : launch_grad_t<float>(a, s, grid);
 }
 
 hipError_t launch_jsd_row_loss(const JsdArgs& a, hipStream_t s) {

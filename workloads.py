@@ -8,7 +8,9 @@ draw identical inputs from it.
 
 Recipe (shared by every consumer):
   * numpy ``Generator(PCG64(seed))``; for workload k and draw j the seed is
-    ``1000 * k + j`` with j = 0 (X_s), 1 (W_s), 2 (X_t), 3 (W_t).
+    ``1000 * k + j`` with j = 0 (X_s), 1 (W_s), 2 (X_t), 3 (W_t). Arrays
+    larger than 2^22 elements are drawn in 2^22-element blocks, block i from
+    ``PCG64(seed).jumped(i)``.
   * ``standard_normal(dtype=float32) * sigma`` with sigma_X = 1 and
     sigma_W = 0.02 (0.02 read as a standard deviation), then rounded to
     bfloat16 with round-to-nearest-even for bfloat16 workloads.
@@ -23,7 +25,9 @@ scenarios in its Summary).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import os
 from typing import Dict, Tuple
 
 import numpy as np
@@ -72,8 +76,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
     # Inputs here are finite draws; NaN payloads are not handled.
-    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
-    return rounded.astype(np.uint16)
+    t = u >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
@@ -84,17 +92,36 @@ def bf16_to_f64(b: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(b).astype(np.float64)
 
 
+# Draws are made in blocks of BLOCK elements; block i comes from the stream
+# PCG64(seed).jumped(i), so large arrays fill in parallel and an array of at
+# most BLOCK elements is exactly PCG64(seed)'s first draws.
+BLOCK = 1 << 22
+
+
 def draw(seed: int, shape: Tuple[int, ...], sigma: float, dtype: str) -> np.ndarray:
     """One seeded normal draw. Returns float32 values or bfloat16 bits (uint16)."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if sigma != 1.0:
-        x *= np.float32(sigma)
-    if dtype == "f32":
-        return x
-    if dtype == "bf16":
-        return f32_to_bf16_bits(x)
-    raise ValueError(f"unknown dtype {dtype!r}")
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    base = np.random.PCG64(seed)
+
+    def fill(i: int) -> None:
+        lo = i * BLOCK
+        hi = min(n, lo + BLOCK)
+        rng = np.random.Generator(base.jumped(i))
+        x = rng.standard_normal(size=hi - lo, dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        out[lo:hi] = x if dtype == "f32" else f32_to_bf16_bits(x)
+
+    nblocks = max(1, -(-n // BLOCK))
+    if nblocks == 1:
+        fill(0)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as pool:
+            list(pool.map(fill, range(nblocks)))
+    return out.reshape(shape)
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
