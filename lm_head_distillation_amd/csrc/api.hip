@@ -329,6 +329,7 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
       g.epilogue = kEpiStore;
       g.splitk = 1;
       g.k_per_split = H;
+      g.group_m = 4;
       hipError_t e = timed(s, FLJSD_KCLASS_GEMM_LOGITS, 2.0 * rows * V * H, gemm_bytes(g, es),
                            [&] { return gemm(dtype, g, s); });
       if (e != hipSuccess) return fail_hip(e, "launch logits GEMM");
@@ -350,6 +351,7 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
       g.ldb = H_s;
       g.a_kcontig = true;
       g.b_kcontig = false;
+      g.group_m = 8;
       const bool split = dtype == FLJSD_BF16 && plan.splitk > 1;
       char* gx = static_cast<char*>(grad_X_s) + r0 * H_s * es;
       if (split) {
@@ -394,6 +396,7 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
       g.epilogue = ci == 0 ? kEpiStore : kEpiAccumulate;
       g.splitk = 1;
       g.k_per_split = rows;
+      g.group_m = 2;
       hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H_s * V,
                            gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
       if (e != hipSuccess) return fail_hip(e, "launch grad_weight GEMM");

@@ -13,14 +13,19 @@
 // 8 (m) x 4 (k) blocks of four 16-byte row segments and transposed in
 // registers into 8-byte LDS writes.
 //
-// Pipeline: two LDS stages; the next K-tile's global loads are issued before
-// the current tile's MFMAs and written to the other stage after them, with one
-// barrier per K-tile.
+// Pipeline: two LDS stages and one barrier per K-tile. For blocks inside the
+// operands, K-contiguous operands are copied straight from global memory into
+// the next stage (gfx950 global_load_lds) while the current stage's MFMAs
+// run; M/N-contiguous operands go through registers and are written to LDS
+// after the MFMAs. Edge blocks and a partial last K-tile take a
+// bounds-checked register path. Within a stage, each 16-wide K step's
+// fragments are read while the previous step's MFMAs run.
 #include "kernels.h"
 #include "plan.h"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 namespace fljsd {
@@ -51,6 +56,27 @@ __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
   for (int i = 0; i < 8; ++i) e[i] = i < n ? p[i] : uint16_t(0);
   return make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+}
+
+constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 XCDs, each with its own L2
+
+// Output tile of workgroup `bid`. Workgroup ids are first renumbered so each
+// XCD receives one contiguous range of logical ids (the hardware deals ids
+// out round-robin across XCDs), then logical ids walk the tiles in groups of
+// `group_m` M-tiles: M fastest within a group, then N, then the next group.
+// Tiles that run together on one XCD therefore share operand panels in its L2.
+__device__ inline void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int group_m, int& tm,
+                               int& tn) {
+  const int xcd = bid % kXcds;
+  const int per = nblk / kXcds;
+  const int rem = nblk % kXcds;
+  const int logical = xcd * per + min(xcd, rem) + bid / kXcds;
+  const int in_group = group_m * tiles_n;
+  const int first_m = (logical / in_group) * group_m;
+  const int gm = min(group_m, tiles_m - first_m);
+  const int r = logical % in_group;
+  tm = first_m + r % gm;
+  tn = r / gm;
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_K, bool B_K, int EPI>
@@ -159,26 +185,194 @@ struct GemmKernel {
     }
   }
 
-  static __device__ void run(const GemmArgs& g, int tiles_m) {
-    __shared__ uint4 lds[2][LDS_STAGE];
+  // Global -> registers for a tile that lies wholly inside the operand.
+  template <int R, int U, bool KCONTIG>
+  static __device__ inline void load_tile_fast(const uint16_t* __restrict__ p, int64_t ld,
+                                               int64_t row0, int64_t k0, uint4* reg) {
+    const int tid = threadIdx.x;
+    if constexpr (KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < 4 * U; ++i) {
+        const int cid = tid + i * NT;
+        reg[i] = *reinterpret_cast<const uint4*>(p + (row0 + cid / CPR) * ld + k0 + (cid % CPR) * 8);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int uid = tid + u * NT;
+        const int64_t mn = row0 + (uid % (R / 8)) * 8;
+        const int64_t kk = k0 + (uid / (R / 8)) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          reg[u * 4 + q] = *reinterpret_cast<const uint4*>(p + (kk + q) * ld + mn);
+      }
+    }
+  }
+
+  // Direct global -> LDS copy of a K-contiguous tile, no registers involved
+  // (gfx950 global_load_lds_dwordx4). One wave instruction fills 8 LDS rows
+  // (1 KB): lane l lands in slot l, i.e. row l/8 at physical chunk l%8, so it
+  // loads the logical chunk the swizzle maps there. Every access is in bounds
+  // (interior tile, whole K-tile).
+  template <int R>
+  static __device__ inline void dma_tile(const uint16_t* __restrict__ p, int64_t ld,
+                                         int64_t row0, int64_t k0, uint4* region) {
+    constexpr int NW = NT / 64;
+    constexpr int INSTS = R / 8 / NW;
+    static_assert(INSTS * NW * 8 == R, "rows must split evenly over the waves");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < INSTS; ++i) {
+      const int rb = (wave + i * NW) * 8;   // first row this instruction fills
+      const int r = rb + lane / 8;
+      const int c = (lane % 8) ^ ((r ^ (r >> 3)) & 7);
+      const uint16_t* src = p + (row0 + r) * ld + k0 + c * 8;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(region + rb * CPR),
+                                       16, 0, 0);
+    }
+  }
+
+  static __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+  // Fragments of one 16-wide K step for this wave.
+  static __device__ inline void read_frags(const uint4* cur, int ks, int lane, int wave_m,
+                                           int wave_n, bf16x8* fa, bf16x8* fb) {
+    const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = wave_m * WM + i * 32 + (lane & 31);
+      fa[i] = __builtin_bit_cast(bf16x8, cur[r * CPR + swz(r, ch)]);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int r = wave_n * WN + j * 32 + (lane & 31);
+      fb[j] = __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz(r, ch)]);
+    }
+  }
+
+  // MFMAs over one LDS stage, with the next K step's fragments read while the
+  // current step's products run.
+  static __device__ inline void compute_stage(const uint4* cur, int lane, int wave_m, int wave_n,
+                                              floatx16 (&acc)[TM][TN]) {
+    constexpr int KS = BK / 16;
+    bf16x8 fa[2][TM], fb[2][TN];
+    read_frags(cur, 0, lane, wave_m, wave_n, fa[0], fb[0]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) read_frags(cur, ks + 1, lane, wave_m, wave_n, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
+                                                              acc[i][j], 0, 0, 0);
+    }
+
+  }
+
+  // Start moving K-tile k0 of both operands towards `stage`: K-contiguous
+  // operands go straight to LDS, the others into registers (ra, rb).
+  static __device__ inline void issue_fast(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
+                                           uint4* stage, uint4* ra, uint4* rb) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    if constexpr (A_K)
+      dma_tile<BM>(A, g.lda, m0, k0, stage);
+    else
+      load_tile_fast<BM, UA, false>(A, g.lda, m0, k0, ra);
+    if constexpr (B_K)
+      dma_tile<BN>(B, g.ldb, n0, k0, stage + BM * CPR);
+    else
+      load_tile_fast<BN, UB, false>(B, g.ldb, n0, k0, rb);
+  }
+
+  // Registers staged by issue_fast -> LDS (the transposing writes).
+  static __device__ inline void finish_fast(uint4* stage, const uint4* ra, const uint4* rb) {
+    if constexpr (!A_K) store_tile<BM, UA, false>(stage, 0, ra);
+    if constexpr (!B_K) store_tile<BN, UB, false>(stage, BM, rb);
+  }
+
+  // Whole K-tiles of an interior block over two LDS stages (two LDS arrays):
+  // the copies into one stage are in flight while the other is read.
+  static __device__ inline void mainloop_fast(const GemmArgs& g, uint4* lds0, uint4* lds1,
+                                              int64_t m0, int64_t n0, int64_t kb, int nkf,
+                                              floatx16 (&acc)[TM][TN]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wave_m = wave % WAVES_M;
+    const int wave_n = wave / WAVES_M;
+    uint4 ra[A_K ? 1 : 4 * UA], rb[B_K ? 1 : 4 * UB];
+    issue_fast(g, m0, n0, kb, lds0, ra, rb);
+    finish_fast(lds0, ra, rb);
+    wait_vmem();
+    __syncthreads();
+    for (int t = 0; t < nkf; ++t) {
+      uint4* cur = (t & 1) ? lds1 : lds0;
+      uint4* nxt = (t & 1) ? lds0 : lds1;
+      const bool more = t + 1 < nkf;
+      if (more) issue_fast(g, m0, n0, kb + static_cast<int64_t>(t + 1) * BK, nxt, ra, rb);
+      compute_stage(cur, lane, wave_m, wave_n, acc);
+      if (more) finish_fast(nxt, ra, rb);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+
+  // Bounds-checked K-tiles [t0, t1) through registers (edge blocks, and the
+  // partial last K-tile of interior blocks). Two LDS stages, one barrier per
+  // K-tile; entered and left with both stages free.
+  static __device__ inline void mainloop_checked(const GemmArgs& g, uint4* lds0, uint4* lds1,
+                                                 int64_t m0, int64_t n0, int64_t kb, int64_t ke,
+                                                 int t0, int t1, floatx16 (&acc)[TM][TN]) {
+    if (t0 >= t1) return;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wave_m = wave % WAVES_M;
+    const int wave_n = wave / WAVES_M;
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    uint4 ra[4 * UA], rb[4 * UB];
+    load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, kb + static_cast<int64_t>(t0) * BK, ke, ra);
+    load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, kb + static_cast<int64_t>(t0) * BK, ke, rb);
+    store_tile<BM, UA, A_K>(lds0, 0, ra);
+    store_tile<BN, UB, B_K>(lds0, BM, rb);
+    __syncthreads();
+    for (int t = t0; t < t1; ++t) {
+      uint4* cur = ((t - t0) & 1) ? lds1 : lds0;
+      uint4* nxt = ((t - t0) & 1) ? lds0 : lds1;
+      const bool more = t + 1 < t1;
+      if (more) {
+        const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
+        load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, k0, ke, ra);
+        load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, k0, ke, rb);
+      }
+      compute_stage(cur, lane, wave_m, wave_n, acc);
+      if (more) {
+        store_tile<BM, UA, A_K>(nxt, 0, ra);
+        store_tile<BN, UB, B_K>(nxt, BM, rb);
+      }
+      __syncthreads();
+    }
+  }
+
+  static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
+    __shared__ uint4 lds0[LDS_STAGE];
+    __shared__ uint4 lds1[LDS_STAGE];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wave_m = wave % WAVES_M;
     const int wave_n = wave / WAVES_M;
 
-    const int64_t bid = blockIdx.x;
-    const int64_t tm = bid % tiles_m;
-    const int64_t tn = bid / tiles_m;
-    const int64_t m0 = tm * BM;
-    const int64_t n0 = tn * BN;
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = static_cast<int64_t>(tm) * BM;
+    const int64_t n0 = static_cast<int64_t>(tn) * BN;
     const int split = blockIdx.y;
     const int64_t kb = static_cast<int64_t>(split) * g.k_per_split;
     const int64_t ke = min(g.K, kb + g.k_per_split);
     const int nk = static_cast<int>((ke - kb + BK - 1) / BK);
-
-    const uint16_t* A = static_cast<const uint16_t*>(g.A);
-    const uint16_t* B = static_cast<const uint16_t*>(g.B);
 
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -188,46 +382,12 @@ struct GemmKernel {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    uint4 ra[4 * UA], rb[4 * UB];
-    load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, kb, ke, ra);
-    load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, kb, ke, rb);
-    store_tile<BM, UA, A_K>(lds[0], 0, ra);
-    store_tile<BN, UB, B_K>(lds[0], BM, rb);
-    __syncthreads();
-
-    for (int t = 0; t < nk; ++t) {
-      const bool more = t + 1 < nk;
-      if (more) {
-        const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
-        load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, k0, ke, ra);
-        load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, k0, ke, rb);
-      }
-      const uint4* cur = lds[t & 1];
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int ch = ks * 2 + (lane >> 5);
-        bf16x8 fa[TM], fb[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = wave_m * WM + i * 32 + (lane & 31);
-          fa[i] = __builtin_bit_cast(bf16x8, cur[r * CPR + swz(r, ch)]);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int r = wave_n * WN + j * 32 + (lane & 31);
-          fb[j] = __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz(r, ch)]);
-        }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        store_tile<BM, UA, A_K>(lds[(t + 1) & 1], 0, ra);
-        store_tile<BN, UB, B_K>(lds[(t + 1) & 1], BM, rb);
-      }
-      __syncthreads();
+    if (m0 + BM <= g.M && n0 + BN <= g.N) {
+      const int nkf = static_cast<int>((ke - kb) / BK);   // whole K-tiles
+      if (nkf > 0) mainloop_fast(g, lds0, lds1, m0, n0, kb, nkf, acc);
+      mainloop_checked(g, lds0, lds1, m0, n0, kb, ke, nkf, nk, acc);
+    } else {
+      mainloop_checked(g, lds0, lds1, m0, n0, kb, ke, 0, nk, acc);
     }
 
     // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
@@ -261,8 +421,10 @@ struct GemmKernel {
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g,
-                                                                           int tiles_m) {
-  GemmKernel<BM, BN, WAVES_M, WAVES_N, A_K, B_K, EPI>::run(g, tiles_m);
+                                                                           int tiles_m,
+                                                                           int tiles_n,
+                                                                           int group_m) {
+  GemmKernel<BM, BN, WAVES_M, WAVES_N, A_K, B_K, EPI>::run(g, tiles_m, tiles_n, group_m);
 }
 
 constexpr int kWavesM = 2;
@@ -274,8 +436,11 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles_n = (g.N + kGemmBN - 1) / kGemmBN;
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n), static_cast<unsigned>(g.splitk));
   const dim3 block(kWavesM * kWavesN * 64);
+  const int group_m = g.group_m > 0 ? static_cast<int>(std::min<int64_t>(g.group_m, tiles_m))
+                                    : static_cast<int>(tiles_m);
   hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, kWavesM, kWavesN, A_K, B_K, EPI>),
-                     grid, block, 0, s, g, static_cast<int>(tiles_m));
+                     grid, block, 0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+                     group_m);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct GemmArgs {
   int epilogue = kEpiStore;
   int splitk = 1;
   int64_t k_per_split = 0; // multiple of the K tile when splitk > 1
+  int group_m = 0;         // M-tiles per tile group in the launch order (0: all)
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
