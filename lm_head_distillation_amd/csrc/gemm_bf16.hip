@@ -7,19 +7,21 @@
 //   logits       Z[C,V]    = X[C,H] W[V,H]^T     A and B K-contiguous
 //   grad_input   gX[C,H]   = dZ[C,V] W[V,H]      A K-contiguous, B N-contiguous
 //   grad_weight  gW[V,H] (+)= dZ[C,V]^T X[C,H]   A M-contiguous, B N-contiguous
-// LDS always holds both operands K-contiguous ([row][k], 64 k per row, 16-byte
-// chunks XOR-swizzled), so the matrix-core loop is shared. A K-contiguous
-// operand is copied 16 bytes at a time; an M/N-contiguous one is read as
-// 8 (m) x 4 (k) blocks of four 16-byte row segments and transposed in
-// registers into 8-byte LDS writes.
+// LDS always holds both operands K-contiguous ([row][k], 16-byte chunks
+// XOR-swizzled so fragment reads are bank-conflict free), so the matrix-core
+// loop is shared. A K-contiguous operand of a block inside the operands is
+// copied straight from global memory into LDS (gfx950 global_load_lds_dwordx4,
+// no registers); an M/N-contiguous one is read as 8 (m) x 4 (k) blocks of four
+// 16-byte row segments and transposed in registers into 8-byte LDS writes.
 //
-// Pipeline: two LDS stages and one barrier per K-tile. For blocks inside the
-// operands, K-contiguous operands are copied straight from global memory into
-// the next stage (gfx950 global_load_lds) while the current stage's MFMAs
-// run; M/N-contiguous operands go through registers and are written to LDS
-// after the MFMAs. Edge blocks and a partial last K-tile take a
-// bounds-checked register path. Within a stage, each 16-wide K step's
-// fragments are read while the previous step's MFMAs run.
+// Pipeline: K-tiles of 64 through two LDS stages (the template also builds
+// deeper pipelines of 32-wide K-tiles for two K-contiguous operands; on the
+// logits product they measured slower than two stages of 64). An
+// M/N-contiguous operand passes through registers. Edge blocks and a partial
+// last K-tile take a bounds-checked register path. Within a stage,
+// each 16-wide K step's fragments are read while the previous step's MFMAs
+// run. Workgroups are renumbered so the tiles one XCD runs together share
+// operand panels in that XCD's L2.
 #include "kernels.h"
 #include "plan.h"
 
@@ -33,30 +35,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
-
-constexpr int BK = kGemmBK;       // K per LDS stage
-constexpr int CPR = BK / 8;       // 16-byte chunks per LDS row
-
-// Physical chunk of logical chunk c in LDS row r. Rows r..r+7 (an MFMA
-// fragment read) and rows 8j+i for consecutive j (a transposed write) each
-// land on 8 distinct chunks.
-__device__ inline int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
-
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
-  // n in [0, 8): elements past n read as zero.
-  uint16_t e[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) e[i] = i < n ? p[i] : uint16_t(0);
-  return make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                    e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
-}
 
 constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 XCDs, each with its own L2
 
@@ -79,35 +57,91 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int 
   tn = r / gm;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_K, bool B_K, int EPI>
+// Physical 16-byte chunk of logical chunk c in LDS row r, for CPR chunks per
+// row. Eight rows' chunk c (one fragment read of eight lanes) land in eight
+// distinct bank groups, and so do the transposed writes of rows 8j + i for
+// consecutive j.
+template <int CPR>
+__device__ inline int swz(int r, int c) {
+  if constexpr (CPR == 8) {
+    return c ^ ((r ^ (r >> 3)) & 7);
+  } else {  // CPR == 4: two rows share one 128-byte bank line
+    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+  }
+}
+
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
+  // n in [0, 8): elements past n read as zero.
+  uint16_t e[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) e[i] = i < n ? p[i] : uint16_t(0);
+  return make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                    e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+}
+
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (loads complete in issue order). Counts this file does not use wait for all.
+__device__ inline void wait_vmem_upto(int n) {
+  switch (n) {
+    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
+          int EPI>
 struct GemmKernel {
   static constexpr int NT = WAVES_M * WAVES_N * 64;
+  static constexpr int NW = NT / 64;
+  static constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = BN / WAVES_N;
   static constexpr int TM = WM / 32;
   static constexpr int TN = WN / 32;
-  // 32-element load units per thread per operand and K-tile.
-  static constexpr int UA = BM * BK / (NT * 32);
-  static constexpr int UB = BN * BK / (NT * 32);
-  static_assert(UA >= 1 && UA * NT * 32 == BM * BK, "A tile must split evenly");
-  static_assert(UB >= 1 && UB * NT * 32 == BN * BK, "B tile must split evenly");
-  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static constexpr int LDS_STAGE = (BM + BN) * CPR;   // uint4 per stage
+  static_assert(CPR == 4 || CPR == 8, "K-tile of 32 or 64");
+  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(STAGES == 2 || (A_K && B_K), "deep pipelines need two K-contiguous operands");
 
-  // Global -> registers for one operand tile of R rows (M or N side).
-  template <int R, int U, bool KCONTIG>
+  // Register path: a K-contiguous tile of R rows moves in 16-byte chunks,
+  // chunks(R) per thread; an M/N-contiguous one in 8 x 4 blocks, units(R) per
+  // thread (each four 16-byte loads).
+  static constexpr int chunks(int R) { return R * CPR / NT; }
+  static constexpr int units(int R) { return R * BK / (NT * 32); }
+  static constexpr int regs(int R, bool kcontig) { return kcontig ? chunks(R) : 4 * units(R); }
+  // Direct copies: one wave instruction fills 64 / CPR rows (1 KB).
+  static constexpr int dma_insts(int R) { return R / (64 / CPR) / NW; }
+  static constexpr int DMA_PER_TILE = (A_K ? dma_insts(BM) : 0) + (B_K ? dma_insts(BN) : 0);
+
+  template <int R, bool KCONTIG>
+  static __device__ inline void check_split() {
+    if constexpr (KCONTIG)
+      static_assert(chunks(R) >= 1 && chunks(R) * NT == R * CPR, "tile must split evenly");
+    else
+      static_assert(units(R) >= 1 && units(R) * NT * 32 == R * BK, "tile must split evenly");
+  }
+
+  // Global -> registers, bounds-checked (rows past `dim`, K past `kend` read 0).
+  template <int R, bool KCONTIG>
   static __device__ inline void load_tile(const uint16_t* __restrict__ p, int64_t ld,
                                           int64_t row0, int64_t dim, int64_t k0, int64_t kend,
                                           uint4* reg) {
+    check_split<R, KCONTIG>();
     const int tid = threadIdx.x;
     if constexpr (KCONTIG) {
 #pragma unroll
-      for (int i = 0; i < 4 * U; ++i) {
+      for (int i = 0; i < chunks(R); ++i) {
         const int cid = tid + i * NT;
-        const int r = cid / CPR;
-        const int ch = cid % CPR;
-        const int64_t row = row0 + r;
-        const int64_t k = k0 + ch * 8;
+        const int64_t row = row0 + cid / CPR;
+        const int64_t k = k0 + (cid % CPR) * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (row < dim && k < kend) {
           const uint16_t* src = p + row * ld + k;
@@ -120,14 +154,13 @@ struct GemmKernel {
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < units(R); ++u) {
         const int uid = tid + u * NT;
-        const int mb = uid % (R / 8);
-        const int kq = uid / (R / 8);
-        const int64_t mn = row0 + mb * 8;
+        const int64_t mn = row0 + (uid % (R / 8)) * 8;
+        const int64_t kk = k0 + (uid / (R / 8)) * 4;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t k = k0 + kq * 4 + q;
+          const int64_t k = kk + q;
           uint4 v = make_uint4(0, 0, 0, 0);
           if (k < kend && mn < dim) {
             const uint16_t* src = p + k * ld + mn;
@@ -142,22 +175,46 @@ struct GemmKernel {
     }
   }
 
-  // Registers -> LDS stage (rows [0, R) of the operand region at `base`).
-  template <int R, int U, bool KCONTIG>
-  static __device__ inline void store_tile(uint4* lds, int base_row, const uint4* reg) {
+  // Global -> registers for a tile that lies wholly inside the operand.
+  template <int R, bool KCONTIG>
+  static __device__ inline void load_tile_fast(const uint16_t* __restrict__ p, int64_t ld,
+                                               int64_t row0, int64_t k0, uint4* reg) {
+    check_split<R, KCONTIG>();
     const int tid = threadIdx.x;
     if constexpr (KCONTIG) {
 #pragma unroll
-      for (int i = 0; i < 4 * U; ++i) {
+      for (int i = 0; i < chunks(R); ++i) {
         const int cid = tid + i * NT;
-        const int r = cid / CPR;
-        const int ch = cid % CPR;
-        lds[(base_row + r) * CPR + swz(r, ch)] = reg[i];
+        reg[i] = *reinterpret_cast<const uint4*>(p + (row0 + cid / CPR) * ld + k0 + (cid % CPR) * 8);
       }
     } else {
-      uint2* lds2 = reinterpret_cast<uint2*>(lds);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < units(R); ++u) {
+        const int uid = tid + u * NT;
+        const int64_t mn = row0 + (uid % (R / 8)) * 8;
+        const int64_t kk = k0 + (uid / (R / 8)) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          reg[u * 4 + q] = *reinterpret_cast<const uint4*>(p + (kk + q) * ld + mn);
+      }
+    }
+  }
+
+  // Registers -> LDS rows [base_row, base_row + R) of `stage`.
+  template <int R, bool KCONTIG>
+  static __device__ inline void store_tile(uint4* stage, int base_row, const uint4* reg) {
+    const int tid = threadIdx.x;
+    if constexpr (KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < chunks(R); ++i) {
+        const int cid = tid + i * NT;
+        const int r = cid / CPR;
+        stage[(base_row + r) * CPR + swz<CPR>(r, cid % CPR)] = reg[i];
+      }
+    } else {
+      uint2* lds2 = reinterpret_cast<uint2*>(stage);
+#pragma unroll
+      for (int u = 0; u < units(R); ++u) {
         const int uid = tid + u * NT;
         const int mb = uid % (R / 8);
         const int kq = uid / (R / 8);
@@ -179,61 +236,33 @@ struct GemmKernel {
             w.y = (a2[d] >> 16) | (a3[d] & 0xffff0000u);
           }
           const int r = mb * 8 + i;
-          lds2[((base_row + r) * CPR + swz(r, kq >> 1)) * 2 + (kq & 1)] = w;
+          lds2[((base_row + r) * CPR + swz<CPR>(r, kq >> 1)) * 2 + (kq & 1)] = w;
         }
       }
     }
   }
 
-  // Global -> registers for a tile that lies wholly inside the operand.
-  template <int R, int U, bool KCONTIG>
-  static __device__ inline void load_tile_fast(const uint16_t* __restrict__ p, int64_t ld,
-                                               int64_t row0, int64_t k0, uint4* reg) {
-    const int tid = threadIdx.x;
-    if constexpr (KCONTIG) {
-#pragma unroll
-      for (int i = 0; i < 4 * U; ++i) {
-        const int cid = tid + i * NT;
-        reg[i] = *reinterpret_cast<const uint4*>(p + (row0 + cid / CPR) * ld + k0 + (cid % CPR) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int uid = tid + u * NT;
-        const int64_t mn = row0 + (uid % (R / 8)) * 8;
-        const int64_t kk = k0 + (uid / (R / 8)) * 4;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          reg[u * 4 + q] = *reinterpret_cast<const uint4*>(p + (kk + q) * ld + mn);
-      }
-    }
-  }
-
-  // Direct global -> LDS copy of a K-contiguous tile, no registers involved
-  // (gfx950 global_load_lds_dwordx4). One wave instruction fills 8 LDS rows
-  // (1 KB): lane l lands in slot l, i.e. row l/8 at physical chunk l%8, so it
-  // loads the logical chunk the swizzle maps there. Every access is in bounds
-  // (interior tile, whole K-tile).
+  // Direct global -> LDS copy of a K-contiguous tile of R rows (interior,
+  // whole K-tile). Lane l of an instruction lands in LDS slot l, i.e. row
+  // l / CPR at physical chunk l % CPR, so it loads the logical chunk the
+  // swizzle maps there (the swizzle is an XOR, its own inverse).
   template <int R>
   static __device__ inline void dma_tile(const uint16_t* __restrict__ p, int64_t ld,
                                          int64_t row0, int64_t k0, uint4* region) {
-    constexpr int NW = NT / 64;
-    constexpr int INSTS = R / 8 / NW;
-    static_assert(INSTS * NW * 8 == R, "rows must split evenly over the waves");
+    constexpr int ROWS = 64 / CPR;
+    static_assert(dma_insts(R) * NW * ROWS == R, "rows must split evenly over the waves");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < INSTS; ++i) {
-      const int rb = (wave + i * NW) * 8;   // first row this instruction fills
-      const int r = rb + lane / 8;
-      const int c = (lane % 8) ^ ((r ^ (r >> 3)) & 7);
+    for (int i = 0; i < dma_insts(R); ++i) {
+      const int rb = (wave + i * NW) * ROWS;   // first row this instruction fills
+      const int r = rb + lane / CPR;
+      const int c = swz<CPR>(r, lane % CPR);
       const uint16_t* src = p + (row0 + r) * ld + k0 + c * 8;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(region + rb * CPR),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(region + rb * CPR), 16, 0, 0);
     }
   }
-
-  static __device__ inline void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
   // Fragments of one 16-wide K step for this wave.
   static __device__ inline void read_frags(const uint4* cur, int ks, int lane, int wave_m,
@@ -242,19 +271,22 @@ struct GemmKernel {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = wave_m * WM + i * 32 + (lane & 31);
-      fa[i] = __builtin_bit_cast(bf16x8, cur[r * CPR + swz(r, ch)]);
+      fa[i] = __builtin_bit_cast(bf16x8, cur[r * CPR + swz<CPR>(r, ch)]);
     }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int r = wave_n * WN + j * 32 + (lane & 31);
-      fb[j] = __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz(r, ch)]);
+      fb[j] = __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz<CPR>(r, ch)]);
     }
   }
 
   // MFMAs over one LDS stage, with the next K step's fragments read while the
   // current step's products run.
-  static __device__ inline void compute_stage(const uint4* cur, int lane, int wave_m, int wave_n,
-                                              floatx16 (&acc)[TM][TN]) {
+  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN]) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wave_m = wave % WAVES_M;
+    const int wave_n = wave / WAVES_M;
     constexpr int KS = BK / 16;
     bf16x8 fa[2][TM], fb[2][TN];
     read_frags(cur, 0, lane, wave_m, wave_n, fa[0], fb[0]);
@@ -268,100 +300,112 @@ struct GemmKernel {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
                                                               acc[i][j], 0, 0, 0);
     }
-
   }
 
-  // Start moving K-tile k0 of both operands towards `stage`: K-contiguous
-  // operands go straight to LDS, the others into registers (ra, rb).
-  static __device__ inline void issue_fast(const GemmArgs& g, int64_t m0, int64_t n0, int64_t k0,
-                                           uint4* stage, uint4* ra, uint4* rb) {
+  // Both operands K-contiguous, interior block, whole K-tiles: every tile is
+  // copied straight into LDS, STAGES - 1 tiles ahead of the one multiplied.
+  // At the top of iteration t, tile t's copies must have landed (each wave
+  // waits for its own, the barrier for everyone's) and stage (t - 1) % STAGES
+  // is free again, so tile t + STAGES - 1 goes there.
+  static __device__ inline void mainloop_dma(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
+                                             int64_t m0, int64_t n0, int64_t kb, int nkf,
+                                             floatx16 (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
-    if constexpr (A_K)
-      dma_tile<BM>(A, g.lda, m0, k0, stage);
-    else
-      load_tile_fast<BM, UA, false>(A, g.lda, m0, k0, ra);
-    if constexpr (B_K)
-      dma_tile<BN>(B, g.ldb, n0, k0, stage + BM * CPR);
-    else
-      load_tile_fast<BN, UB, false>(B, g.ldb, n0, k0, rb);
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) {
+      if (p < nkf) {
+        dma_tile<BM>(A, g.lda, m0, kb + static_cast<int64_t>(p) * BK, lds[p]);
+        dma_tile<BN>(B, g.ldb, n0, kb + static_cast<int64_t>(p) * BK, lds[p] + BM * CPR);
+      }
+    }
+    for (int t = 0; t < nkf; ++t) {
+      // Tiles t+1 .. min(t + STAGES - 2, nkf - 1) may still be in flight.
+      wait_vmem_upto(min(STAGES - 2, nkf - 1 - t) * DMA_PER_TILE);
+      __syncthreads();
+      const int tn = t + STAGES - 1;
+      if (tn < nkf) {
+        uint4* st = lds[tn % STAGES];
+        dma_tile<BM>(A, g.lda, m0, kb + static_cast<int64_t>(tn) * BK, st);
+        dma_tile<BN>(B, g.ldb, n0, kb + static_cast<int64_t>(tn) * BK, st + BM * CPR);
+      }
+      compute_stage(lds[t % STAGES], acc);
+    }
+    __syncthreads();
   }
 
-  // Registers staged by issue_fast -> LDS (the transposing writes).
-  static __device__ inline void finish_fast(uint4* stage, const uint4* ra, const uint4* rb) {
-    if constexpr (!A_K) store_tile<BM, UA, false>(stage, 0, ra);
-    if constexpr (!B_K) store_tile<BN, UB, false>(stage, BM, rb);
-  }
-
-  // Whole K-tiles of an interior block over two LDS stages (two LDS arrays):
-  // the copies into one stage are in flight while the other is read.
-  static __device__ inline void mainloop_fast(const GemmArgs& g, uint4* lds0, uint4* lds1,
-                                              int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                              floatx16 (&acc)[TM][TN]) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wave_m = wave % WAVES_M;
-    const int wave_n = wave / WAVES_M;
-    uint4 ra[A_K ? 1 : 4 * UA], rb[B_K ? 1 : 4 * UB];
-    issue_fast(g, m0, n0, kb, lds0, ra, rb);
-    finish_fast(lds0, ra, rb);
-    wait_vmem();
+  // One operand M/N-contiguous, interior block, whole K-tiles, two stages:
+  // the K-contiguous operand is copied straight into the next stage and the
+  // other staged through registers while the current stage is multiplied.
+  static __device__ inline void mainloop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
+                                               int64_t m0, int64_t n0, int64_t kb, int nkf,
+                                               floatx16 (&acc)[TM][TN]) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    uint4 ra[A_K ? 1 : regs(BM, false)], rb[B_K ? 1 : regs(BN, false)];
+    auto issue = [&](int64_t k0, uint4* st) {
+      if constexpr (A_K) dma_tile<BM>(A, g.lda, m0, k0, st);
+      else load_tile_fast<BM, false>(A, g.lda, m0, k0, ra);
+      if constexpr (B_K) dma_tile<BN>(B, g.ldb, n0, k0, st + BM * CPR);
+      else load_tile_fast<BN, false>(B, g.ldb, n0, k0, rb);
+    };
+    auto finish = [&](uint4* st) {
+      if constexpr (!A_K) store_tile<BM, false>(st, 0, ra);
+      if constexpr (!B_K) store_tile<BN, false>(st, BM, rb);
+    };
+    issue(kb, lds[0]);
+    finish(lds[0]);
+    wait_vmem_upto(0);
     __syncthreads();
     for (int t = 0; t < nkf; ++t) {
-      uint4* cur = (t & 1) ? lds1 : lds0;
-      uint4* nxt = (t & 1) ? lds0 : lds1;
+      uint4* cur = lds[t & 1];
+      uint4* nxt = lds[(t + 1) & 1];
       const bool more = t + 1 < nkf;
-      if (more) issue_fast(g, m0, n0, kb + static_cast<int64_t>(t + 1) * BK, nxt, ra, rb);
-      compute_stage(cur, lane, wave_m, wave_n, acc);
-      if (more) finish_fast(nxt, ra, rb);
-      wait_vmem();
+      if (more) issue(kb + static_cast<int64_t>(t + 1) * BK, nxt);
+      compute_stage(cur, acc);
+      if (more) finish(nxt);
+      wait_vmem_upto(0);
       __syncthreads();
     }
   }
 
   // Bounds-checked K-tiles [t0, t1) through registers (edge blocks, and the
-  // partial last K-tile of interior blocks). Two LDS stages, one barrier per
-  // K-tile; entered and left with both stages free.
-  static __device__ inline void mainloop_checked(const GemmArgs& g, uint4* lds0, uint4* lds1,
+  // partial last K-tile of interior blocks); two stages, one barrier per
+  // K-tile; entered and left with every stage free.
+  static __device__ inline void mainloop_checked(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                                  int64_t m0, int64_t n0, int64_t kb, int64_t ke,
                                                  int t0, int t1, floatx16 (&acc)[TM][TN]) {
     if (t0 >= t1) return;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wave_m = wave % WAVES_M;
-    const int wave_n = wave / WAVES_M;
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
-    uint4 ra[4 * UA], rb[4 * UB];
-    load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, kb + static_cast<int64_t>(t0) * BK, ke, ra);
-    load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, kb + static_cast<int64_t>(t0) * BK, ke, rb);
-    store_tile<BM, UA, A_K>(lds0, 0, ra);
-    store_tile<BN, UB, B_K>(lds0, BM, rb);
+    uint4 ra[regs(BM, A_K)], rb[regs(BN, B_K)];
+    load_tile<BM, A_K>(A, g.lda, m0, g.M, kb + static_cast<int64_t>(t0) * BK, ke, ra);
+    load_tile<BN, B_K>(B, g.ldb, n0, g.N, kb + static_cast<int64_t>(t0) * BK, ke, rb);
+    store_tile<BM, A_K>(lds[0], 0, ra);
+    store_tile<BN, B_K>(lds[0], BM, rb);
     __syncthreads();
     for (int t = t0; t < t1; ++t) {
-      uint4* cur = ((t - t0) & 1) ? lds1 : lds0;
-      uint4* nxt = ((t - t0) & 1) ? lds0 : lds1;
+      uint4* cur = lds[(t - t0) & 1];
+      uint4* nxt = lds[(t - t0 + 1) & 1];
       const bool more = t + 1 < t1;
       if (more) {
         const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
-        load_tile<BM, UA, A_K>(A, g.lda, m0, g.M, k0, ke, ra);
-        load_tile<BN, UB, B_K>(B, g.ldb, n0, g.N, k0, ke, rb);
+        load_tile<BM, A_K>(A, g.lda, m0, g.M, k0, ke, ra);
+        load_tile<BN, B_K>(B, g.ldb, n0, g.N, k0, ke, rb);
       }
-      compute_stage(cur, lane, wave_m, wave_n, acc);
+      compute_stage(cur, acc);
       if (more) {
-        store_tile<BM, UA, A_K>(nxt, 0, ra);
-        store_tile<BN, UB, B_K>(nxt, BM, rb);
+        store_tile<BM, A_K>(nxt, 0, ra);
+        store_tile<BN, B_K>(nxt, BM, rb);
       }
       __syncthreads();
     }
   }
 
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
-    __shared__ uint4 lds0[LDS_STAGE];
-    __shared__ uint4 lds1[LDS_STAGE];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    __shared__ uint4 lds[STAGES][LDS_STAGE];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     const int wave_m = wave % WAVES_M;
     const int wave_n = wave / WAVES_M;
 
@@ -384,10 +428,15 @@ struct GemmKernel {
 
     if (m0 + BM <= g.M && n0 + BN <= g.N) {
       const int nkf = static_cast<int>((ke - kb) / BK);   // whole K-tiles
-      if (nkf > 0) mainloop_fast(g, lds0, lds1, m0, n0, kb, nkf, acc);
-      mainloop_checked(g, lds0, lds1, m0, n0, kb, ke, nkf, nk, acc);
+      if (nkf > 0) {
+        if constexpr (A_K && B_K)
+          mainloop_dma(g, lds, m0, n0, kb, nkf, acc);
+        else
+          mainloop_mixed(g, lds, m0, n0, kb, nkf, acc);
+      }
+      mainloop_checked(g, lds, m0, n0, kb, ke, nkf, nk, acc);
     } else {
-      mainloop_checked(g, lds0, lds1, m0, n0, kb, ke, 0, nk, acc);
+      mainloop_checked(g, lds, m0, n0, kb, ke, 0, nk, acc);
     }
 
     // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
@@ -419,16 +468,25 @@ struct GemmKernel {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_K, bool B_K, int EPI>
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
+          int EPI>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g,
                                                                            int tiles_m,
                                                                            int tiles_n,
                                                                            int group_m) {
-  GemmKernel<BM, BN, WAVES_M, WAVES_N, A_K, B_K, EPI>::run(g, tiles_m, tiles_n, group_m);
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI>::run(g, tiles_m, tiles_n,
+                                                                       group_m);
 }
 
 constexpr int kWavesM = 2;
 constexpr int kWavesN = 4;
+
+// K-tile and pipeline depth per layout (see the file comment).
+template <bool A_K, bool B_K>
+struct Pipe {
+  static constexpr int BK = 64;
+  static constexpr int STAGES = 2;
+};
 
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
@@ -438,7 +496,8 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const dim3 block(kWavesM * kWavesN * 64);
   const int group_m = g.group_m > 0 ? static_cast<int>(std::min<int64_t>(g.group_m, tiles_m))
                                     : static_cast<int>(tiles_m);
-  hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, kWavesM, kWavesN, A_K, B_K, EPI>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, Pipe<A_K, B_K>::BK,
+                                       Pipe<A_K, B_K>::STAGES, kWavesM, kWavesN, A_K, B_K, EPI>),
                      grid, block, 0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
                      group_m);
   return hipGetLastError();
