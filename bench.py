@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--sweep", action="store_true",
+                   help="also time the 1024- and 8192-row workloads at 1, 8 and 32 chunks")
     return p.parse_args()
 
 
@@ -93,6 +95,52 @@ def traffic_for(cls):
     if entry.get("source_digest") != source_digest():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def sweep(fljsd, steps, warmup):
+    """ms per step and tokens/s of the two H=4096, V=128256 workloads per chunk count."""
+    import torch
+
+    import workloads
+    out = []
+    for key in ("llama3_head", "large_batch"):
+        w = workloads.WORKLOADS[key]
+        X_s, W_s, X_t, W_t = device_inputs(workloads.make_inputs(w))
+        for nc in (1, 8, 32):
+            ws = torch.empty(fljsd.fljsd_workspace_size(w.BT, w.H_s, w.H_t, w.V, fljsd.BF16, nc),
+                             dtype=torch.uint8, device="cuda")
+            out_t = (torch.empty(1, dtype=torch.float32, device="cuda"), torch.empty_like(X_s),
+                     torch.empty_like(W_s))
+            torch.cuda.reset_peak_memory_stats()
+
+            def step():
+                fljsd.fljsd_forward_backward(X_s, W_s, X_t, W_t, w.beta, w.temperature,
+                                             w.reduction, nc, workspace=ws, out=out_t)
+            for _ in range(warmup):
+                step()
+            torch.cuda.synchronize()
+            fljsd.fljsd_profile_enable(True)
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) / steps * 1e3
+            kernels = fljsd.fljsd_profile_read()
+            fljsd.fljsd_profile_enable(False)
+            rec = {"workload": key, "BT": w.BT, "num_chunks": nc, "ms_per_step": round(ms, 3),
+                   "tokens_per_s": round(w.BT / ms * 1e3, 1),
+                   "peak_hbm_mb": round(torch.cuda.max_memory_allocated() / 2**20, 1),
+                   "workspace_mb": round(ws.numel() / 2**20, 1),
+                   "kernel_ms_per_step": {c: round(k["ms"] / steps, 3) for c, k in kernels.items()
+                                          if k["launches"]}}
+            log(f"  sweep {key:12s} nc={nc:2d}: {ms:8.2f} ms/step  {rec['tokens_per_s']:>10,.0f} tokens/s  "
+                f"peak {rec['peak_hbm_mb']:.0f} MB  " +
+                " ".join(f"{c}={v:.2f}" for c, v in rec["kernel_ms_per_step"].items()))
+            out.append(rec)
+            del ws, out_t
+        del X_s, W_s, X_t, W_t
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(inp, w, rows):
@@ -220,6 +268,8 @@ def main():
                         "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4)}
                     for c, r in per_class.items()},
     }
+    if args.sweep:
+        result["sweep"] = sweep(fljsd, max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         del X_s, W_s, X_t, W_t, ws, gX, gW
         torch.cuda.empty_cache()
