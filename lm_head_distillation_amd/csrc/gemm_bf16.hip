@@ -110,6 +110,13 @@ struct GemmKernel {
   static_assert(CPR == 4 || CPR == 8, "K-tile of 32 or 64");
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
   static_assert(STAGES == 2 || (A_K && B_K), "deep pipelines need two K-contiguous operands");
+  // The accumulating epilogue reads, adds to and rewrites C. It computes the
+  // transposed 32x32 products (B's fragment first), which leaves four
+  // consecutive output columns of one row in each group of four accumulator
+  // registers: the old values then come in as 8-byte loads, all issued
+  // before any is used, so a block pays one memory latency instead of one
+  // per batch of 2-byte loads.
+  static constexpr bool SWAP_D = EPI == kEpiAccumulate;
 
   // Register path: a K-contiguous tile of R rows moves in 16-byte chunks,
   // chunks(R) per thread; an M/N-contiguous one in 8 x 4 blocks, units(R) per
@@ -297,8 +304,10 @@ struct GemmKernel {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
-                                                              acc[i][j], 0, 0, 0);
+          acc[i][j] = SWAP_D ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
+                                                                       acc[i][j], 0, 0, 0)
+                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
+                                                                       acc[i][j], 0, 0, 0);
     }
   }
 
@@ -402,6 +411,69 @@ struct GemmKernel {
     }
   }
 
+  // C = C + A B with the transposed accumulator layout (SWAP_D): register r
+  // of lane l in a 32x32 tile holds row l%32 and column 8*(r/4) + 4*(l/32) +
+  // r%4. All old values are loaded first, then added (fp32) and rounded once.
+  static __device__ inline void epilogue_accumulate(const GemmArgs& g, int64_t m0, int64_t n0,
+                                                    int lane, int wave_m, int wave_n,
+                                                    floatx16 (&acc)[TM][TN]) {
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    const bool vec_ok = (g.ldc & 3) == 0;
+    uint2 old[TM][TN][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wave_m * WM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          uint2 v = make_uint2(0, 0);
+          if (m < g.M) {
+            const uint16_t* src = C + m * g.ldc + n;
+            if (vec_ok && n + 4 <= g.N) {
+              v = *reinterpret_cast<const uint2*>(src);
+            } else {
+              uint16_t e[4] = {0, 0, 0, 0};
+              for (int k = 0; k < 4; ++k)
+                if (n + k < g.N) e[k] = src[k];
+              v = make_uint2(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16));
+            }
+          }
+          old[i][j][q] = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t m = m0 + wave_m * WM + i * 32 + (lane & 31);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (n >= g.N) continue;
+          const uint2 o = old[i][j][q];
+          const float out[4] = {acc[i][j][4 * q] + __uint_as_float(o.x << 16),
+                                acc[i][j][4 * q + 1] + __uint_as_float(o.x & 0xffff0000u),
+                                acc[i][j][4 * q + 2] + __uint_as_float(o.y << 16),
+                                acc[i][j][4 * q + 3] + __uint_as_float(o.y & 0xffff0000u)};
+          uint16_t* dst = C + m * g.ldc + n;
+          if (vec_ok && n + 4 <= g.N) {
+            uint2 w;
+            w.x = f32_to_bf16_bits(out[0]) | (f32_to_bf16_bits(out[1]) << 16);
+            w.y = f32_to_bf16_bits(out[2]) | (f32_to_bf16_bits(out[3]) << 16);
+            *reinterpret_cast<uint2*>(dst) = w;
+          } else {
+            for (int k = 0; k < 4; ++k)
+              if (n + k < g.N) dst[k] = static_cast<uint16_t>(f32_to_bf16_bits(out[k]));
+          }
+        }
+      }
+    }
+  }
+
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
@@ -439,7 +511,11 @@ struct GemmKernel {
       mainloop_checked(g, lds, m0, n0, kb, ke, 0, nk, acc);
     }
 
-    // Epilogue. Accumulator register r of lane l in a 32x32 tile holds
+    if constexpr (SWAP_D) {
+      epilogue_accumulate(g, m0, n0, lane, wave_m, wave_n, acc);
+      return;
+    }
+    // Store epilogues. Accumulator register r of lane l in a 32x32 tile holds
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
