@@ -114,6 +114,41 @@ int fljsd_forward_backward(const void* X_s, const void* W_s,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* Flag bits of fljsd_forward_backward_ex. */
+#define FLJSD_ACCUMULATE_GRAD_W 1u  /* add this call's weight gradient to the
+                                       values grad_W_s already holds */
+
+/*
+ * fljsd_forward_backward_ex - fljsd_forward_backward with a choice of
+ * weight-gradient accumulation (PR #1429 Details: the accum_dtype=float32
+ * path, where the per-chunk products add up in fp32).
+ *
+ * Same arguments, outputs, workspace and errors as fljsd_forward_backward,
+ * plus:
+ *   grad_w_dtype  element type of grad_W_s: `dtype`, or FLJSD_F32 with
+ *                 FLJSD_BF16 inputs. With FLJSD_F32 the bf16 products
+ *                 (fp32-accumulated inside each GEMM) are stored and summed
+ *                 over chunks in fp32 with no rounding in between, so the
+ *                 result does not carry one bf16 rounding per chunk. Any
+ *                 other value is FLJSD_EDTYPE.
+ *   flags         0, or FLJSD_ACCUMULATE_GRAD_W: the first chunk adds to
+ *                 grad_W_s instead of overwriting it, so grad_W_s must hold
+ *                 initialized values on entry (for summing gradients over
+ *                 several calls, e.g. micro-batches of one optimizer step).
+ *                 Unknown bits are FLJSD_EINVAL.
+ * fljsd_forward_backward(...) is fljsd_forward_backward_ex(..., dtype, 0, ...).
+ * The workspace size does not depend on these two arguments.
+ */
+int fljsd_forward_backward_ex(const void* X_s, const void* W_s,
+                              const void* X_t, const void* W_t,
+                              int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
+                              int dtype, float beta, float temperature,
+                              int reduction, int num_chunks,
+                              float* loss, void* grad_X_s, void* grad_W_s,
+                              int grad_w_dtype, unsigned flags,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /*
  * fljsd_generalized_jsd - the loss step alone over given logits: the three
  * online-softmax passes (PR #1352 Details: statistics m/d for both

@@ -137,8 +137,9 @@ hipError_t gemm(int dtype, const GemmArgs& g, hipStream_t s) {
 
 double gemm_bytes(const GemmArgs& g, int es) {
   const double in = (static_cast<double>(g.M) * g.K + static_cast<double>(g.N) * g.K) * es;
-  const double out_es = g.epilogue == kEpiPartialF32 ? 4.0 : es;
-  const double out = static_cast<double>(g.M) * g.N * out_es * (g.epilogue == kEpiAccumulate ? 2 : 1);
+  const bool f32_out = g.epilogue == kEpiPartialF32 || g.epilogue == kEpiAccumulateF32;
+  const bool rmw = g.epilogue == kEpiAccumulate || g.epilogue == kEpiAccumulateF32;
+  const double out = static_cast<double>(g.M) * g.N * (f32_out ? 4.0 : es) * (rmw ? 2 : 1);
   return in + out;
 }
 
@@ -253,6 +254,18 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
                                         int reduction, int num_chunks, float* loss,
                                         void* grad_X_s, void* grad_W_s, void* workspace,
                                         size_t workspace_bytes, void* stream) {
+  return fljsd_forward_backward_ex(X_s, W_s, X_t, W_t, BT, H_s, H_t, V, dtype, beta, temperature,
+                                   reduction, num_chunks, loss, grad_X_s, grad_W_s, dtype, 0u,
+                                   workspace, workspace_bytes, stream);
+}
+
+FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, const void* X_t,
+                                           const void* W_t, int64_t BT, int64_t H_s,
+                                           int64_t H_t, int64_t V, int dtype, float beta,
+                                           float temperature, int reduction, int num_chunks,
+                                           float* loss, void* grad_X_s, void* grad_W_s,
+                                           int grad_w_dtype, unsigned flags, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (!X_s || !W_s || !X_t || !W_t || !loss)
     return fail(FLJSD_EINVAL, "X_s, W_s, X_t, W_t and loss must not be NULL");
@@ -262,6 +275,12 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
   int rc = check_common(dtype, beta, temperature, reduction);
   if (rc != FLJSD_OK) return rc;
   if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
+  if (grad_w_dtype != dtype && !(dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32))
+    return fail(FLJSD_EDTYPE, "grad_w_dtype must equal dtype, or be F32 with BF16 inputs");
+  if (flags & ~static_cast<unsigned>(FLJSD_ACCUMULATE_GRAD_W))
+    return fail(FLJSD_EINVAL, "unknown flag bits");
+  const bool gw_f32_acc = dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32;
+  const bool gw_add_existing = (flags & FLJSD_ACCUMULATE_GRAD_W) != 0;
   const int vec = dtype_vec(dtype);
   const void* ptrs[] = {X_s, W_s, X_t, W_t, loss, grad_X_s, grad_W_s, workspace};
   for (const void* p : ptrs)
@@ -393,7 +412,14 @@ FLJSD_EXPORT int fljsd_forward_backward(const void* X_s, const void* W_s, const 
       g.ldc = H_s;
       g.a_kcontig = false;
       g.b_kcontig = false;
-      g.epilogue = ci == 0 ? kEpiStore : kEpiAccumulate;
+      // Chunk 0 overwrites unless the caller asked to add to grad_W's
+      // contents; later chunks add. An fp32 grad_W takes the bf16 product
+      // unrounded (one-split fp32 store, or fp32 read-add-write).
+      const bool add = ci > 0 || gw_add_existing;
+      if (gw_f32_acc)
+        g.epilogue = add ? kEpiAccumulateF32 : kEpiPartialF32;
+      else
+        g.epilogue = add ? kEpiAccumulate : kEpiStore;
       g.splitk = 1;
       g.k_per_split = rows;
       g.group_m = 2;

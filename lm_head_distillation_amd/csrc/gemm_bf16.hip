@@ -86,6 +86,61 @@ __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
 }
 
+// Four consecutive outputs of one row of C: bf16 (8 bytes) or fp32 (16
+// bytes). `left` is how many columns remain in the row (fewer than four only
+// at the right edge); `vec` says the row stride keeps whole quads aligned.
+template <class Out>
+struct QuadOf;
+template <>
+struct QuadOf<uint16_t> { using type = uint2; };
+template <>
+struct QuadOf<float> { using type = float4; };
+
+__device__ inline uint2 load_quad(const uint16_t* p, int64_t left, bool vec) {
+  if (vec && left >= 4) return *reinterpret_cast<const uint2*>(p);
+  uint16_t e[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) e[k] = k < left ? p[k] : uint16_t(0);
+  return make_uint2(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16));
+}
+__device__ inline float4 load_quad(const float* p, int64_t left, bool vec) {
+  if (vec && left >= 4) return *reinterpret_cast<const float4*>(p);
+  float e[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) e[k] = k < left ? p[k] : 0.f;
+  return make_float4(e[0], e[1], e[2], e[3]);
+}
+__device__ inline void unpack_quad(uint2 q, float (&v)[4]) {
+  v[0] = __uint_as_float(q.x << 16);
+  v[1] = __uint_as_float(q.x & 0xffff0000u);
+  v[2] = __uint_as_float(q.y << 16);
+  v[3] = __uint_as_float(q.y & 0xffff0000u);
+}
+__device__ inline void unpack_quad(float4 q, float (&v)[4]) {
+  v[0] = q.x;
+  v[1] = q.y;
+  v[2] = q.z;
+  v[3] = q.w;
+}
+__device__ inline void store_quad(uint16_t* p, const float (&v)[4], int64_t left, bool vec) {
+  if (vec && left >= 4) {
+    *reinterpret_cast<uint2*>(p) =
+        make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                   f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+    return;
+  }
+  for (int k = 0; k < 4; ++k)
+    if (k < left) p[k] = static_cast<uint16_t>(f32_to_bf16_bits(v[k]));
+}
+__device__ inline void store_quad(float* p, const float (&v)[4], int64_t left, bool vec) {
+  if (vec && left >= 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    return;
+  }
+  for (int k = 0; k < 4; ++k)
+    if (k < left) p[k] = v[k];
+}
+
 // Wait until at most n of this wave's vector-memory loads are outstanding
 // (loads complete in issue order). Counts this file does not use wait for all.
 __device__ inline void wait_vmem_upto(int n) {
@@ -116,7 +171,7 @@ struct GemmKernel {
   // registers: the old values then come in as 8-byte loads, all issued
   // before any is used, so a block pays one memory latency instead of one
   // per batch of 2-byte loads.
-  static constexpr bool SWAP_D = EPI == kEpiAccumulate;
+  static constexpr bool SWAP_D = EPI == kEpiAccumulate || EPI == kEpiAccumulateF32;
 
   // Register path: a K-contiguous tile of R rows moves in 16-byte chunks,
   // chunks(R) per thread; an M/N-contiguous one in 8 x 4 blocks, units(R) per
@@ -413,61 +468,49 @@ struct GemmKernel {
 
   // C = C + A B with the transposed accumulator layout (SWAP_D): register r
   // of lane l in a 32x32 tile holds row l%32 and column 8*(r/4) + 4*(l/32) +
-  // r%4. All old values are loaded first, then added (fp32) and rounded once.
+  // r%4, so registers 4q..4q+3 are four consecutive columns of one row. The
+  // old values of IG row blocks are all loaded before any is used (64
+  // registers in flight), then added in fp32 and rounded once to Out.
+  template <class Out>
   static __device__ inline void epilogue_accumulate(const GemmArgs& g, int64_t m0, int64_t n0,
                                                     int lane, int wave_m, int wave_n,
                                                     floatx16 (&acc)[TM][TN]) {
-    uint16_t* C = static_cast<uint16_t*>(g.C);
+    using Quad = typename QuadOf<Out>::type;
+    constexpr int IG = sizeof(Out) == 4 ? (TM >= 2 ? TM / 2 : 1) : TM;
+    static_assert(TM % IG == 0, "row groups");
+    Out* C = static_cast<Out*>(g.C);
     const bool vec_ok = (g.ldc & 3) == 0;
-    uint2 old[TM][TN][4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wave_m * WM + i * 32 + (lane & 31);
+    for (int i0 = 0; i0 < TM; i0 += IG) {
+      Quad old[IG][TN][4];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
+      for (int i = 0; i < IG; ++i) {
+        const int64_t m = m0 + wave_m * WM + (i0 + i) * 32 + (lane & 31);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-          uint2 v = make_uint2(0, 0);
-          if (m < g.M) {
-            const uint16_t* src = C + m * g.ldc + n;
-            if (vec_ok && n + 4 <= g.N) {
-              v = *reinterpret_cast<const uint2*>(src);
-            } else {
-              uint16_t e[4] = {0, 0, 0, 0};
-              for (int k = 0; k < 4; ++k)
-                if (n + k < g.N) e[k] = src[k];
-              v = make_uint2(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16));
-            }
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+            old[i][j][q] = m < g.M ? load_quad(C + m * g.ldc + n, g.N - n, vec_ok)
+                                   : Quad{};
           }
-          old[i][j][q] = v;
         }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t m = m0 + wave_m * WM + i * 32 + (lane & 31);
-      if (m >= g.M) continue;
+      for (int i = 0; i < IG; ++i) {
+        const int64_t m = m0 + wave_m * WM + (i0 + i) * 32 + (lane & 31);
+        if (m >= g.M) continue;
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-          if (n >= g.N) continue;
-          const uint2 o = old[i][j][q];
-          const float out[4] = {acc[i][j][4 * q] + __uint_as_float(o.x << 16),
-                                acc[i][j][4 * q + 1] + __uint_as_float(o.x & 0xffff0000u),
-                                acc[i][j][4 * q + 2] + __uint_as_float(o.y << 16),
-                                acc[i][j][4 * q + 3] + __uint_as_float(o.y & 0xffff0000u)};
-          uint16_t* dst = C + m * g.ldc + n;
-          if (vec_ok && n + 4 <= g.N) {
-            uint2 w;
-            w.x = f32_to_bf16_bits(out[0]) | (f32_to_bf16_bits(out[1]) << 16);
-            w.y = f32_to_bf16_bits(out[2]) | (f32_to_bf16_bits(out[3]) << 16);
-            *reinterpret_cast<uint2*>(dst) = w;
-          } else {
-            for (int k = 0; k < 4; ++k)
-              if (n + k < g.N) dst[k] = static_cast<uint16_t>(f32_to_bf16_bits(out[k]));
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+            if (n >= g.N) continue;
+            float v[4];
+            unpack_quad(old[i][j][q], v);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] += acc[i0 + i][j][4 * q + k];
+            store_quad(C + m * g.ldc + n, v, g.N - n, vec_ok);
           }
         }
       }
@@ -511,8 +554,11 @@ struct GemmKernel {
       mainloop_checked(g, lds, m0, n0, kb, ke, 0, nk, acc);
     }
 
-    if constexpr (SWAP_D) {
-      epilogue_accumulate(g, m0, n0, lane, wave_m, wave_n, acc);
+    if constexpr (EPI == kEpiAccumulate) {
+      epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
+      return;
+    } else if constexpr (EPI == kEpiAccumulateF32) {
+      epilogue_accumulate<float>(g, m0, n0, lane, wave_m, wave_n, acc);
       return;
     }
     // Store epilogues. Accumulator register r of lane l in a 32x32 tile holds
@@ -584,7 +630,12 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
   switch (g.epilogue) {
     case kEpiStore: return launch_cfg<A_K, B_K, kEpiStore>(g, s);
     case kEpiAccumulate: return launch_cfg<A_K, B_K, kEpiAccumulate>(g, s);
-    default: return launch_cfg<A_K, B_K, kEpiPartialF32>(g, s);
+    case kEpiPartialF32: return launch_cfg<A_K, B_K, kEpiPartialF32>(g, s);
+    case kEpiAccumulateF32:
+      // Only the weight-gradient product accumulates into an fp32 C.
+      if constexpr (!A_K && !B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
 }
 

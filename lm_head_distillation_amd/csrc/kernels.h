@@ -49,6 +49,8 @@ enum GemmEpilogue : int {
   kEpiStore = 0,        // C = A B, rounded once to the dtype
   kEpiAccumulate = 1,   // C = C + A B, added in fp32 and rounded once
   kEpiPartialF32 = 2,   // fp32 partial sum of one K-split at C + split * M * ldc
+                        // (with one split: C = A B stored in fp32)
+  kEpiAccumulateF32 = 3,  // fp32 C = C + A B, no rounding (bf16 operands)
 };
 
 struct GemmArgs {

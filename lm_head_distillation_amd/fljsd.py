@@ -52,6 +52,10 @@ def load_library() -> ctypes.CDLL:
     lib.fljsd_forward_backward.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, cint, f32, f32,
                                            cint, cint, vp, vp, vp, vp, sz, vp]
     lib.fljsd_forward_backward.restype = cint
+    lib.fljsd_forward_backward_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, cint, f32, f32,
+                                              cint, cint, vp, vp, vp, cint, ctypes.c_uint, vp, sz,
+                                              vp]
+    lib.fljsd_forward_backward_ex.restype = cint
     lib.fljsd_generalized_jsd.argtypes = [vp, vp, i64, i64, i64, cint, f32, f32, cint, vp, vp,
                                           vp, sz, vp]
     lib.fljsd_generalized_jsd.restype = cint
@@ -138,6 +142,9 @@ def default_budget_bytes() -> int:
     return free // 2
 
 
+FLJSD_ACCUMULATE_GRAD_W = 1
+
+
 def fljsd_forward_backward(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tensor,
                            W_t: torch.Tensor, beta: float, temperature: float,
                            reduction: str = "batchmean", num_chunks: int = 0, *,
@@ -151,6 +158,26 @@ def fljsd_forward_backward(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tens
     budget (the given workspace's size, else default_budget_bytes()).
     Gradients not asked for are returned as None.
     """
+    return fljsd_forward_backward_ex(X_s, W_s, X_t, W_t, beta, temperature, reduction,
+                                     num_chunks, grad_w_dtype=None, flags=0,
+                                     grad_input=grad_input, grad_weight=grad_weight,
+                                     workspace=workspace, out=out, stream=stream, _entry="plain")
+
+
+def fljsd_forward_backward_ex(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tensor,
+                              W_t: torch.Tensor, beta: float, temperature: float,
+                              reduction: str = "batchmean", num_chunks: int = 0, *,
+                              grad_w_dtype: Optional[torch.dtype] = None, flags: int = 0,
+                              grad_input: bool = True, grad_weight: bool = True,
+                              workspace: Optional[torch.Tensor] = None,
+                              out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]] = None,
+                              stream=None, _entry: str = "ex"):
+    """fljsd_forward_backward with a weight-gradient dtype and flags.
+
+    grad_w_dtype: None (the input dtype) or torch.float32 (fp32 accumulation
+    over chunks for bf16 inputs). flags: 0 or FLJSD_ACCUMULATE_GRAD_W, which
+    adds to the grad_W_s given in ``out`` instead of overwriting it.
+    """
     lib = load_library()
     _require_device(X_s, W_s, X_t, W_t)
     dt = _dtype_code(X_s)
@@ -163,6 +190,10 @@ def fljsd_forward_backward(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tens
     if W_s.shape != (V, H_s) or X_t.shape != (BT, H_t) or W_t.shape != (V, H_t):
         raise ValueError("shape mismatch: X_s [BT,H_s], W_s [V,H_s], X_t [BT,H_t], W_t [V,H_t]")
     red = _reduction_code(reduction)
+    gw_torch = X_s.dtype if grad_w_dtype is None else grad_w_dtype
+    gw_code = {torch.float32: 0, torch.bfloat16: 1}.get(gw_torch, -1)
+    if (flags & FLJSD_ACCUMULATE_GRAD_W) and (out is None or out[2] is None):
+        raise ValueError("FLJSD_ACCUMULATE_GRAD_W needs the grad_W_s to add to, passed in `out`")
     nc = int(num_chunks)
     if nc == 0:
         budget = workspace.numel() * workspace.element_size() if workspace is not None else default_budget_bytes()
@@ -175,11 +206,14 @@ def fljsd_forward_backward(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tens
     else:
         loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X_s.device)
         gX = torch.empty_like(X_s) if grad_input else None
-        gW = torch.empty_like(W_s) if grad_weight else None
-    rc = lib.fljsd_forward_backward(
-        X_s.data_ptr(), W_s.data_ptr(), X_t.data_ptr(), W_t.data_ptr(), BT, H_s, H_t, V, dt,
-        float(beta), float(temperature), red, nc, loss.data_ptr(), _ptr(gX), _ptr(gW),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+        gW = torch.empty(V, H_s, dtype=gw_torch, device=X_s.device) if grad_weight else None
+    args = (X_s.data_ptr(), W_s.data_ptr(), X_t.data_ptr(), W_t.data_ptr(), BT, H_s, H_t, V, dt,
+            float(beta), float(temperature), red, nc, loss.data_ptr(), _ptr(gX), _ptr(gW))
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    if _entry == "plain":
+        rc = lib.fljsd_forward_backward(*args, *tail)
+    else:
+        rc = lib.fljsd_forward_backward_ex(*args, gw_code, int(flags), *tail)
     _check(rc)
     return (loss if red == 3 else loss[0]), gX, gW
 

@@ -39,7 +39,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("fljsd_forward_backward", "fljsd_generalized_jsd", "fljsd_workspace_size",
+    for n in ("fljsd_forward_backward", "fljsd_forward_backward_ex", "fljsd_generalized_jsd",
+              "fljsd_workspace_size",
               "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
               "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read"):
         assert n in names
@@ -60,7 +61,11 @@ def test_header_compiles_as_c():
            'int (*fb)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
            ' int64_t, int, float, float, int, int, float*, void*, void*, void*, size_t, void*)'
            ' = fljsd_forward_backward;\n'
-           'int main(void){return fb == 0 && FLJSD_KCLASS_COUNT == 8;}\n')
+           'int (*fbx)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
+           ' int64_t, int, float, float, int, int, float*, void*, void*, int, unsigned, void*, size_t,'
+           ' void*) = fljsd_forward_backward_ex;\n'
+           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 8 '
+           '&& FLJSD_ACCUMULATE_GRAD_W == 1u;}\n')
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-",
                           "-I", os.path.join(ROOT, "include")], input=src, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
@@ -154,6 +159,32 @@ def fb(lib, **over):
 ])
 def test_forward_backward_rejects(lib, over, code):
     assert fb(lib, **over) == code
+    assert lib.fljsd_last_error()
+
+
+def fbx(lib, **over):
+    """fljsd_forward_backward_ex with fake pointers; always at least one
+    invalid argument."""
+    a = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
+             beta=0.5, T=1.0, reduction=0, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, gw_dtype=BF16,
+             flags=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return lib.fljsd_forward_backward_ex(a["X_s"], a["W_s"], a["X_t"], a["W_t"], a["BT"], a["H_s"],
+                                         a["H_t"], a["V"], a["dtype"], a["beta"], a["T"],
+                                         a["reduction"], a["nc"], a["loss"], a["gX"], a["gW"],
+                                         a["gw_dtype"], a["flags"], a["ws"], a["ws_bytes"],
+                                         a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(gw_dtype=2), EDTYPE), (dict(gw_dtype=-1), EDTYPE),
+    (dict(dtype=F32, gw_dtype=BF16), EDTYPE),
+    (dict(flags=2), EINVAL), (dict(flags=0x80000001), EINVAL),
+    (dict(gw_dtype=F32, X_s=None), EINVAL), (dict(gw_dtype=F32, flags=1, ws_bytes=100), EWORKSPACE),
+    (dict(gw_dtype=F32, gW=FAKE + 8), EALIGN),
+])
+def test_forward_backward_ex_rejects(lib, over, code):
+    assert fbx(lib, **over) == code
     assert lib.fljsd_last_error()
 
 
