@@ -343,8 +343,11 @@ struct GemmKernel {
   }
 
   // MFMAs over one LDS stage, with the next K step's fragments read while the
-  // current step's products run.
-  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN]) {
+  // current step's products run. hook(ks) runs before step ks's MFMAs (the
+  // main loops issue the next tile's global loads from it).
+  template <class Hook>
+  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN],
+                                              Hook&& hook) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wave_m = wave % WAVES_M;
@@ -355,6 +358,7 @@ struct GemmKernel {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks + 1 < KS) read_frags(cur, ks + 1, lane, wave_m, wave_n, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      hook(ks);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -363,6 +367,41 @@ struct GemmKernel {
                                                                        acc[i][j], 0, 0, 0)
                              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
                                                                        acc[i][j], 0, 0, 0);
+    }
+  }
+  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN]) {
+    compute_stage(cur, acc, [](int) {});
+  }
+
+  // Two-stage schedules stagger the next tile's loads between the two waves
+  // that share a SIMD (waves w and w + NW/2): the first half issues them
+  // before K step 0, the second half before step kLateStep. While one wave
+  // waits for its loads to be accepted by the memory pipeline, the other
+  // keeps the SIMD's matrix core busy. Measured on the 8192 x 128256 x 4096
+  // logits product: 9% faster than every wave issuing at step 0.
+  static constexpr int kLateStep = BK / 32;
+  static __device__ inline bool late_wave() { return (threadIdx.x >> 6) >= NW / 2; }
+
+  template <int STEP>
+  static __device__ inline void loop_dma2(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
+                                          int64_t n0, int64_t kb, int nkf,
+                                          floatx16 (&acc)[TM][TN]) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    for (int t = 0; t < nkf; ++t) {
+      wait_vmem_upto(0);
+      __syncthreads();
+      const bool more = t + 1 < nkf;
+      uint4* st = lds[(t + 1) & 1];
+      const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
+      auto issue = [&] {
+        dma_tile<BM>(A, g.lda, m0, k0, st);
+        dma_tile<BN>(B, g.ldb, n0, k0, st + BM * CPR);
+      };
+      if (STEP == 0 && more) issue();
+      compute_stage(lds[t & 1], acc, [&](int ks) {
+        if (STEP > 0 && more && ks == STEP) issue();
+      });
     }
   }
 
@@ -376,6 +415,16 @@ struct GemmKernel {
                                              floatx16 (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    if constexpr (STAGES == 2) {
+      dma_tile<BM>(A, g.lda, m0, kb, lds[0]);
+      dma_tile<BN>(B, g.ldb, n0, kb, lds[0] + BM * CPR);
+      if (late_wave())
+        loop_dma2<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
+      else
+        loop_dma2<0>(g, lds, m0, n0, kb, nkf, acc);
+      __syncthreads();
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p) {
       if (p < nkf) {
@@ -398,12 +447,15 @@ struct GemmKernel {
     __syncthreads();
   }
 
-  // One operand M/N-contiguous, interior block, whole K-tiles, two stages:
-  // the K-contiguous operand is copied straight into the next stage and the
-  // other staged through registers while the current stage is multiplied.
-  static __device__ inline void mainloop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
-                                               int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                               floatx16 (&acc)[TM][TN]) {
+  // One or both operands M/N-contiguous, interior block, whole K-tiles, two
+  // stages: a K-contiguous operand is copied straight into the next stage
+  // and an M/N-contiguous one staged through registers while the current
+  // stage is multiplied. Loads for the next tile are issued before the
+  // stage's first fragment reads (STEP 0) or before K step STEP.
+  template <int STEP>
+  static __device__ inline void loop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
+                                           int64_t m0, int64_t n0, int64_t kb, int nkf,
+                                           floatx16 (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     uint4 ra[A_K ? 1 : regs(BM, false)], rb[B_K ? 1 : regs(BN, false)];
@@ -425,11 +477,61 @@ struct GemmKernel {
       uint4* cur = lds[t & 1];
       uint4* nxt = lds[(t + 1) & 1];
       const bool more = t + 1 < nkf;
-      if (more) issue(kb + static_cast<int64_t>(t + 1) * BK, nxt);
-      compute_stage(cur, acc);
+      const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
+      if (STEP == 0 && more) issue(k0, nxt);
+      compute_stage(cur, acc, [&](int ks) {
+        if (STEP > 0 && more && ks == STEP) issue(k0, nxt);
+      });
       if (more) finish(nxt);
       wait_vmem_upto(0);
       __syncthreads();
+    }
+  }
+
+  // Both operands through registers: every wave issues the next tile's
+  // loads before the stage's MFMAs (the staggered order spills registers
+  // here, and measured slower).
+  static __device__ inline void loop_regs(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
+                                          int64_t n0, int64_t kb, int nkf,
+                                          floatx16 (&acc)[TM][TN]) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    uint4 ra[regs(BM, false)], rb[regs(BN, false)];
+    load_tile_fast<BM, false>(A, g.lda, m0, kb, ra);
+    load_tile_fast<BN, false>(B, g.ldb, n0, kb, rb);
+    store_tile<BM, false>(lds[0], 0, ra);
+    store_tile<BN, false>(lds[0], BM, rb);
+    wait_vmem_upto(0);
+    __syncthreads();
+    for (int t = 0; t < nkf; ++t) {
+      uint4* cur = lds[t & 1];
+      uint4* nxt = lds[(t + 1) & 1];
+      const bool more = t + 1 < nkf;
+      if (more) {
+        const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
+        load_tile_fast<BM, false>(A, g.lda, m0, k0, ra);
+        load_tile_fast<BN, false>(B, g.ldb, n0, k0, rb);
+      }
+      compute_stage(cur, acc);
+      if (more) {
+        store_tile<BM, false>(nxt, 0, ra);
+        store_tile<BN, false>(nxt, BM, rb);
+      }
+      wait_vmem_upto(0);
+      __syncthreads();
+    }
+  }
+
+  static __device__ inline void mainloop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
+                                               int64_t m0, int64_t n0, int64_t kb, int nkf,
+                                               floatx16 (&acc)[TM][TN]) {
+    if constexpr (A_K || B_K) {
+      if (late_wave())
+        loop_mixed<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
+      else
+        loop_mixed<0>(g, lds, m0, n0, kb, nkf, acc);
+    } else {
+      loop_regs(g, lds, m0, n0, kb, nkf, acc);
     }
   }
 
