@@ -214,7 +214,8 @@ const char* fljsd_last_error(void);
 #define FLJSD_KCLASS_SPLITK_REDUCE 5    /* split-K partial sums -> grad_X */
 #define FLJSD_KCLASS_GEMM_GRAD_WEIGHT 6 /* grad_W (=|+=) dZ^T X_s */
 #define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss */
-#define FLJSD_KCLASS_COUNT 8
+#define FLJSD_KCLASS_TRANSPOSE 8        /* dZ^T and X_s^T for the grad_W product */
+#define FLJSD_KCLASS_COUNT 9
 
 int fljsd_profile_enable(int enable);
 int fljsd_profile_read(double* total_ms, int64_t* launches, double* flops,

@@ -401,17 +401,37 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
 
     if (grad_W_s) {
       GemmArgs g;
-      g.A = Zs;                       // A(m=v, k=r) = dZ[r, v]
-      g.B = Xs + r0 * H_s * es;       // B(n=h, k=r) = X_s[r, h]
+      if (plan.transposed_grad_w) {
+        // dZ^T [V, ldt] over the teacher logits (dead after the loss
+        // passes) and X_s^T [H_s, ldt]: both operands K-contiguous.
+        void* dzt = ws + plan.off_zt;
+        void* xt = ws + plan.off_xt;
+        const double tbytes = 2.0 * static_cast<double>(rows) * (V + H_s) * es;
+        hipError_t e = timed(s, FLJSD_KCLASS_TRANSPOSE, 0.0, tbytes, [&] {
+          hipError_t t = launch_transpose_bf16(Zs, rows, V, plan.ldz, dzt, plan.ldt, s);
+          if (t != hipSuccess) return t;
+          return launch_transpose_bf16(Xs + r0 * H_s * es, rows, H_s, H_s, xt, plan.ldt, s);
+        });
+        if (e != hipSuccess) return fail_hip(e, "launch transpose");
+        g.A = dzt;                    // A(m=v, k=r) = dZ^T[v, r]
+        g.B = xt;                     // B(n=h, k=r) = X_s^T[h, r]
+        g.lda = plan.ldt;
+        g.ldb = plan.ldt;
+        g.a_kcontig = true;
+        g.b_kcontig = true;
+      } else {
+        g.A = Zs;                     // A(m=v, k=r) = dZ[r, v]
+        g.B = Xs + r0 * H_s * es;     // B(n=h, k=r) = X_s[r, h]
+        g.lda = plan.ldz;
+        g.ldb = H_s;
+        g.a_kcontig = false;
+        g.b_kcontig = false;
+      }
       g.C = grad_W_s;
       g.M = V;
       g.N = H_s;
       g.K = rows;
-      g.lda = plan.ldz;
-      g.ldb = H_s;
       g.ldc = H_s;
-      g.a_kcontig = false;
-      g.b_kcontig = false;
       // Chunk 0 overwrites unless the caller asked to add to grad_W's
       // contents; later chunks add. An fp32 grad_W takes the bf16 product
       // unrounded (one-split fp32 store, or fp32 read-add-write).
@@ -422,7 +442,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
         g.epilogue = add ? kEpiAccumulate : kEpiStore;
       g.splitk = 1;
       g.k_per_split = rows;
-      g.group_m = 2;
+      g.group_m = 1;
       hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H_s * V,
                            gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
       if (e != hipSuccess) return fail_hip(e, "launch grad_weight GEMM");

@@ -735,7 +735,7 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
     case kEpiPartialF32: return launch_cfg<A_K, B_K, kEpiPartialF32>(g, s);
     case kEpiAccumulateF32:
       // Only the weight-gradient product accumulates into an fp32 C.
-      if constexpr (!A_K && !B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);
+      if constexpr (A_K == B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

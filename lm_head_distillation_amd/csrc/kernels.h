@@ -68,6 +68,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+
+// bf16 dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols.
+hipError_t launch_transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                 void* dst, int64_t ld_dst, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmArgs& g, hipStream_t s);
 
 }  // namespace fljsd

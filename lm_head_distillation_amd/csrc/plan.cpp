@@ -57,11 +57,14 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
     p.splitk = 1;
     p.k_per_split = V;
   }
+  p.transposed_grad_w = dtype == 1;
+  p.ldt = round_up(p.C, kJsdVec);
+  const int64_t zt_elems = p.transposed_grad_w ? std::max(p.C * p.ldz, V * p.ldt) : p.C * p.ldz;
   size_t off = 0;
   p.off_zs = off;
   off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
   p.off_zt = off;
-  off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
+  off = align256(off + static_cast<size_t>(zt_elems * es));
   p.off_row_loss = off;
   off = align256(off + static_cast<size_t>(BT) * 4);
   p.off_stats = off;
@@ -70,6 +73,8 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 8);
   p.off_partial = off;
   if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H_s * 4);
+  p.off_xt = off;
+  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H_s * p.ldt * es));
   p.total = off;
   return p;
 }

@@ -49,12 +49,17 @@ struct ChunkPlan {
   int64_t C = 0;          // rows per chunk
   int64_t n_chunks = 0;   // chunks actually run: ceil(BT / C)
   int64_t ldz = 0;        // row stride (elements) of the logits chunk buffers
+  // bf16 with a weight gradient: dZ^T [V, ldt] reuses the teacher-logits
+  // buffer once the loss passes are done, and X_s^T [H_s, ldt] has its own
+  // region, so grad_W = dZ^T X_s reads both operands with K (rows) fastest.
+  bool transposed_grad_w = false;
+  int64_t ldt = 0;        // row stride of the transposed operands: C rounded up to 8
   SlicePlan slices;       // for C rows
   int splitk = 1;         // split-K factor of grad_input = dZ W_s
   int64_t k_per_split = 0;
   // Workspace layout, byte offsets from the workspace base.
   size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0,
-         off_partial = 0, total = 0;
+         off_partial = 0, off_xt = 0, total = 0;
 };
 
 // Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).

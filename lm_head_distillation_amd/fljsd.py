@@ -24,7 +24,7 @@ REDUCTIONS = {"batchmean": 0, "sum": 1, "mean": 2, "none": 3}
 STATUS = {0: "FLJSD_OK", -1: "FLJSD_EINVAL", -2: "FLJSD_EDTYPE", -3: "FLJSD_EWORKSPACE",
           -4: "FLJSD_EALIGN", -5: "FLJSD_EHIP", -6: "FLJSD_EDEVICE"}
 KERNEL_CLASSES = ["gemm_logits", "jsd_stats", "jsd_loss", "jsd_grad", "gemm_grad_input",
-                  "splitk_reduce", "gemm_grad_weight", "loss_reduce"]
+                  "splitk_reduce", "gemm_grad_weight", "loss_reduce", "transpose"]
 
 _lib = None
 

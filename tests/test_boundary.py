@@ -64,7 +64,7 @@ def test_header_compiles_as_c():
            'int (*fbx)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
            ' int64_t, int, float, float, int, int, float*, void*, void*, int, unsigned, void*, size_t,'
            ' void*) = fljsd_forward_backward_ex;\n'
-           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 8 '
+           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 9 '
            '&& FLJSD_ACCUMULATE_GRAD_W == 1u;}\n')
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-",
                           "-I", os.path.join(ROOT, "include")], input=src, capture_output=True, text=True)
@@ -96,7 +96,12 @@ def test_workspace_size_accounts_for_each_buffer(lib):
             got = lib.fljsd_workspace_size(BT, H, H, V, dtype, nc)
             logits = 2 * a256(C * ldz * es)
             # logits chunks + per-row loss + (stats, partial sums) + optional split-K
+            # (+ bf16: dZ^T may need more than the teacher chunk, and X_s^T)
             assert got >= logits + a256(BT * 4) + a256(C * 16) + a256(C * 8)
+            if dtype == BF16:
+                ldt = cdiv(C, 8) * 8
+                zt = max(C * ldz, V * ldt) * es
+                assert got >= a256(C * ldz * es) + a256(zt) + a256(H * ldt * es)
             assert got <= logits + a256(BT * 4) + 64 * (a256(C * 16) + a256(C * 8)) + 4096 * C * H * 4 + 4096
 
 
@@ -109,9 +114,11 @@ def test_workspace_size_rejects_bad_arguments(lib):
 
 
 def test_large_shapes_workspace(lib):
-    # 8192 x 4096 x 128256 bf16 in one chunk: both logits chunks dominate.
+    # 8192 x 4096 x 128256 bf16 in one chunk: both logits chunks dominate; the
+    # transposed X_s chunk for the grad_W product adds C * H_s * 2 bytes.
     one = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 1)
-    assert 2 * 8192 * 128256 * 2 <= one < 2 * 8192 * 128256 * 2 + 64 * 2**20
+    xt = 8192 * 4096 * 2
+    assert 2 * 8192 * 128256 * 2 + xt <= one < 2 * 8192 * 128256 * 2 + xt + 64 * 2**20
     eight = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 8)
     assert eight < one / 4
 
