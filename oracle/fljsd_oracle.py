@@ -30,6 +30,9 @@ What it computes, and where the pages fix it:
   * grad_input = dZ W_s and grad_W = dZ^T X_s, accumulated over row chunks
     (PR #1429 "write the weight-gradient product directly into grad_weight",
     Summary); the oracle accumulates in fp64.
+  * Two adjacent public losses over given distributions: the generalized
+    JSD in log-probability space (PR #1352, Open question 3) and the total
+    variation distance with the p == q gradient fix (PR #1374).
   * Reductions: batchmean divides by the number of rows. PR #1374's tie table
     prints -0.0625 at (8, 512) for a -0.5 per-element TVD slope, i.e. a scale
     of 1/8 = 1/rows. sum uses 1, mean uses 1/(rows*V), none returns per-row
@@ -136,6 +139,73 @@ def generalized_jsd(logits_s, logits_t, beta: float, temperature: float,
     row_loss, dA = jsd_rows(logits_s, logits_t, beta, temperature)
     grad = dA * (scale / temperature)
     loss = row_loss if reduction == "none" else scale * np.sum(row_loss)
+    return loss, grad
+
+
+def jsd_logprob(logq, logp, beta: float, reduction: str = "batchmean"):
+    """Generalized JSD over given log-probabilities, with the gradient w.r.t.
+    the student's log-probabilities (the log-space contract of the public JSD
+    op that PR #1352, Open question 3, keeps apart from the fused path).
+
+    logq: student log-probabilities [R, V]; logp: teacher log-probabilities.
+    Element terms, with Q = exp(logq), P = exp(logp), taken as given (no
+    renormalization; each element is an independent variable):
+      beta == 0: l = P (logp - logq);             g = dl/dlogq = -P
+      beta == 1: l = Q (logq - logp);             g = Q (logq - logp) + Q
+      otherwise: M = beta P + (1-beta) Q,
+                 l = beta P (logp - log M) + (1-beta) Q (logq - log M),
+                 g = (1-beta) Q (logq - log M)
+    (in the generalized branch the derivatives of log M cancel against the
+    mixture weights, leaving g). Tie rule (PR #1374): where P == Q exactly,
+    l = 0 and, in the generalized branch, g = 0. 0 log 0 is taken as 0.
+    Returns (loss, grad): loss = scale * sum l (per-row sums for "none"),
+    grad = scale * g.
+    """
+    if not 0.0 <= beta <= 1.0:
+        raise ValueError("beta must be in [0, 1]")
+    logq = np.asarray(logq, dtype=np.float64)
+    logp = np.asarray(logp, dtype=np.float64)
+    R, V = logq.shape
+    scale = reduction_scale(reduction, R, V)
+    Q = np.exp(logq)
+    P = np.exp(logp)
+    tie = P == Q
+    if beta == 0.0:
+        l = np.where(P > 0, P * (logp - logq), 0.0)
+        g = -P
+    elif beta == 1.0:
+        l = np.where(Q > 0, Q * (logq - logp), 0.0)
+        g = np.where(Q > 0, Q * (logq - logp), 0.0) + Q
+    else:
+        logM = np.logaddexp(np.log(beta) + logp, np.log1p(-beta) + logq)
+        term_p = np.where(P > 0, beta * P * (logp - logM), 0.0)
+        term_q = np.where(Q > 0, (1.0 - beta) * Q * (logq - logM), 0.0)
+        l = term_p + term_q
+        g = np.where(tie, 0.0, term_q)
+    l = np.where(tie, 0.0, l)
+    row_loss = np.sum(l, axis=-1)
+    loss = row_loss if reduction == "none" else scale * np.sum(row_loss)
+    return loss, scale * g
+
+
+def tvd(p, q, reduction: str = "batchmean"):
+    """Total variation distance between given distributions, with the
+    gradient w.r.t. p (PR #1374 "Fix TVD gradient at p == q", Summary).
+
+    Element loss 0.5 |p - q|; its derivative w.r.t. p is +0.5 where p > q,
+    -0.5 where p < q, and 0 at an exact tie p == q (the fix: a three-way
+    sign). Returns (loss, grad): loss = scale * sum over all elements, or the
+    elementwise [R, V] losses for "none" (the plain elementwise reading of the
+    page's reference torch.abs(p - q) / 2); grad = scale * derivative.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    R, V = p.shape
+    scale = reduction_scale(reduction, R, V)
+    diff = p - q
+    elem = 0.5 * np.abs(diff)
+    grad = scale * 0.5 * np.sign(diff)
+    loss = elem if reduction == "none" else scale * np.sum(elem)
     return loss, grad
 
 

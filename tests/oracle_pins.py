@@ -270,6 +270,132 @@ def pin_padded_slots_exact_zero(o):
         assert np.all(g[:, V - pad:] == 0.0), f"padded logit grads beta={beta}"
 
 
+# ---- the log-probability JSD and the TVD -------------------------------------------------
+
+def pin_logprob_kl_library(o):
+    """Over normalized log-probabilities, beta=0 is KL(P||Q) and beta=1 is
+    KL(Q||P) (scipy's rel_entr), as in the logit path (PR #1352 Testing Done)."""
+    logq = sps.log_softmax(_logits(21, 5, 29, 2.0), axis=-1)
+    logp = sps.log_softmax(_logits(22, 5, 29, 2.0), axis=-1)
+    Q, P = np.exp(logq), np.exp(logp)
+    fwd, _ = o.jsd_logprob(logq, logp, 0.0, "none")
+    rev, _ = o.jsd_logprob(logq, logp, 1.0, "none")
+    assert np.allclose(fwd, _kl_rows(P, Q), rtol=1e-10, atol=1e-14), "logprob beta=0 != KL(P||Q)"
+    assert np.allclose(rev, _kl_rows(Q, P), rtol=1e-10, atol=1e-14), "logprob beta=1 != KL(Q||P)"
+
+
+def pin_logprob_disjoint_closed_form(o):
+    """Disjoint supports give h(beta) exactly; swapping roles maps beta to 1-beta."""
+    logq = np.full((1, 6), -1e4)
+    logp = np.full((1, 6), -1e4)
+    logq[0, 1] = 0.0
+    logp[0, 4] = 0.0
+    for beta in (0.1, 0.5, 0.9):
+        loss, _ = o.jsd_logprob(logq, logp, beta, "none")
+        assert np.allclose(loss, _h(beta), rtol=1e-12, atol=0), f"logprob disjoint beta={beta}"
+    a = sps.log_softmax(_logits(23, 3, 17, 2.0), axis=-1)
+    b = sps.log_softmax(_logits(24, 3, 17, 2.0), axis=-1)
+    for beta in (0.2, 0.5):
+        x, _ = o.jsd_logprob(a, b, beta, "none")
+        y, _ = o.jsd_logprob(b, a, 1.0 - beta, "none")
+        assert np.allclose(x, y, rtol=1e-12, atol=1e-15), f"logprob role swap beta={beta}"
+
+
+def pin_logprob_finite_differences(o):
+    """grad = d loss / d logq elementwise, by central differences, for
+    arbitrary (also unnormalized) log-probabilities and every reduction."""
+    rng = _rng(25)
+    logq = rng.standard_normal((3, 6)) - 2.0
+    logp = rng.standard_normal((3, 6)) - 2.0
+    h = 1e-6
+    for beta in BETAS:
+        for red in ("batchmean", "sum", "mean"):
+            _, g = o.jsd_logprob(logq, logp, beta, red)
+            fd = np.zeros_like(logq)
+            for idx in np.ndindex(*logq.shape):
+                xp = logq.copy()
+                xm = logq.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                fd[idx] = (o.jsd_logprob(xp, logp, beta, red)[0] -
+                           o.jsd_logprob(xm, logp, beta, red)[0]) / (2 * h)
+            assert np.allclose(g, fd, rtol=1e-6, atol=1e-10), f"logprob fd beta={beta} {red}"
+
+
+def pin_logprob_ties_and_logit_path(o):
+    """Equal inputs: loss 0 and, in the generalized branch, gradient exactly 0
+    (PR #1374). Over log_softmax outputs at T = 1 the loss equals the logit
+    path's loss."""
+    a = sps.log_softmax(_logits(26, 4, 21, 2.0), axis=-1)
+    for beta in BETAS:
+        loss, g = o.jsd_logprob(a, a.copy(), beta, "batchmean")
+        assert loss == 0.0, f"logprob self loss beta={beta}"
+        if 0.0 < beta < 1.0:
+            assert np.all(g == 0.0), f"logprob self grad beta={beta}"
+    zs = _logits(27, 4, 21, 2.0)
+    zt = _logits(28, 4, 21, 2.0)
+    for beta in BETAS:
+        x, _ = o.jsd_logprob(sps.log_softmax(zs, axis=-1), sps.log_softmax(zt, axis=-1), beta, "sum")
+        y, _ = o.generalized_jsd(zs, zt, beta, 1.0, "sum")
+        assert abs(x - y) <= 1e-12 * max(1.0, abs(y)), f"logprob vs logit path beta={beta}"
+
+
+def pin_tvd_golden_ties(o):
+    """PR #1374's tie table at (8, 512) fp32, batchmean: with p == q everywhere
+    every gradient element is 0.0 (after the fix); the page's pre-fix value
+    -0.0625 is the p < q slope, which untied elements with p < q still get."""
+    g = _golden("tvd_tie_batchmean.json")
+    R, V = g["rows"], g["vocab"]
+    p = sps.softmax(_logits(29, R, V), axis=-1)
+    loss, grad = o.tvd(p, p.copy(), "batchmean")
+    assert loss == 0.0
+    assert np.count_nonzero(grad) == 0 and grad.size == g["elements"]
+    assert np.all(grad == g["gradient_at_tie_after_fix"])
+    q = p.copy()
+    q[:, ::2] *= 1.5          # p < q on even columns, p > q on odd ones after renormalizing
+    q /= q.sum(axis=-1, keepdims=True)
+    _, grad = o.tvd(p, q, "batchmean")
+    assert np.all(grad[p < q] == g["gradient_at_tie_before_fix"])
+    assert np.all(grad[p > q] == -g["gradient_at_tie_before_fix"])
+
+
+def pin_tvd_library_and_closed_form(o):
+    """Row TVD is half the L1 distance (numpy's norm); disjoint rows give 1;
+    reductions scale the total as batchmean 1/rows, mean 1/(rows V), sum 1."""
+    p = sps.softmax(_logits(30, 5, 23), axis=-1)
+    q = sps.softmax(_logits(31, 5, 23), axis=-1)
+    elem, _ = o.tvd(p, q, "none")
+    assert elem.shape == p.shape
+    rows = np.array([0.5 * np.linalg.norm(p[r] - q[r], ord=1) for r in range(5)])
+    assert np.allclose(elem.sum(axis=-1), rows, rtol=1e-14, atol=0)
+    tot = rows.sum()
+    assert abs(o.tvd(p, q, "sum")[0] - tot) <= 1e-14
+    assert abs(o.tvd(p, q, "batchmean")[0] - tot / 5) <= 1e-14
+    assert abs(o.tvd(p, q, "mean")[0] - tot / (5 * 23)) <= 1e-15
+    a = np.zeros((2, 4))
+    b = np.zeros((2, 4))
+    a[0, 0] = b[0, 3] = 1.0
+    a[1, :2] = b[1, 2:] = 0.5
+    assert np.allclose(o.tvd(a, b, "none")[0].sum(axis=-1), 1.0, rtol=0, atol=1e-15)
+
+
+def pin_tvd_finite_differences(o):
+    """Away from ties, grad = d loss / d p by central differences."""
+    rng = _rng(32)
+    p = rng.random((3, 7))
+    q = rng.random((3, 7))
+    h = 1e-7
+    for red in ("batchmean", "sum", "mean"):
+        _, g = o.tvd(p, q, red)
+        for idx in np.ndindex(*p.shape):
+            pp = p.copy()
+            pm = p.copy()
+            pp[idx] += h
+            pm[idx] -= h
+            fd = (o.tvd(pp, q, red)[0] - o.tvd(pm, q, red)[0]) / (2 * h)
+            assert abs(fd - g[idx]) <= 1e-7, f"tvd fd {red} {idx}"
+
+
 ALL_PINS = [
     pin_log_softmax_library,
     pin_batchmean_scale_golden,
@@ -285,6 +411,13 @@ ALL_PINS = [
     pin_gradient_rows_sum_to_zero,
     pin_block_invariance_and_reductions,
     pin_padded_slots_exact_zero,
+    pin_logprob_kl_library,
+    pin_logprob_disjoint_closed_form,
+    pin_logprob_finite_differences,
+    pin_logprob_ties_and_logit_path,
+    pin_tvd_golden_ties,
+    pin_tvd_library_and_closed_form,
+    pin_tvd_finite_differences,
 ]
 
 

@@ -51,6 +51,18 @@ MUTANTS = [
      "scale = reduction_scale(reduction, min(BT, block_rows), V)\n    grad_X", 1),
     ("forward_kl_swapped_roles", "l = np.where(P > 0, P * (logP - logQ), 0.0)",
      "l = np.where(Q > 0, Q * (logQ - logP), 0.0)", 1),
+    ("logprob_forward_grad_sign", "        g = -P\n", "        g = P\n", 1),
+    ("logprob_reverse_missing_q", "g = np.where(Q > 0, Q * (logq - logp), 0.0) + Q",
+     "g = np.where(Q > 0, Q * (logq - logp), 0.0)", 1),
+    ("logprob_dropped_1_minus_beta", "term_q = np.where(Q > 0, (1.0 - beta) * Q * (logq - logM), 0.0)",
+     "term_q = np.where(Q > 0, Q * (logq - logM), 0.0)", 1),
+    ("logprob_grad_unscaled", "return loss, scale * g", "return loss, g", 1),
+    ("logprob_tie_rule_dropped", "g = np.where(tie, 0.0, term_q)", "g = term_q", 1),
+    ("tvd_two_way_sign", "grad = scale * 0.5 * np.sign(diff)",
+     "grad = scale * 0.5 * np.where(diff > 0, 1.0, -1.0)", 1),
+    ("tvd_dropped_half", "elem = 0.5 * np.abs(diff)", "elem = np.abs(diff)", 1),
+    ("tvd_grad_wrong_sign", "grad = scale * 0.5 * np.sign(diff)", "grad = -scale * 0.5 * np.sign(diff)", 1),
+    ("tvd_grad_unscaled", "grad = scale * 0.5 * np.sign(diff)", "grad = 0.5 * np.sign(diff)", 1),
 ]
 
 
