@@ -117,6 +117,9 @@ int fljsd_forward_backward(const void* X_s, const void* W_s,
 /* Flag bits of fljsd_forward_backward_ex. */
 #define FLJSD_ACCUMULATE_GRAD_W 1u  /* add this call's weight gradient to the
                                        values grad_W_s already holds */
+#define FLJSD_TEMPERATURE_SQUARED 2u /* multiply the loss, and so every gradient,
+                                        by temperature^2 (PR #1352, Open question 2:
+                                        the soft-target convention of Hinton et al.) */
 
 /*
  * fljsd_forward_backward_ex - fljsd_forward_backward with a choice of
@@ -131,10 +134,13 @@ int fljsd_forward_backward(const void* X_s, const void* W_s,
  *                 over chunks in fp32 with no rounding in between, so the
  *                 result does not carry one bf16 rounding per chunk. Any
  *                 other value is FLJSD_EDTYPE.
- *   flags         0, or FLJSD_ACCUMULATE_GRAD_W: the first chunk adds to
- *                 grad_W_s instead of overwriting it, so grad_W_s must hold
+ *   flags         bitwise OR of:
+ *                 FLJSD_ACCUMULATE_GRAD_W: the first chunk adds to grad_W_s
+ *                 instead of overwriting it, so grad_W_s must hold
  *                 initialized values on entry (for summing gradients over
- *                 several calls, e.g. micro-batches of one optimizer step).
+ *                 several calls, e.g. micro-batches of one optimizer step);
+ *                 FLJSD_TEMPERATURE_SQUARED: loss (also each per-row loss of
+ *                 FLJSD_NONE) and gradients carry an extra factor T^2.
  *                 Unknown bits are FLJSD_EINVAL.
  * fljsd_forward_backward(...) is fljsd_forward_backward_ex(..., dtype, 0, ...).
  * The workspace size does not depend on these two arguments.
@@ -171,6 +177,47 @@ int fljsd_generalized_jsd(const void* logits_s, const void* logits_t,
                           float* loss, void* grad_logits_s,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * fljsd_jsd_logprob - generalized JSD over given log-probabilities, the
+ * log-space contract of the public JSD op (PR #1352, Open question 3), in
+ * one pass.
+ *
+ *   logq_s, logp_t [BT, ld] in dtype: student and teacher log-probabilities
+ *             (natural log), first V columns used; -inf means probability 0.
+ *             They are taken as given: nothing renormalizes them.
+ *   beta in [0, 1]: 0 is KL(P||Q) (P = exp(logp_t), Q = exp(logq_s)),
+ *             1 is KL(Q||P), between them beta KL(P||M) + (1-beta) KL(Q||M).
+ *   loss      fp32: 1 value, or BT per-row sums for FLJSD_NONE.
+ *   grad_logq_s [BT, ld] in dtype, or NULL: d loss / d logq_s elementwise
+ *             (each input element is an independent variable; no softmax
+ *             chain rule), including the reduction scale. May equal logq_s.
+ *   Exact ties P == Q contribute no loss and, for 0 < beta < 1, no
+ *   gradient (PR #1374); in the KL branches the tie gradient is the true
+ *   derivative (-P for beta 0, Q for beta 1).
+ * Workspace: at least fljsd_generalized_jsd_workspace_size(BT, V, dtype).
+ * Errors: as fljsd_generalized_jsd.
+ */
+int fljsd_jsd_logprob(const void* logq_s, const void* logp_t,
+                      int64_t BT, int64_t V, int64_t ld, int dtype,
+                      float beta, int reduction, float* loss, void* grad_logq_s,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fljsd_tvd - total variation distance between given distributions, with the
+ * gradient fix at ties (PR #1374 "Fix TVD gradient at p == q", Summary).
+ *
+ *   p, q   [BT, ld] in dtype, first V columns used.
+ *   loss   fp32: 1 value, or for FLJSD_NONE the BT x V elementwise losses
+ *          |p - q| / 2, dense with row stride V.
+ *   grad_p [BT, ld] in dtype, or NULL: d loss / d p = scale/2 * sign(p - q),
+ *          exactly 0 where p == q. May equal p.
+ * Workspace: at least fljsd_generalized_jsd_workspace_size(BT, V, dtype).
+ * Errors: as fljsd_generalized_jsd (beta and temperature do not apply).
+ */
+int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, int64_t ld,
+              int dtype, int reduction, float* loss, void* grad_p,
+              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes fljsd_forward_backward needs for this shape with
  * num_chunks >= 1 chunks. Pure host arithmetic; no device is touched.
@@ -215,7 +262,8 @@ const char* fljsd_last_error(void);
 #define FLJSD_KCLASS_GEMM_GRAD_WEIGHT 6 /* grad_W (=|+=) dZ^T X_s */
 #define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss */
 #define FLJSD_KCLASS_TRANSPOSE 8        /* dZ^T and X_s^T for the grad_W product */
-#define FLJSD_KCLASS_COUNT 9
+#define FLJSD_KCLASS_ELEM_LOSS 9        /* fljsd_jsd_logprob / fljsd_tvd element pass */
+#define FLJSD_KCLASS_COUNT 10
 
 int fljsd_profile_enable(int enable);
 int fljsd_profile_read(double* total_ms, int64_t* launches, double* flops,

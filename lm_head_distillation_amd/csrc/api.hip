@@ -277,7 +277,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
   if (grad_w_dtype != dtype && !(dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32))
     return fail(FLJSD_EDTYPE, "grad_w_dtype must equal dtype, or be F32 with BF16 inputs");
-  if (flags & ~static_cast<unsigned>(FLJSD_ACCUMULATE_GRAD_W))
+  if (flags & ~static_cast<unsigned>(FLJSD_ACCUMULATE_GRAD_W | FLJSD_TEMPERATURE_SQUARED))
     return fail(FLJSD_EINVAL, "unknown flag bits");
   const bool gw_f32_acc = dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32;
   const bool gw_add_existing = (flags & FLJSD_ACCUMULATE_GRAD_W) != 0;
@@ -320,7 +320,13 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   ja.S = plan.slices.S;
   ja.k2 = static_cast<float>(1.4426950408889634 / static_cast<double>(temperature));
   ja.beta = beta;
-  ja.grad_scale = static_cast<float>(scale / static_cast<double>(temperature));
+  // The optional T^2 factor (PR #1352, Open question 2) multiplies the loss
+  // and, with it, every gradient.
+  const double t2 = (flags & FLJSD_TEMPERATURE_SQUARED)
+                        ? static_cast<double>(temperature) * static_cast<double>(temperature)
+                        : 1.0;
+  ja.grad_scale = static_cast<float>(scale * t2 / static_cast<double>(temperature));
+  ja.row_scale = static_cast<float>(t2);
   ja.mode = mode_for(beta);
   ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
@@ -510,4 +516,94 @@ FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_
     if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
   }
   return FLJSD_OK;
+}
+
+namespace fljsd {
+namespace {
+
+// Shared by the two one-pass losses: checks, planning and the launch
+// sequence (element pass, per-row merge, scalar reduction).
+template <class Launch>
+int run_elem_loss(const void* a_ptr, const void* b_ptr, int64_t BT, int64_t V, int64_t ld,
+                  int dtype, int reduction, float* loss, void* grad, bool elementwise_none,
+                  float beta, int mode, void* workspace, size_t workspace_bytes, void* stream,
+                  int kclass, Launch&& launch) {
+  if (!a_ptr || !b_ptr || !loss) return fail(FLJSD_EINVAL, "inputs and loss must not be NULL");
+  if (BT <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT and V must be > 0");
+  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
+  if (ld < V) return fail(FLJSD_EINVAL, "ld must be >= V");
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
+  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
+    return fail(FLJSD_EDTYPE, "unknown reduction");
+  const void* ptrs[] = {a_ptr, b_ptr, loss, grad, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
+  const JsdPlan plan = plan_jsd(BT, V);
+  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
+  if (workspace_bytes < plan.total)
+    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
+  int rc = check_device();
+  if (rc != FLJSD_OK) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const double scale = reduction_scale(reduction, BT, V);
+  const bool none = reduction == FLJSD_NONE;
+  ElemArgs ea;
+  ea.a = a_ptr;
+  ea.b = b_ptr;
+  ea.grad = grad;
+  ea.elem_loss = (none && elementwise_none) ? loss : nullptr;
+  ea.ld = ld;
+  ea.vec_ok = ld % dtype_vec(dtype) == 0;
+  ea.rows = BT;
+  ea.V = V;
+  ea.slice_w = plan.slices.slice_w;
+  ea.S = plan.slices.S;
+  ea.beta = beta;
+  ea.grad_scale = static_cast<float>(scale);
+  ea.mode = mode;
+  ea.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
+  const double bytes = static_cast<double>(BT) * V * dtype_size(dtype) * (grad ? 3 : 2);
+  hipError_t e = timed(s, kclass, 0.0, bytes, [&] { return launch(ea, dtype, s); });
+  if (e != hipSuccess) return fail_hip(e, "launch loss kernel");
+  if (none && elementwise_none) return FLJSD_OK;
+  // Per-row sums of the slice partials, then the scalar.
+  JsdArgs ja;
+  ja.rows = BT;
+  ja.S = plan.slices.S;
+  ja.lg = ea.lg;
+  ja.row_loss = none ? loss : reinterpret_cast<float*>(ws + plan.off_row_loss);
+  e = launch_jsd_row_loss(ja, s);
+  if (e != hipSuccess) return fail_hip(e, "launch row loss");
+  if (!none) {
+    e = timed(s, FLJSD_KCLASS_LOSS_REDUCE, 0.0, 4.0 * BT, [&] {
+      return launch_loss_reduce(ja.row_loss, BT, static_cast<float>(scale), loss, s);
+    });
+    if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
+  }
+  return FLJSD_OK;
+}
+
+}  // namespace
+}  // namespace fljsd
+
+FLJSD_EXPORT int fljsd_jsd_logprob(const void* logq_s, const void* logp_t, int64_t BT, int64_t V,
+                                   int64_t ld, int dtype, float beta, int reduction, float* loss,
+                                   void* grad_logq_s, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_last_error.clear();
+  if (!(beta >= 0.0f && beta <= 1.0f)) return fail(FLJSD_EINVAL, "beta must be in [0, 1]");
+  return run_elem_loss(logq_s, logp_t, BT, V, ld, dtype, reduction, loss, grad_logq_s, false,
+                       beta, mode_for(beta), workspace, workspace_bytes, stream,
+                       FLJSD_KCLASS_ELEM_LOSS, launch_logprob_jsd);
+}
+
+FLJSD_EXPORT int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, int64_t ld,
+                           int dtype, int reduction, float* loss, void* grad_p, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return run_elem_loss(p, q, BT, V, ld, dtype, reduction, loss, grad_p, true, 0.0f,
+                       kModeGeneralized, workspace, workspace_bytes, stream,
+                       FLJSD_KCLASS_ELEM_LOSS, launch_tvd);
 }

@@ -37,6 +37,7 @@
 // log2, v_rcp_f32). expm1 on (-1/2, 0] is a degree-9 Taylor polynomial and
 // log1p on [-1/4, 0] the atanh series, so both keep full relative accuracy as
 // their argument goes to 0.
+#include "elem_math.h"
 #include "kernels.h"
 
 #include <hip/hip_runtime.h>
@@ -50,72 +51,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr float kLn2 = 0.693147180559945309f;
-
-__device__ inline float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ inline float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
-__device__ inline float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-
-__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                       // round to nearest even
-  return u >> 16;
-}
-
-// Load up to 8 consecutive elements starting at column v; lanes at or past n
-// read as -inf (a masked column carries no probability mass). A full group
-// uses 16-byte loads when `vec` says the rows are 16-byte aligned.
-__device__ inline void load8(const float* p, int64_t v, int n, bool vec, float* x) {
-  if (n == 8 && vec) {
-    const float4 a = *reinterpret_cast<const float4*>(p + v);
-    const float4 b = *reinterpret_cast<const float4*>(p + v + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = i < n ? p[v + i] : -INFINITY;
-  }
-}
-
-__device__ inline void load8(const uint16_t* p, int64_t v, int n, bool vec, float* x) {
-  if (n == 8 && vec) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p + v);
-    x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x);
-    x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
-    x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z);
-    x[6] = bf16_lo(q.w); x[7] = bf16_hi(q.w);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = i < n ? __uint_as_float(uint32_t(p[v + i]) << 16) : -INFINITY;
-  }
-}
-
-__device__ inline void store8(float* p, int64_t v, int n, bool vec, const float* x) {
-  if (n == 8 && vec) {
-    *reinterpret_cast<float4*>(p + v) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(p + v + 4) = make_float4(x[4], x[5], x[6], x[7]);
-  } else {
-    for (int i = 0; i < n; ++i) p[v + i] = x[i];
-  }
-}
-
-__device__ inline void store8(uint16_t* p, int64_t v, int n, bool vec, const float* x) {
-  if (n == 8 && vec) {
-    uint4 q;
-    q.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-    q.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
-    q.z = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
-    q.w = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
-    *reinterpret_cast<uint4*>(p + v) = q;
-  } else {
-    for (int i = 0; i < n; ++i) p[v + i] = static_cast<uint16_t>(f32_to_bf16_bits(x[i]));
-  }
-}
-
 // Merge of two (max, denominator) pairs; maxima in logit units, denominators
 // in base 2 with scale k. Commutative bit for bit (max and a two-term IEEE
 // sum are), so both butterfly partners agree.
@@ -146,12 +81,6 @@ __device__ inline void md_update8(float& m, float& d, const float* z, float k) {
   d += acc;
 }
 
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 __device__ inline void wave_md(float& m, float& d, float k) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -159,63 +88,6 @@ __device__ inline void wave_md(float& m, float& d, float k) {
     const float dof = __shfl_xor(d, o, 64);
     md_merge(m, d, mo, dof, k);
   }
-}
-
-// expm1(w) for w <= 0: Taylor polynomial on (-1/2, 0], 2^(w log2 e) - 1 below.
-// `t` is w / ln 2 (the same value in base 2).
-__device__ inline float expm1_nonpos(float w, float t) {
-  float p = 1.f / 362880.f;
-  p = fmaf(p, w, 1.f / 40320.f);
-  p = fmaf(p, w, 1.f / 5040.f);
-  p = fmaf(p, w, 1.f / 720.f);
-  p = fmaf(p, w, 1.f / 120.f);
-  p = fmaf(p, w, 1.f / 24.f);
-  p = fmaf(p, w, 1.f / 6.f);
-  p = fmaf(p, w, 0.5f);
-  p = fmaf(p, w, 1.f);
-  const float poly = p * w;
-  return w > -0.5f ? poly : hw_exp2(t) - 1.f;
-}
-
-// log1p(x) for x in (-1, 0]. Near 0 (x >= -1/4): 2 atanh(s) with
-// s = x / (2 + x) in [-1/7, 0], an odd series whose truncation error is below
-// 1e-10 relative; further out, ln(1 + x) from the hardware log2, whose result
-// is then at least 0.41 in magnitude.
-__device__ inline float log1p_nonpos(float x) {
-  const float s = x * hw_rcp(2.f + x);
-  const float s2 = s * s;
-  float p = 1.f / 11.f;
-  p = fmaf(p, s2, 1.f / 9.f);
-  p = fmaf(p, s2, 1.f / 7.f);
-  p = fmaf(p, s2, 1.f / 5.f);
-  p = fmaf(p, s2, 1.f / 3.f);
-  p = fmaf(p, s2, 1.f);
-  const float series = 2.f * s * p;
-  return x >= -0.25f ? series : hw_log2(1.f + x) * kLn2;
-}
-
-// D e^D - expm1(D) for |D| < 1/4: sum over k >= 2 of (k-1) D^k / k!.
-__device__ inline float kl_fwd_series(float D) {
-  float p = 1.f / 5760.f;
-  p = fmaf(p, D, 1.f / 840.f);
-  p = fmaf(p, D, 1.f / 144.f);
-  p = fmaf(p, D, 1.f / 30.f);
-  p = fmaf(p, D, 1.f / 8.f);
-  p = fmaf(p, D, 1.f / 3.f);
-  p = fmaf(p, D, 0.5f);
-  return p * D * D;
-}
-
-// expm1(D) - D for |D| < 1/4: sum over k >= 2 of D^k / k!.
-__device__ inline float kl_rev_series(float D) {
-  float p = 1.f / 40320.f;
-  p = fmaf(p, D, 1.f / 5040.f);
-  p = fmaf(p, D, 1.f / 720.f);
-  p = fmaf(p, D, 1.f / 120.f);
-  p = fmaf(p, D, 1.f / 24.f);
-  p = fmaf(p, D, 1.f / 6.f);
-  p = fmaf(p, D, 0.5f);
-  return p * D * D;
 }
 
 // Per-element terms of the divergence; see the file comment. Inputs are the
@@ -370,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
       acc.y += lg[j].y;
     }
     sh_G = acc.y;
-    if (s == 0) a.row_loss[row] = acc.x;
+    if (s == 0) a.row_loss[row] = acc.x * a.row_scale;
   }
   __syncthreads();
   const float G = sh_G;
@@ -396,7 +268,7 @@ __global__ __launch_bounds__(64) void jsd_row_loss_kernel(JsdArgs a) {
     const float2* lg = a.lg + row * a.S;
     float acc = lg[0].x;
     for (int j = 1; j < a.S; ++j) acc += lg[j].x;
-    a.row_loss[row] = acc;
+    a.row_loss[row] = acc * a.row_scale;
   }
 }
 

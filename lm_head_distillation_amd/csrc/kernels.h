@@ -28,7 +28,28 @@ struct JsdArgs {
   float4* stats = nullptr;      // [rows * S] partial (m_s, d_s, m_t, d_t), base 2
   float2* lg = nullptr;         // [rows * S] partial (loss, dX_sum)
   float* row_loss = nullptr;    // [rows] per-row loss out
+  float row_scale = 1.f;        // multiplies the per-row losses (T^2 when asked)
 };
+
+// The one-pass losses over given distributions (log-probability JSD, TVD).
+struct ElemArgs {
+  const void* a = nullptr;      // student log-probabilities, or p   [rows, ld]
+  const void* b = nullptr;      // teacher log-probabilities, or q   [rows, ld]
+  void* grad = nullptr;         // d loss / d a [rows, ld], or null; may equal a
+  float* elem_loss = nullptr;   // TVD elementwise losses [rows, V] (reduction none)
+  int64_t ld = 0;
+  bool vec_ok = true;
+  int64_t rows = 0;
+  int64_t V = 0;
+  int64_t slice_w = 0;
+  int S = 1;
+  float beta = 0.f;
+  float grad_scale = 0.f;       // reduction scale
+  int mode = kModeGeneralized;
+  float2* lg = nullptr;         // [rows * S] partial loss sums (.x)
+};
+hipError_t launch_logprob_jsd(const ElemArgs& a, int dtype, hipStream_t s);
+hipError_t launch_tvd(const ElemArgs& a, int dtype, hipStream_t s);
 
 // Loss passes. dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);

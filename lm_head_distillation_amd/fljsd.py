@@ -24,7 +24,7 @@ REDUCTIONS = {"batchmean": 0, "sum": 1, "mean": 2, "none": 3}
 STATUS = {0: "FLJSD_OK", -1: "FLJSD_EINVAL", -2: "FLJSD_EDTYPE", -3: "FLJSD_EWORKSPACE",
           -4: "FLJSD_EALIGN", -5: "FLJSD_EHIP", -6: "FLJSD_EDEVICE"}
 KERNEL_CLASSES = ["gemm_logits", "jsd_stats", "jsd_loss", "jsd_grad", "gemm_grad_input",
-                  "splitk_reduce", "gemm_grad_weight", "loss_reduce", "transpose"]
+                  "splitk_reduce", "gemm_grad_weight", "loss_reduce", "transpose", "elem_loss"]
 
 _lib = None
 
@@ -59,6 +59,10 @@ def load_library() -> ctypes.CDLL:
     lib.fljsd_generalized_jsd.argtypes = [vp, vp, i64, i64, i64, cint, f32, f32, cint, vp, vp,
                                           vp, sz, vp]
     lib.fljsd_generalized_jsd.restype = cint
+    lib.fljsd_jsd_logprob.argtypes = [vp, vp, i64, i64, i64, cint, f32, cint, vp, vp, vp, sz, vp]
+    lib.fljsd_jsd_logprob.restype = cint
+    lib.fljsd_tvd.argtypes = [vp, vp, i64, i64, i64, cint, cint, vp, vp, vp, sz, vp]
+    lib.fljsd_tvd.restype = cint
     lib.fljsd_workspace_size.argtypes = [i64, i64, i64, i64, cint, cint]
     lib.fljsd_workspace_size.restype = sz
     lib.fljsd_generalized_jsd_workspace_size.argtypes = [i64, i64, cint]
@@ -143,6 +147,7 @@ def default_budget_bytes() -> int:
 
 
 FLJSD_ACCUMULATE_GRAD_W = 1
+FLJSD_TEMPERATURE_SQUARED = 2
 
 
 def fljsd_forward_backward(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.Tensor,
@@ -257,6 +262,73 @@ def fljsd_generalized_jsd(logits_s: torch.Tensor, logits_t: torch.Tensor, beta: 
         logits_s.data_ptr(), logits_t.data_ptr(), BT, V, ld, dt, float(beta), float(temperature),
         red, loss.data_ptr(), _ptr(grad), workspace.data_ptr(),
         workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return (loss if red == 3 else loss[0]), grad
+
+
+def _pair_2d(a: torch.Tensor, b: torch.Tensor, what: str):
+    for t in (a, b):
+        if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1:
+            raise ValueError(f"{what} must be 2-D GPU tensors with unit column stride")
+    dt = _dtype_code(a)
+    if _dtype_code(b) != dt:
+        raise ValueError(f"{what} must share one dtype")
+    BT, V = a.shape
+    ld = a.stride(0)
+    if b.shape != (BT, V) or b.stride(0) != ld:
+        raise ValueError(f"{what}: second input must match the first in shape and row stride")
+    return dt, BT, V, ld
+
+
+def _grad_like(a: torch.Tensor, grad, in_place: bool, want_grad: bool):
+    if in_place:
+        return a
+    if not want_grad:
+        return None
+    if grad is None:
+        grad = torch.empty_strided(a.shape, a.stride(), dtype=a.dtype, device=a.device)
+    if grad.stride() != a.stride() or grad.shape != a.shape:
+        raise ValueError("grad must match the input in shape and strides")
+    return grad
+
+
+def fljsd_jsd_logprob(logq_s: torch.Tensor, logp_t: torch.Tensor, beta: float,
+                      reduction: str = "batchmean", *, grad: Optional[torch.Tensor] = None,
+                      in_place: bool = False, want_grad: bool = True,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Generalized JSD over given log-probabilities [BT, V]. Returns
+    (loss, d loss / d logq_s or None)."""
+    lib = load_library()
+    dt, BT, V, ld = _pair_2d(logq_s, logp_t, "log-probabilities")
+    red = _reduction_code(reduction)
+    if workspace is None:
+        workspace = torch.empty(fljsd_generalized_jsd_workspace_size(BT, V, dt), dtype=torch.uint8,
+                                device=logq_s.device)
+    loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=logq_s.device)
+    grad = _grad_like(logq_s, grad, in_place, want_grad)
+    rc = lib.fljsd_jsd_logprob(logq_s.data_ptr(), logp_t.data_ptr(), BT, V, ld, dt, float(beta), red,
+                               loss.data_ptr(), _ptr(grad), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return (loss if red == 3 else loss[0]), grad
+
+
+def fljsd_tvd(p: torch.Tensor, q: torch.Tensor, reduction: str = "batchmean", *,
+              grad: Optional[torch.Tensor] = None, in_place: bool = False, want_grad: bool = True,
+              workspace: Optional[torch.Tensor] = None, stream=None):
+    """Total variation distance between distributions p, q [BT, V]. Returns
+    (loss, d loss / d p or None); reduction "none" gives the [BT, V] losses."""
+    lib = load_library()
+    dt, BT, V, ld = _pair_2d(p, q, "distributions")
+    red = _reduction_code(reduction)
+    if workspace is None:
+        workspace = torch.empty(fljsd_generalized_jsd_workspace_size(BT, V, dt), dtype=torch.uint8,
+                                device=p.device)
+    loss = torch.empty((BT, V) if red == 3 else (1,), dtype=torch.float32, device=p.device)
+    grad = _grad_like(p, grad, in_place, want_grad)
+    rc = lib.fljsd_tvd(p.data_ptr(), q.data_ptr(), BT, V, ld, dt, red, loss.data_ptr(), _ptr(grad),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       _stream(stream))
     _check(rc)
     return (loss if red == 3 else loss[0]), grad
 

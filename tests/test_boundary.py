@@ -40,7 +40,7 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fljsd_forward_backward", "fljsd_forward_backward_ex", "fljsd_generalized_jsd",
-              "fljsd_workspace_size",
+              "fljsd_jsd_logprob", "fljsd_tvd", "fljsd_workspace_size",
               "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
               "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read"):
         assert n in names
@@ -64,7 +64,7 @@ def test_header_compiles_as_c():
            'int (*fbx)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
            ' int64_t, int, float, float, int, int, float*, void*, void*, int, unsigned, void*, size_t,'
            ' void*) = fljsd_forward_backward_ex;\n'
-           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 9 '
+           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 10 '
            '&& FLJSD_ACCUMULATE_GRAD_W == 1u;}\n')
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-",
                           "-I", os.path.join(ROOT, "include")], input=src, capture_output=True, text=True)
@@ -186,7 +186,7 @@ def fbx(lib, **over):
 @pytest.mark.parametrize("over,code", [
     (dict(gw_dtype=2), EDTYPE), (dict(gw_dtype=-1), EDTYPE),
     (dict(dtype=F32, gw_dtype=BF16), EDTYPE),
-    (dict(flags=2), EINVAL), (dict(flags=0x80000001), EINVAL),
+    (dict(flags=4), EINVAL), (dict(flags=0x80000001), EINVAL), (dict(flags=3, X_s=None), EINVAL),
     (dict(gw_dtype=F32, X_s=None), EINVAL), (dict(gw_dtype=F32, flags=1, ws_bytes=100), EWORKSPACE),
     (dict(gw_dtype=F32, gW=FAKE + 8), EALIGN),
 ])
@@ -214,8 +214,37 @@ def test_generalized_jsd_rejects(lib, over, code):
     assert jsd(lib, **over) == code
 
 
+def elem(lib, fn, **over):
+    a = dict(a=FAKE, b=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, reduction=0,
+             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    if fn == "logprob":
+        return lib.fljsd_jsd_logprob(a["a"], a["b"], a["BT"], a["V"], a["ld"], a["dtype"], a["beta"],
+                                     a["reduction"], a["loss"], a["grad"], a["ws"], a["ws_bytes"],
+                                     a["stream"])
+    return lib.fljsd_tvd(a["a"], a["b"], a["BT"], a["V"], a["ld"], a["dtype"], a["reduction"],
+                         a["loss"], a["grad"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["logprob", "tvd"])
+@pytest.mark.parametrize("over,code", [
+    (dict(a=None), EINVAL), (dict(b=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=-1), EINVAL), (dict(ld=100), EINVAL), (dict(dtype=3), EDTYPE),
+    (dict(reduction=9), EDTYPE), (dict(b=FAKE + 2), EALIGN), (dict(grad=FAKE + 4), EALIGN),
+    (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
+])
+def test_elementwise_losses_reject(lib, fn, over, code):
+    assert elem(lib, fn, **over) == code
+    assert lib.fljsd_last_error()
+
+
+def test_logprob_rejects_beta(lib):
+    assert elem(lib, "logprob", beta=1.5) == EINVAL
+    assert elem(lib, "logprob", beta=float("nan")) == EINVAL
+
+
 def test_profile_interface_without_work(lib):
-    n = 8
+    n = 10
     ms = (ctypes.c_double * n)()
     launches = (ctypes.c_int64 * n)()
     assert lib.fljsd_profile_enable(1) == OK
