@@ -33,6 +33,10 @@ What it computes, and where the pages fix it:
   * Two adjacent public losses over given distributions: the generalized
     JSD in log-probability space (PR #1352, Open question 3) and the total
     variation distance with the p == q gradient fix (PR #1374).
+  * The fused-linear cross-entropy that PR #1352 (Details) names as the
+    pattern the JSD path follows: lm_head logits, a two-pass online softmax,
+    hard labels with an ignore index, optional label smoothing, and
+    grad_input / grad_weight products as above.
   * Reductions: batchmean divides by the number of rows. PR #1374's tie table
     prints -0.0625 at (8, 512) for a -0.5 per-element TVD slope, i.e. a scale
     of 1/8 = 1/rows. sum uses 1, mean uses 1/(rows*V), none returns per-row
@@ -238,6 +242,81 @@ def fused_linear_jsd(X_s, W_s, X_t, W_t, beta: float, temperature: float,
         dZ = dA * (scale / temperature)
         grad_X[r0:r1] = dZ @ W_s
         grad_W += dZ.T @ X_s[r0:r1]
+        row_loss[r0:r1] = loss_rows
+    loss = row_loss if reduction == "none" else scale * np.sum(row_loss)
+    return loss, grad_X, grad_W
+
+
+def cross_entropy_rows(logits, labels, ignore_index: int = -100,
+                       label_smoothing: float = 0.0):
+    """Per-row cross-entropy with hard labels and its gradient w.r.t. the
+    logits, unscaled (the cross-entropy the fused-linear pattern of PR #1352,
+    Details, comes from: a two-pass online softmax over the lm_head logits).
+
+    With q = softmax(z) over the row and eps = label_smoothing:
+        loss_r = -(1 - eps) log q[y] - (eps / V) sum_v log q[v]
+        dz_r   = q - (1 - eps) onehot(y) - eps / V
+    Rows whose label is ignore_index, or outside [0, V), are ignored: loss 0,
+    gradient 0. Returns (row_loss[R], dz[R, V], valid[R] bool).
+    """
+    if not 0.0 <= label_smoothing <= 1.0:
+        raise ValueError("label_smoothing must be in [0, 1]")
+    z = np.asarray(logits, dtype=np.float64)
+    y = np.asarray(labels, dtype=np.int64)
+    R, V = z.shape
+    valid = (y != ignore_index) & (y >= 0) & (y < V)
+    logq = log_softmax(z)
+    yc = np.where(valid, y, 0)
+    logq_y = logq[np.arange(R), yc]
+    eps = label_smoothing
+    row_loss = -(1.0 - eps) * logq_y - (eps / V) * np.sum(logq, axis=-1)
+    dz = np.exp(logq) - eps / V
+    dz[np.arange(R), yc] -= (1.0 - eps)
+    row_loss = np.where(valid, row_loss, 0.0)
+    dz = np.where(valid[:, None], dz, 0.0)
+    return row_loss, dz, valid
+
+
+def ce_reduction_scale(reduction: str, rows: int, n_valid: int) -> float:
+    """mean: 1 / (number of rows whose label counts), the usual cross-entropy
+    mean (nan when no row counts); batchmean: 1 / rows; sum and none: 1."""
+    if reduction == "mean":
+        return 1.0 / n_valid if n_valid > 0 else float("nan")
+    if reduction == "batchmean":
+        return 1.0 / float(rows)
+    if reduction in ("sum", "none"):
+        return 1.0
+    raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def fused_linear_cross_entropy(X, W, labels, ignore_index: int = -100,
+                               label_smoothing: float = 0.0, reduction: str = "mean",
+                               block_rows: int = 256):
+    """Loss, grad_input and grad_weight of the fused-linear cross-entropy:
+    Z = X W^T, cross-entropy over each row of Z (cross_entropy_rows), then
+    grad_X = dZ W and grad_W = dZ^T X with dZ = scale * dz. Rows are processed
+    in blocks only to bound memory; grad_W accumulates in fp64. With no
+    counted row, the mean is nan and the gradients are 0.
+    Returns (loss, grad_X [BT, H], grad_W [V, H]); loss is per-row for "none".
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    y = np.asarray(labels, dtype=np.int64)
+    BT = X.shape[0]
+    V = W.shape[0]
+    n_valid = int(np.sum((y != ignore_index) & (y >= 0) & (y < V)))
+    scale = ce_reduction_scale(reduction, BT, n_valid)
+    gscale = scale if n_valid > 0 else 0.0
+    grad_X = np.empty_like(X)
+    grad_W = np.zeros_like(W)
+    row_loss = np.empty(BT, dtype=np.float64)
+    for r0 in range(0, BT, block_rows):
+        r1 = min(BT, r0 + block_rows)
+        Z = X[r0:r1] @ W.T
+        loss_rows, dz, _ = cross_entropy_rows(Z, y[r0:r1], ignore_index, label_smoothing)
+        dZ = dz * gscale
+        grad_X[r0:r1] = dZ @ W
+        grad_W += dZ.T @ X[r0:r1]
         row_loss[r0:r1] = loss_rows
     loss = row_loss if reduction == "none" else scale * np.sum(row_loss)
     return loss, grad_X, grad_W

@@ -396,6 +396,100 @@ def pin_tvd_finite_differences(o):
             assert abs(fd - g[idx]) <= 1e-7, f"tvd fd {red} {idx}"
 
 
+# ---- fused-linear cross-entropy ------------------------------------------------------------
+
+def _ce_case(seed, R=9, V=13, H=6, ignore=-100):
+    rng = _rng(seed)
+    X = rng.standard_normal((R, H))
+    W = rng.standard_normal((V, H)) * 0.5
+    y = rng.integers(0, V, size=R)
+    y[1] = ignore
+    y[-1] = ignore
+    return X, W, y
+
+
+def pin_ce_torch_library(o):
+    """Row losses and every reduction equal torch's fp64 CPU cross_entropy,
+    with ignored labels and label smoothing."""
+    import torch
+    import torch.nn.functional as F
+    X, W, y = _ce_case(41)
+    Z = X @ W.T
+    for eps in (0.0, 0.1, 0.7):
+        rows, _, valid = o.cross_entropy_rows(Z, y, -100, eps)
+        ref = F.cross_entropy(torch.from_numpy(Z), torch.from_numpy(y), ignore_index=-100,
+                              label_smoothing=eps, reduction="none").numpy()
+        assert np.allclose(rows, ref, rtol=1e-12, atol=1e-14), f"rows eps={eps}"
+        for red in ("mean", "sum", "none"):
+            loss, _, _ = o.fused_linear_cross_entropy(X, W, y, -100, eps, red, block_rows=4)
+            ref = F.cross_entropy(torch.from_numpy(Z), torch.from_numpy(y), ignore_index=-100,
+                                  label_smoothing=eps, reduction=red).numpy()
+            assert np.allclose(loss, ref, rtol=1e-12, atol=1e-14), f"{red} eps={eps}"
+        assert valid.sum() == len(y) - 2
+
+
+def pin_ce_autograd(o):
+    """grad_X and grad_W equal torch autograd of linear + cross_entropy (fp64)."""
+    import torch
+    import torch.nn.functional as F
+    X, W, y = _ce_case(42)
+    for eps in (0.0, 0.2):
+        for red in ("mean", "sum"):
+            tX = torch.from_numpy(X.copy()).requires_grad_(True)
+            tW = torch.from_numpy(W.copy()).requires_grad_(True)
+            F.cross_entropy(tX @ tW.T, torch.from_numpy(y), ignore_index=-100, label_smoothing=eps,
+                            reduction=red).backward()
+            _, gX, gW = o.fused_linear_cross_entropy(X, W, y, -100, eps, red, block_rows=3)
+            assert np.allclose(gX, tX.grad.numpy(), rtol=1e-11, atol=1e-14), f"gX {red} {eps}"
+            assert np.allclose(gW, tW.grad.numpy(), rtol=1e-11, atol=1e-14), f"gW {red} {eps}"
+
+
+def pin_ce_finite_differences(o):
+    """Gradients by central differences of the summed loss on a tiny case."""
+    X, W, y = _ce_case(43, R=4, V=5, H=3, ignore=7)
+    h = 1e-6
+    _, gX, gW = o.fused_linear_cross_entropy(X, W, y, 7, 0.3, "sum", block_rows=2)
+    for A, G in ((X, gX), (W, gW)):
+        for idx in np.ndindex(*A.shape):
+            Ap = A.copy()
+            Am = A.copy()
+            Ap[idx] += h
+            Am[idx] -= h
+            args_p = (Ap, W) if A is X else (X, Ap)
+            args_m = (Am, W) if A is X else (X, Am)
+            fd = (o.fused_linear_cross_entropy(*args_p, y, 7, 0.3, "sum")[0] -
+                  o.fused_linear_cross_entropy(*args_m, y, 7, 0.3, "sum")[0]) / (2 * h)
+            assert abs(fd - G[idx]) <= 1e-7 * max(1.0, abs(fd)), f"fd {idx}"
+
+
+def pin_ce_closed_forms(o):
+    """Uniform logits give log V per counted row; each row of dz sums to 0;
+    with no counted row the sum is 0, the mean nan, and the gradients 0."""
+    V = 11
+    Z = np.zeros((3, V))
+    rows, dz, _ = o.cross_entropy_rows(Z, np.array([0, 4, 10]), -100, 0.25)
+    assert np.allclose(rows, math.log(V), rtol=1e-14)
+    rows, dz, _ = o.cross_entropy_rows(_logits(44, 5, V, 3.0), np.array([1, 2, 3, 4, -100]), -100, 0.1)
+    assert np.allclose(dz.sum(axis=-1), 0.0, atol=1e-15)
+    X, W, _ = _ce_case(45)
+    y = np.full(X.shape[0], -100)
+    loss, gX, gW = o.fused_linear_cross_entropy(X, W, y, -100, 0.0, "sum")
+    assert loss == 0.0 and np.all(gX == 0.0) and np.all(gW == 0.0)
+    loss, gX, gW = o.fused_linear_cross_entropy(X, W, y, -100, 0.0, "mean")
+    assert math.isnan(loss) and np.all(gX == 0.0) and np.all(gW == 0.0)
+
+
+def pin_ce_blocks_and_batchmean(o):
+    """Results do not depend on the row blocking; batchmean divides by all rows."""
+    X, W, y = _ce_case(46, R=10)
+    a = o.fused_linear_cross_entropy(X, W, y, -100, 0.1, "sum", block_rows=1)
+    b = o.fused_linear_cross_entropy(X, W, y, -100, 0.1, "sum", block_rows=256)
+    for u, v in zip(a, b):
+        assert np.allclose(u, v, rtol=1e-13, atol=1e-15)
+    bm = o.fused_linear_cross_entropy(X, W, y, -100, 0.1, "batchmean")[0]
+    assert abs(bm - a[0] / 10) <= 1e-14
+
+
 ALL_PINS = [
     pin_log_softmax_library,
     pin_batchmean_scale_golden,
@@ -418,6 +512,11 @@ ALL_PINS = [
     pin_tvd_golden_ties,
     pin_tvd_library_and_closed_form,
     pin_tvd_finite_differences,
+    pin_ce_torch_library,
+    pin_ce_autograd,
+    pin_ce_finite_differences,
+    pin_ce_closed_forms,
+    pin_ce_blocks_and_batchmean,
 ]
 
 

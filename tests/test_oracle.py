@@ -63,6 +63,12 @@ MUTANTS = [
     ("tvd_dropped_half", "elem = 0.5 * np.abs(diff)", "elem = np.abs(diff)", 1),
     ("tvd_grad_wrong_sign", "grad = scale * 0.5 * np.sign(diff)", "grad = -scale * 0.5 * np.sign(diff)", 1),
     ("tvd_grad_unscaled", "grad = scale * 0.5 * np.sign(diff)", "grad = 0.5 * np.sign(diff)", 1),
+    ("ce_smoothing_divisor", "(eps / V) * np.sum(logq, axis=-1)", "eps * np.sum(logq, axis=-1)", 1),
+    ("ce_onehot_weight", "dz[np.arange(R), yc] -= (1.0 - eps)", "dz[np.arange(R), yc] -= 1.0", 1),
+    ("ce_mean_over_rows", 'return 1.0 / n_valid if n_valid > 0 else float("nan")', "return 1.0 / rows", 1),
+    ("ce_ignored_rows_kept", "row_loss = np.where(valid, row_loss, 0.0)", "row_loss = row_loss", 1),
+    ("ce_grad_unscaled", "dZ = dz * gscale", "dZ = dz", 1),
+    ("ce_smoothing_grad_dropped", "dz = np.exp(logq) - eps / V", "dz = np.exp(logq)", 1),
 ]
 
 
