@@ -219,6 +219,46 @@ int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, int64_t ld,
               int dtype, int reduction, float* loss, void* grad_p,
               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fljsd_flce_forward_backward - fused-linear cross-entropy with hard labels,
+ * forward and backward: the pattern the JSD pass follows (PR #1352, Details:
+ * lm_head GEMM, online softmax in two passes, gradient written over the
+ * logits in place; PR #1429: grad_weight written straight from the product,
+ * first chunk overwriting).
+ *
+ *   X [BT, H], W [V, H] in dtype (16-byte aligned, H a multiple of 8 bf16 /
+ *             4 fp32 elements); labels [BT] int64 (8-byte aligned).
+ *   A row counts unless its label is ignore_index or lies outside [0, V);
+ *   a row that does not count has loss 0 and gradient 0.
+ *   label_smoothing eps in [0, 1]: row loss
+ *             lse - (1 - eps) z_y - (eps / V) sum_v z_v, with lse the row's
+ *             log-sum-exp of the logits z = X W^T (eps = 0: -log softmax(z)_y).
+ *   reduction FLJSD_MEAN: sum over counted rows / number of counted rows
+ *             (nan loss and zero gradients when none counts); FLJSD_BATCHMEAN:
+ *             / BT; FLJSD_SUM; FLJSD_NONE: loss[r] per row.
+ *   num_chunks as for fljsd_forward_backward (0: fljsd_flce_plan_num_chunks
+ *             for the workspace size).
+ * Outputs (every element written): loss fp32 (1 or BT values); grad_X
+ *   [BT, H] and grad_W [V, H] in dtype, each optional (NULL skips it).
+ * Workspace: at least fljsd_flce_workspace_size(BT, H, V, dtype, num_chunks).
+ * Errors: FLJSD_EINVAL (NULL required pointer, sizes <= 0, label_smoothing
+ *   outside [0, 1] or nan, num_chunks < 0), FLJSD_EDTYPE, FLJSD_EALIGN,
+ *   FLJSD_EWORKSPACE, FLJSD_EDEVICE, FLJSD_EHIP.
+ */
+int fljsd_flce_forward_backward(const void* X, const void* W, const int64_t* labels,
+                                int64_t BT, int64_t H, int64_t V, int dtype,
+                                int64_t ignore_index, float label_smoothing,
+                                int reduction, int num_chunks, float* loss,
+                                void* grad_X, void* grad_W,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of fljsd_flce_forward_backward (0 for invalid arguments),
+ * and the smallest chunk count whose workspace fits `budget_bytes` (or a
+ * negative status code). Host-only. */
+size_t fljsd_flce_workspace_size(int64_t BT, int64_t H, int64_t V, int dtype, int num_chunks);
+int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
+                               size_t budget_bytes);
+
 /* Workspace bytes fljsd_forward_backward needs for this shape with
  * num_chunks >= 1 chunks. Pure host arithmetic; no device is touched.
  * Returns 0 for invalid arguments (sizes <= 0, num_chunks < 1, bad dtype). */
@@ -263,7 +303,9 @@ const char* fljsd_last_error(void);
 #define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss */
 #define FLJSD_KCLASS_TRANSPOSE 8        /* dZ^T and X_s^T for the grad_W product */
 #define FLJSD_KCLASS_ELEM_LOSS 9        /* fljsd_jsd_logprob / fljsd_tvd element pass */
-#define FLJSD_KCLASS_COUNT 10
+#define FLJSD_KCLASS_CE_STATS 10        /* cross-entropy pass 1: row max / denominator */
+#define FLJSD_KCLASS_CE_GRAD 11         /* cross-entropy pass 2: dZ in place, row loss */
+#define FLJSD_KCLASS_COUNT 12
 
 int fljsd_profile_enable(int enable);
 int fljsd_profile_read(double* total_ms, int64_t* launches, double* flops,

@@ -174,6 +174,120 @@ int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int
   return FLJSD_OK;
 }
 
+// ---- the per-chunk GEMMs shared by the JSD and cross-entropy passes --------
+
+// Z[rows, ldz] = X[rows, H] W[V, H]^T, rounded once to the dtype.
+int run_logits_gemm(int dtype, const void* X, const void* W, void* Z, int64_t rows, int64_t V,
+                    int64_t H, int64_t ldz, hipStream_t s) {
+  GemmArgs g;
+  g.A = X;
+  g.B = W;
+  g.C = Z;
+  g.M = rows;
+  g.N = V;
+  g.K = H;
+  g.lda = H;
+  g.ldb = H;
+  g.ldc = ldz;
+  g.a_kcontig = true;
+  g.b_kcontig = true;
+  g.epilogue = kEpiStore;
+  g.splitk = 1;
+  g.k_per_split = H;
+  g.group_m = 4;
+  hipError_t e = timed(s, FLJSD_KCLASS_GEMM_LOGITS, 2.0 * rows * V * H,
+                       gemm_bytes(g, dtype_size(dtype)), [&] { return gemm(dtype, g, s); });
+  return e == hipSuccess ? FLJSD_OK : fail_hip(e, "launch logits GEMM");
+}
+
+// gx[rows, H] = dZ[rows, ldz] W[V, H]; bf16 splits K when the output has few
+// tiles, summing fp32 partials (in `partial`) in split order.
+int run_grad_input(int dtype, const void* dZ, int64_t ldz, const void* W, int64_t rows,
+                   int64_t H, int64_t V, void* gx, int splitk, int64_t k_per_split,
+                   void* partial, hipStream_t s) {
+  const int es = dtype_size(dtype);
+  GemmArgs g;
+  g.A = dZ;
+  g.B = W;
+  g.M = rows;
+  g.N = H;
+  g.K = V;
+  g.lda = ldz;
+  g.ldb = H;
+  g.ldc = H;
+  g.a_kcontig = true;
+  g.b_kcontig = false;
+  g.group_m = 8;
+  const bool split = dtype == FLJSD_BF16 && splitk > 1;
+  if (split) {
+    g.C = partial;
+    g.epilogue = kEpiPartialF32;
+    g.splitk = splitk;
+    g.k_per_split = k_per_split;
+  } else {
+    g.C = gx;
+    g.epilogue = kEpiStore;
+    g.splitk = 1;
+    g.k_per_split = V;
+  }
+  hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_INPUT, 2.0 * rows * H * V, gemm_bytes(g, es),
+                       [&] { return gemm(dtype, g, s); });
+  if (e != hipSuccess) return fail_hip(e, "launch grad_input GEMM");
+  if (split) {
+    const double red_bytes = static_cast<double>(rows) * H * (4.0 * splitk + es);
+    e = timed(s, FLJSD_KCLASS_SPLITK_REDUCE, 0.0, red_bytes, [&] {
+      return launch_splitk_reduce(static_cast<const float*>(partial), splitk, rows, H, gx, H,
+                                  dtype, s);
+    });
+    if (e != hipSuccess) return fail_hip(e, "launch split-K reduce");
+  }
+  return FLJSD_OK;
+}
+
+// gW[V, H] (epilogue: store or add, bf16 or fp32) = dZ[rows, ldz]^T X[rows, H].
+// `transposed`: first write dZ^T [V, ldt] to dzt and X^T [H, ldt] to xt, so
+// both operands are K-contiguous for the direct-copy matrix-core path.
+int run_grad_weight(int dtype, const void* dZ, int64_t ldz, const void* X, int64_t rows,
+                    int64_t H, int64_t V, void* gW, bool transposed, void* dzt, void* xt,
+                    int64_t ldt, int epilogue, hipStream_t s) {
+  const int es = dtype_size(dtype);
+  GemmArgs g;
+  if (transposed) {
+    const double tbytes = 2.0 * static_cast<double>(rows) * (V + H) * es;
+    hipError_t e = timed(s, FLJSD_KCLASS_TRANSPOSE, 0.0, tbytes, [&] {
+      hipError_t t = launch_transpose_bf16(dZ, rows, V, ldz, dzt, ldt, s);
+      if (t != hipSuccess) return t;
+      return launch_transpose_bf16(X, rows, H, H, xt, ldt, s);
+    });
+    if (e != hipSuccess) return fail_hip(e, "launch transpose");
+    g.A = dzt;                    // A(m=v, k=r) = dZ^T[v, r]
+    g.B = xt;                     // B(n=h, k=r) = X^T[h, r]
+    g.lda = ldt;
+    g.ldb = ldt;
+    g.a_kcontig = true;
+    g.b_kcontig = true;
+  } else {
+    g.A = dZ;                     // A(m=v, k=r) = dZ[r, v]
+    g.B = X;                      // B(n=h, k=r) = X[r, h]
+    g.lda = ldz;
+    g.ldb = H;
+    g.a_kcontig = false;
+    g.b_kcontig = false;
+  }
+  g.C = gW;
+  g.M = V;
+  g.N = H;
+  g.K = rows;
+  g.ldc = H;
+  g.epilogue = epilogue;
+  g.splitk = 1;
+  g.k_per_split = rows;
+  g.group_m = 1;
+  hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H * V, gemm_bytes(g, es),
+                       [&] { return gemm(dtype, g, s); });
+  return e == hipSuccess ? FLJSD_OK : fail_hip(e, "launch grad_weight GEMM");
+}
+
 }  // namespace
 }  // namespace fljsd
 
@@ -337,28 +451,9 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
     const int64_t r0 = ci * plan.C;
     const int64_t rows = std::min(plan.C, BT - r0);
 
-    for (int who = 0; who < 2; ++who) {
-      GemmArgs g;
-      const int64_t H = who == 0 ? H_s : H_t;
-      g.A = (who == 0 ? Xs : Xt) + r0 * H * es;
-      g.B = who == 0 ? W_s : W_t;
-      g.C = who == 0 ? Zs : Zt;
-      g.M = rows;
-      g.N = V;
-      g.K = H;
-      g.lda = H;
-      g.ldb = H;
-      g.ldc = plan.ldz;
-      g.a_kcontig = true;
-      g.b_kcontig = true;
-      g.epilogue = kEpiStore;
-      g.splitk = 1;
-      g.k_per_split = H;
-      g.group_m = 4;
-      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_LOGITS, 2.0 * rows * V * H, gemm_bytes(g, es),
-                           [&] { return gemm(dtype, g, s); });
-      if (e != hipSuccess) return fail_hip(e, "launch logits GEMM");
-    }
+    rc = run_logits_gemm(dtype, Xs + r0 * H_s * es, W_s, Zs, rows, V, H_s, plan.ldz, s);
+    if (rc == FLJSD_OK) rc = run_logits_gemm(dtype, Xt + r0 * H_t * es, W_t, Zt, rows, V, H_t, plan.ldz, s);
+    if (rc != FLJSD_OK) return rc;
 
     ja.rows = rows;
     ja.row_loss = row_loss + r0;
@@ -366,92 +461,24 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
     if (rc != FLJSD_OK) return rc;
 
     if (grad_X_s) {
-      GemmArgs g;
-      g.A = Zs;
-      g.B = W_s;
-      g.M = rows;
-      g.N = H_s;
-      g.K = V;
-      g.lda = plan.ldz;
-      g.ldb = H_s;
-      g.a_kcontig = true;
-      g.b_kcontig = false;
-      g.group_m = 8;
-      const bool split = dtype == FLJSD_BF16 && plan.splitk > 1;
-      char* gx = static_cast<char*>(grad_X_s) + r0 * H_s * es;
-      if (split) {
-        g.C = ws + plan.off_partial;
-        g.ldc = H_s;
-        g.epilogue = kEpiPartialF32;
-        g.splitk = plan.splitk;
-        g.k_per_split = plan.k_per_split;
-      } else {
-        g.C = gx;
-        g.ldc = H_s;
-        g.epilogue = kEpiStore;
-        g.splitk = 1;
-        g.k_per_split = V;
-      }
-      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_INPUT, 2.0 * rows * H_s * V,
-                           gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
-      if (e != hipSuccess) return fail_hip(e, "launch grad_input GEMM");
-      if (split) {
-        const double red_bytes = static_cast<double>(rows) * H_s * (4.0 * plan.splitk + es);
-        e = timed(s, FLJSD_KCLASS_SPLITK_REDUCE, 0.0, red_bytes, [&] {
-          return launch_splitk_reduce(static_cast<const float*>(g.C), plan.splitk, rows, H_s,
-                                      gx, H_s, dtype, s);
-        });
-        if (e != hipSuccess) return fail_hip(e, "launch split-K reduce");
-      }
+      rc = run_grad_input(dtype, Zs, plan.ldz, W_s, rows, H_s, V,
+                          static_cast<char*>(grad_X_s) + r0 * H_s * es, plan.splitk,
+                          plan.k_per_split, ws + plan.off_partial, s);
+      if (rc != FLJSD_OK) return rc;
     }
 
     if (grad_W_s) {
-      GemmArgs g;
-      if (plan.transposed_grad_w) {
-        // dZ^T [V, ldt] over the teacher logits (dead after the loss
-        // passes) and X_s^T [H_s, ldt]: both operands K-contiguous.
-        void* dzt = ws + plan.off_zt;
-        void* xt = ws + plan.off_xt;
-        const double tbytes = 2.0 * static_cast<double>(rows) * (V + H_s) * es;
-        hipError_t e = timed(s, FLJSD_KCLASS_TRANSPOSE, 0.0, tbytes, [&] {
-          hipError_t t = launch_transpose_bf16(Zs, rows, V, plan.ldz, dzt, plan.ldt, s);
-          if (t != hipSuccess) return t;
-          return launch_transpose_bf16(Xs + r0 * H_s * es, rows, H_s, H_s, xt, plan.ldt, s);
-        });
-        if (e != hipSuccess) return fail_hip(e, "launch transpose");
-        g.A = dzt;                    // A(m=v, k=r) = dZ^T[v, r]
-        g.B = xt;                     // B(n=h, k=r) = X_s^T[h, r]
-        g.lda = plan.ldt;
-        g.ldb = plan.ldt;
-        g.a_kcontig = true;
-        g.b_kcontig = true;
-      } else {
-        g.A = Zs;                     // A(m=v, k=r) = dZ[r, v]
-        g.B = Xs + r0 * H_s * es;     // B(n=h, k=r) = X_s[r, h]
-        g.lda = plan.ldz;
-        g.ldb = H_s;
-        g.a_kcontig = false;
-        g.b_kcontig = false;
-      }
-      g.C = grad_W_s;
-      g.M = V;
-      g.N = H_s;
-      g.K = rows;
-      g.ldc = H_s;
       // Chunk 0 overwrites unless the caller asked to add to grad_W's
       // contents; later chunks add. An fp32 grad_W takes the bf16 product
-      // unrounded (one-split fp32 store, or fp32 read-add-write).
+      // unrounded (one-split fp32 store, or fp32 read-add-write). With bf16
+      // inputs dZ^T goes over the teacher logits, dead after the loss passes.
       const bool add = ci > 0 || gw_add_existing;
-      if (gw_f32_acc)
-        g.epilogue = add ? kEpiAccumulateF32 : kEpiPartialF32;
-      else
-        g.epilogue = add ? kEpiAccumulate : kEpiStore;
-      g.splitk = 1;
-      g.k_per_split = rows;
-      g.group_m = 1;
-      hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H_s * V,
-                           gemm_bytes(g, es), [&] { return gemm(dtype, g, s); });
-      if (e != hipSuccess) return fail_hip(e, "launch grad_weight GEMM");
+      const int epi = gw_f32_acc ? (add ? kEpiAccumulateF32 : kEpiPartialF32)
+                                 : (add ? kEpiAccumulate : kEpiStore);
+      rc = run_grad_weight(dtype, Zs, plan.ldz, Xs + r0 * H_s * es, rows, H_s, V, grad_W_s,
+                           plan.transposed_grad_w, ws + plan.off_zt, ws + plan.off_xt, plan.ldt,
+                           epi, s);
+      if (rc != FLJSD_OK) return rc;
     }
   }
 
@@ -606,4 +633,115 @@ FLJSD_EXPORT int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, 
   return run_elem_loss(p, q, BT, V, ld, dtype, reduction, loss, grad_p, true, 0.0f,
                        kModeGeneralized, workspace, workspace_bytes, stream,
                        FLJSD_KCLASS_ELEM_LOSS, launch_tvd);
+}
+
+FLJSD_EXPORT size_t fljsd_flce_workspace_size(int64_t BT, int64_t H, int64_t V, int dtype,
+                                              int num_chunks) {
+  if (BT <= 0 || H <= 0 || V <= 0 || num_chunks < 1) return 0;
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
+  return plan_ce_chunks(BT, H, V, dtype, num_chunks).total;
+}
+
+FLJSD_EXPORT int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
+                                            size_t budget_bytes) {
+  g_last_error.clear();
+  if (BT <= 0 || H <= 0 || V <= 0) return fail(FLJSD_EINVAL, "sizes must be > 0");
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
+  const int64_t nc = policy_num_chunks_ce(BT, H, V, dtype, budget_bytes);
+  if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the budget");
+  if (nc > INT32_MAX) return fail(FLJSD_EINVAL, "chunk count overflows int");
+  return static_cast<int>(nc);
+}
+
+FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const int64_t* labels,
+                                             int64_t BT, int64_t H, int64_t V, int dtype,
+                                             int64_t ignore_index, float label_smoothing,
+                                             int reduction, int num_chunks, float* loss,
+                                             void* grad_X, void* grad_W, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (!X || !W || !labels || !loss) return fail(FLJSD_EINVAL, "X, W, labels and loss must not be NULL");
+  if (BT <= 0 || H <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT, H and V must be > 0");
+  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
+  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
+  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
+    return fail(FLJSD_EDTYPE, "unknown reduction");
+  if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
+    return fail(FLJSD_EINVAL, "label_smoothing must be in [0, 1]");
+  if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
+  const void* ptrs[] = {X, W, loss, grad_X, grad_W, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(labels) & 7u) != 0)
+    return fail(FLJSD_EALIGN, "labels must be 8-byte aligned");
+  if (H % dtype_vec(dtype) != 0) return fail(FLJSD_EALIGN, "H must be a multiple of 16 bytes of elements");
+  int64_t nc = num_chunks;
+  if (nc == 0) {
+    nc = policy_num_chunks_ce(BT, H, V, dtype, workspace_bytes);
+    if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
+  }
+  const CePlan plan = plan_ce_chunks(BT, H, V, dtype, nc);
+  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
+  if (workspace_bytes < plan.total)
+    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
+  int rc = check_device();
+  if (rc != FLJSD_OK) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int es = dtype_size(dtype);
+  char* ws = static_cast<char*>(workspace);
+  void* Z = ws + plan.off_z;
+  float* scale = reinterpret_cast<float*>(ws + plan.off_scale);
+  float* row_loss = reduction == FLJSD_NONE ? loss : reinterpret_cast<float*>(ws + plan.off_row_loss);
+  const bool write_grad = grad_X != nullptr || grad_W != nullptr;
+  hipError_t e = launch_ce_scale(labels, BT, V, ignore_index, reduction, scale, s);
+  if (e != hipSuccess) return fail_hip(e, "launch label count");
+
+  CeArgs ca;
+  ca.z = Z;
+  ca.grad = Z;  // dZ replaces the logits in place
+  ca.ld = plan.ldz;
+  ca.vec_ok = true;
+  ca.V = V;
+  ca.slice_w = plan.slices.slice_w;
+  ca.S = plan.slices.S;
+  ca.ignore_index = ignore_index;
+  ca.eps = label_smoothing;
+  ca.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
+  ca.zy = reinterpret_cast<float*>(ws + plan.off_zy);
+  ca.scale = scale;
+  const char* Xc = static_cast<const char*>(X);
+  for (int64_t ci = 0; ci < plan.n_chunks; ++ci) {
+    const int64_t r0 = ci * plan.C;
+    const int64_t rows = std::min(plan.C, BT - r0);
+    rc = run_logits_gemm(dtype, Xc + r0 * H * es, W, Z, rows, V, H, plan.ldz, s);
+    if (rc != FLJSD_OK) return rc;
+    ca.rows = rows;
+    ca.labels = labels + r0;
+    ca.row_loss = row_loss + r0;
+    const double row_bytes = static_cast<double>(rows) * V * es;
+    e = timed(s, FLJSD_KCLASS_CE_STATS, 0.0, row_bytes, [&] { return launch_ce_stats(ca, dtype, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch ce_stats");
+    e = timed(s, FLJSD_KCLASS_CE_GRAD, 0.0, write_grad ? 2 * row_bytes : 0.0,
+              [&] { return launch_ce_grad(ca, dtype, write_grad, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch ce_grad");
+    if (grad_X) {
+      rc = run_grad_input(dtype, Z, plan.ldz, W, rows, H, V,
+                          static_cast<char*>(grad_X) + r0 * H * es, plan.splitk,
+                          plan.k_per_split, ws + plan.off_partial, s);
+      if (rc != FLJSD_OK) return rc;
+    }
+    if (grad_W) {
+      rc = run_grad_weight(dtype, Z, plan.ldz, Xc + r0 * H * es, rows, H, V, grad_W,
+                           plan.transposed_grad_w, ws + plan.off_zt, ws + plan.off_xt, plan.ldt,
+                           ci == 0 ? kEpiStore : kEpiAccumulate, s);
+      if (rc != FLJSD_OK) return rc;
+    }
+  }
+  if (reduction != FLJSD_NONE) {
+    e = timed(s, FLJSD_KCLASS_LOSS_REDUCE, 0.0, 4.0 * BT,
+              [&] { return launch_loss_reduce_dev(row_loss, BT, scale, loss, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
+  }
+  return FLJSD_OK;
 }

@@ -51,44 +51,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-// Merge of two (max, denominator) pairs; maxima in logit units, denominators
-// in base 2 with scale k. Commutative bit for bit (max and a two-term IEEE
-// sum are), so both butterfly partners agree.
-__device__ inline void md_merge(float& m, float& d, float mo, float dof, float k) {
-  const float M = fmaxf(m, mo);
-  if (M == -INFINITY) {
-    m = -INFINITY;
-    d = 0.f;
-    return;
-  }
-  d = d * hw_exp2((m - M) * k) + dof * hw_exp2((mo - M) * k);
-  m = M;
-}
-
-// Fold 8 logits into a running (max, denominator).
-__device__ inline void md_update8(float& m, float& d, const float* z, float k) {
-  float mx = z[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
-  if (mx == -INFINITY) return;
-  if (mx > m) {
-    d *= hw_exp2((m - mx) * k);
-    m = mx;
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc += hw_exp2((z[i] - m) * k);
-  d += acc;
-}
-
-__device__ inline void wave_md(float& m, float& d, float k) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float mo = __shfl_xor(m, o, 64);
-    const float dof = __shfl_xor(d, o, 64);
-    md_merge(m, d, mo, dof, k);
-  }
-}
 
 // Per-element terms of the divergence; see the file comment. Inputs are the
 // log2 probabilities a_s, a_t. Outputs: Q and P, the loss term l, the

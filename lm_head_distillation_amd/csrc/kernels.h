@@ -51,6 +51,33 @@ struct ElemArgs {
 hipError_t launch_logprob_jsd(const ElemArgs& a, int dtype, hipStream_t s);
 hipError_t launch_tvd(const ElemArgs& a, int dtype, hipStream_t s);
 
+// Cross-entropy over a logits chunk with hard labels.
+struct CeArgs {
+  const void* z = nullptr;        // logits [rows, ld]
+  void* grad = nullptr;           // dZ [rows, ld]; may equal z
+  int64_t ld = 0;
+  bool vec_ok = true;
+  int64_t rows = 0;
+  int64_t V = 0;
+  int64_t slice_w = 0;
+  int S = 1;
+  const int64_t* labels = nullptr;  // [rows]
+  int64_t ignore_index = -100;
+  float eps = 0.f;                // label smoothing
+  float4* stats = nullptr;        // [rows * S] partial (m, d, sum z, -), d base 2
+  float* zy = nullptr;            // [rows] logit of the label
+  const float* scale = nullptr;   // device: [0] gradient scale, [1] loss scale
+  float* row_loss = nullptr;      // [rows]
+};
+// scale[0], scale[1] from the labels of all BT rows (reduction as fljsd_reduction).
+hipError_t launch_ce_scale(const int64_t* labels, int64_t BT, int64_t V, int64_t ignore_index,
+                           int reduction, float* scale, hipStream_t s);
+hipError_t launch_ce_stats(const CeArgs& a, int dtype, hipStream_t s);
+hipError_t launch_ce_grad(const CeArgs& a, int dtype, bool write_grad, hipStream_t s);
+// loss[0] = scale[1] * sum(row_loss[0..n)), deterministic order.
+hipError_t launch_loss_reduce_dev(const float* row_loss, int64_t n, const float* scale,
+                                  float* loss, hipStream_t s);
+
 // Loss passes. dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s);

@@ -93,6 +93,53 @@ JsdPlan plan_jsd(int64_t BT, int64_t V) {
   return p;
 }
 
+CePlan plan_ce_chunks(int64_t BT, int64_t H, int64_t V, int dtype, int64_t num_chunks) {
+  CePlan p;
+  p.C = cdiv(BT, num_chunks);
+  p.n_chunks = cdiv(BT, p.C);
+  p.ldz = round_up(V, kJsdVec);
+  p.ldt = round_up(p.C, kJsdVec);
+  p.slices = plan_slices(p.C, V);
+  const int64_t es = dtype_size(dtype);
+  if (dtype == 1) {
+    plan_splitk(p.C, H, V, &p.splitk, &p.k_per_split);
+  } else {
+    p.splitk = 1;
+    p.k_per_split = V;
+  }
+  p.transposed_grad_w = dtype == 1;
+  size_t off = 0;
+  p.off_z = off;
+  off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
+  p.off_zt = off;
+  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(V * p.ldt * es));
+  p.off_xt = off;
+  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H * p.ldt * es));
+  p.off_row_loss = off;
+  off = align256(off + static_cast<size_t>(BT) * 4);
+  p.off_stats = off;
+  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 16);
+  p.off_zy = off;
+  off = align256(off + static_cast<size_t>(p.C) * 4);
+  p.off_scale = off;
+  off = align256(off + 16);
+  p.off_partial = off;
+  if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H * 4);
+  p.total = off;
+  return p;
+}
+
+int64_t policy_num_chunks_ce(int64_t BT, int64_t H, int64_t V, int dtype, size_t budget) {
+  int64_t nc = 1;
+  while (nc <= BT) {
+    const CePlan p = plan_ce_chunks(BT, H, V, dtype, nc);
+    if (p.total <= budget) return nc;
+    if (p.C == 1) break;
+    nc = cdiv(BT, p.C - 1);
+  }
+  return 0;
+}
+
 int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
                           size_t budget) {
   // Distinct chunk sizes only: C = ceil(BT / nc) changes at most 2*sqrt(BT) times.

@@ -80,4 +80,18 @@ JsdPlan plan_jsd(int64_t BT, int64_t V);
 int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
                           size_t budget);
 
+// Fused-linear cross-entropy: one logits chunk, the same GEMM planning.
+struct CePlan {
+  int64_t C = 0, n_chunks = 0, ldz = 0, ldt = 0;
+  SlicePlan slices;
+  int splitk = 1;
+  int64_t k_per_split = 0;
+  bool transposed_grad_w = false;
+  size_t off_z = 0, off_zt = 0, off_xt = 0, off_row_loss = 0, off_stats = 0, off_zy = 0,
+         off_scale = 0, off_partial = 0, total = 0;
+};
+
+CePlan plan_ce_chunks(int64_t BT, int64_t H, int64_t V, int dtype, int64_t num_chunks);
+int64_t policy_num_chunks_ce(int64_t BT, int64_t H, int64_t V, int dtype, size_t budget);
+
 }  // namespace fljsd

@@ -24,7 +24,7 @@ REDUCTIONS = {"batchmean": 0, "sum": 1, "mean": 2, "none": 3}
 STATUS = {0: "FLJSD_OK", -1: "FLJSD_EINVAL", -2: "FLJSD_EDTYPE", -3: "FLJSD_EWORKSPACE",
           -4: "FLJSD_EALIGN", -5: "FLJSD_EHIP", -6: "FLJSD_EDEVICE"}
 KERNEL_CLASSES = ["gemm_logits", "jsd_stats", "jsd_loss", "jsd_grad", "gemm_grad_input",
-                  "splitk_reduce", "gemm_grad_weight", "loss_reduce", "transpose", "elem_loss"]
+                  "splitk_reduce", "gemm_grad_weight", "loss_reduce", "transpose", "elem_loss", "ce_stats", "ce_grad"]
 
 _lib = None
 
@@ -63,6 +63,13 @@ def load_library() -> ctypes.CDLL:
     lib.fljsd_jsd_logprob.restype = cint
     lib.fljsd_tvd.argtypes = [vp, vp, i64, i64, i64, cint, cint, vp, vp, vp, sz, vp]
     lib.fljsd_tvd.restype = cint
+    lib.fljsd_flce_forward_backward.argtypes = [vp, vp, vp, i64, i64, i64, cint, i64, f32, cint, cint,
+                                                vp, vp, vp, vp, sz, vp]
+    lib.fljsd_flce_forward_backward.restype = cint
+    lib.fljsd_flce_workspace_size.argtypes = [i64, i64, i64, cint, cint]
+    lib.fljsd_flce_workspace_size.restype = sz
+    lib.fljsd_flce_plan_num_chunks.argtypes = [i64, i64, i64, cint, sz]
+    lib.fljsd_flce_plan_num_chunks.restype = cint
     lib.fljsd_workspace_size.argtypes = [i64, i64, i64, i64, cint, cint]
     lib.fljsd_workspace_size.restype = sz
     lib.fljsd_generalized_jsd_workspace_size.argtypes = [i64, i64, cint]
@@ -331,6 +338,54 @@ def fljsd_tvd(p: torch.Tensor, q: torch.Tensor, reduction: str = "batchmean", *,
                        _stream(stream))
     _check(rc)
     return (loss if red == 3 else loss[0]), grad
+
+
+def fljsd_flce_workspace_size(BT: int, H: int, V: int, dtype: int, num_chunks: int) -> int:
+    return int(load_library().fljsd_flce_workspace_size(BT, H, V, dtype, num_chunks))
+
+
+def fljsd_flce_plan_num_chunks(BT: int, H: int, V: int, dtype: int, budget_bytes: int) -> int:
+    lib = load_library()
+    rc = lib.fljsd_flce_plan_num_chunks(BT, H, V, dtype, budget_bytes)
+    _check(rc if rc < 0 else 0)
+    return rc
+
+
+def fljsd_flce_forward_backward(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                                ignore_index: int = -100, label_smoothing: float = 0.0,
+                                reduction: str = "mean", num_chunks: int = 0, *,
+                                grad_input: bool = True, grad_weight: bool = True,
+                                workspace: Optional[torch.Tensor] = None, stream=None):
+    """Fused-linear cross-entropy forward + backward with hard labels.
+    Returns (loss, grad_X or None, grad_W or None)."""
+    lib = load_library()
+    _require_device(X, W)
+    dt = _dtype_code(X)
+    if _dtype_code(W) != dt:
+        raise ValueError("X and W must share one dtype")
+    BT, H = X.shape
+    V = W.shape[0]
+    if W.shape != (V, H):
+        raise ValueError("shape mismatch: X [BT,H], W [V,H]")
+    if labels.dtype != torch.int64 or labels.shape != (BT,) or not labels.is_cuda or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int64 GPU tensor of shape [BT]")
+    red = _reduction_code(reduction)
+    nc = int(num_chunks)
+    if nc == 0:
+        budget = workspace.numel() * workspace.element_size() if workspace is not None else default_budget_bytes()
+        nc = fljsd_flce_plan_num_chunks(BT, H, V, dt, budget)
+    if workspace is None:
+        workspace = torch.empty(fljsd_flce_workspace_size(BT, H, V, dt, nc), dtype=torch.uint8,
+                                device=X.device)
+    loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X.device)
+    gX = torch.empty_like(X) if grad_input else None
+    gW = torch.empty_like(W) if grad_weight else None
+    rc = lib.fljsd_flce_forward_backward(
+        X.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt, int(ignore_index),
+        float(label_smoothing), red, nc, loss.data_ptr(), _ptr(gX), _ptr(gW), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc)
+    return (loss if red == 3 else loss[0]), gX, gW
 
 
 def fljsd_profile_enable(enable: bool = True) -> None:

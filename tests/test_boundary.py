@@ -40,7 +40,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fljsd_forward_backward", "fljsd_forward_backward_ex", "fljsd_generalized_jsd",
-              "fljsd_jsd_logprob", "fljsd_tvd", "fljsd_workspace_size",
+              "fljsd_jsd_logprob", "fljsd_tvd", "fljsd_flce_forward_backward",
+              "fljsd_flce_workspace_size", "fljsd_flce_plan_num_chunks", "fljsd_workspace_size",
               "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
               "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read"):
         assert n in names
@@ -64,7 +65,7 @@ def test_header_compiles_as_c():
            'int (*fbx)(const void*, const void*, const void*, const void*, int64_t, int64_t, int64_t,'
            ' int64_t, int, float, float, int, int, float*, void*, void*, int, unsigned, void*, size_t,'
            ' void*) = fljsd_forward_backward_ex;\n'
-           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 10 '
+           'int main(void){return (fb == 0 || fbx == 0) && FLJSD_KCLASS_COUNT == 12 '
            '&& FLJSD_ACCUMULATE_GRAD_W == 1u;}\n')
     res = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", "-",
                           "-I", os.path.join(ROOT, "include")], input=src, capture_output=True, text=True)
@@ -236,6 +237,42 @@ def elem(lib, fn, **over):
 def test_elementwise_losses_reject(lib, fn, over, code):
     assert elem(lib, fn, **over) == code
     assert lib.fljsd_last_error()
+
+
+def flce(lib, **over):
+    a = dict(X=FAKE, W=FAKE, labels=FAKE, BT=8, H=64, V=512, dtype=BF16, ignore=-100, eps=0.0,
+             reduction=2, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return lib.fljsd_flce_forward_backward(a["X"], a["W"], a["labels"], a["BT"], a["H"], a["V"],
+                                           a["dtype"], a["ignore"], a["eps"], a["reduction"], a["nc"],
+                                           a["loss"], a["gX"], a["gW"], a["ws"], a["ws_bytes"],
+                                           a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(X=None), EINVAL), (dict(labels=None), EINVAL), (dict(loss=None), EINVAL),
+    (dict(BT=0), EINVAL), (dict(H=-1), EINVAL), (dict(V=0), EINVAL), (dict(eps=-0.1), EINVAL),
+    (dict(eps=1.5), EINVAL), (dict(eps=float("nan")), EINVAL), (dict(nc=-2), EINVAL),
+    (dict(dtype=5), EDTYPE), (dict(reduction=4), EDTYPE), (dict(X=FAKE + 8), EALIGN),
+    (dict(labels=FAKE + 4), EALIGN), (dict(gW=FAKE + 2), EALIGN), (dict(H=60), EALIGN),
+    (dict(ws_bytes=64), EWORKSPACE), (dict(nc=0, ws_bytes=64), EWORKSPACE), (dict(ws=None), EINVAL),
+])
+def test_flce_rejects(lib, over, code):
+    assert flce(lib, **over) == code
+    assert lib.fljsd_last_error()
+
+
+def test_flce_workspace_and_policy(lib):
+    BT, H, V = 8192, 4096, 128256
+    one = lib.fljsd_flce_workspace_size(BT, H, V, BF16, 1)
+    # logits chunk + dZ^T + X^T dominate
+    assert BT * V * 2 * 2 + BT * H * 2 <= one < BT * V * 2 * 2 + BT * H * 2 + 64 * 2**20
+    assert lib.fljsd_flce_workspace_size(BT, H, V, 7, 1) == 0
+    assert lib.fljsd_flce_workspace_size(BT, H, V, BF16, 0) == 0
+    assert lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, one) == 1
+    nc = lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, one // 3)
+    assert nc > 1 and lib.fljsd_flce_workspace_size(BT, H, V, BF16, nc) <= one // 3
+    assert lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, 100) == EWORKSPACE
 
 
 def test_logprob_rejects_beta(lib):

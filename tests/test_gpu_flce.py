@@ -1,0 +1,107 @@
+"""GPU parity of the fused-linear cross-entropy (fljsd_flce_forward_backward)
+against the oracle: hard labels with ignored and out-of-range rows, label
+smoothing, every reduction, chunk counts, ragged shapes, and the degenerate
+all-ignored batch."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_util import TOL, assert_loss_close, assert_tensor_close, from_device, to_device, \
+    to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fl():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lm_head_distillation_amd import fljsd
+    fljsd.load_library()
+    return fljsd
+
+
+def _case(seed, BT, H, V, dtype, ignore=-100):
+    w = workloads.Workload("flce", seed, BT, H, H, V, dtype, 0.5, 1.0, "mean", "independent")
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(seed)
+    labels = rng.integers(0, V, size=BT).astype(np.int64)
+    if BT >= 4:
+        labels[1] = ignore
+        labels[BT // 2] = ignore
+        labels[-1] = V + 5            # out of range: does not count
+    return inp["X_s"], inp["W_s"], labels
+
+
+def _run(fl, X, W, labels, dtype, ignore, eps, red, nc, **kw):
+    out = fl.fljsd_flce_forward_backward(to_device(X, dtype), to_device(W, dtype),
+                                         torch.from_numpy(labels).cuda(), ignore, eps, red, nc, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(dtype, got, ref, what=""):
+    loss, gX, gW = got
+    rl, rX, rW = ref
+    tol = TOL[dtype]
+    e0 = assert_loss_close(from_device(loss), rl, tol, f"loss {what}")
+    e1 = assert_tensor_close(from_device(gX), rX, tol, f"grad_X {what}")
+    e2 = assert_tensor_close(from_device(gW), rW, tol, f"grad_W {what}")
+    print(f"{what}: loss {e0:.2e} grad_X {e1:.2e} grad_W {e2:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none", "batchmean"])
+@pytest.mark.parametrize("nc", [1, 3])
+def test_tiny_f32(fl, eps, reduction, nc):
+    X, W, y = _case(601, 8, 64, 512, "f32")
+    got = _run(fl, X, W, y, "f32", -100, eps, reduction, nc)
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, "f32"), to_f64(W, "f32"), y, -100, eps,
+                                            reduction)
+    _check("f32", got, ref, f"{reduction} eps={eps} nc={nc}")
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+@pytest.mark.parametrize("nc", [1, 4])
+def test_multiblock_bf16(fl, eps, nc):
+    X, W, y = _case(602, 64, 256, 40960 + 37, "bf16", ignore=7)
+    got = _run(fl, X, W, y, "bf16", 7, eps, "mean", nc)
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, "bf16"), to_f64(W, "bf16"), y, 7, eps, "mean")
+    _check("bf16", got, ref, f"eps={eps} nc={nc}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("BT,H,V,nc", [
+    (1, 64, 100, 1), (300, 72, 1000, 7), (513, 264, 5003, 2), (10, 64, 777, 100),
+    (256, 1024, 32064, 1),
+])
+def test_shapes(fl, dtype, BT, H, V, nc):
+    X, W, y = _case(603, BT, H, V, dtype)
+    got = _run(fl, X, W, y, dtype, -100, 0.05, "mean", nc)
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, dtype), to_f64(W, dtype), y, -100, 0.05, "mean")
+    _check(dtype, got, ref, f"{BT}x{H}x{V} nc={nc}")
+
+
+def test_all_rows_ignored(fl):
+    X, W, _ = _case(604, 16, 64, 300, "bf16")
+    y = np.full(16, -100, dtype=np.int64)
+    loss, gX, gW = _run(fl, X, W, y, "bf16", -100, 0.0, "mean", 2)
+    assert np.isnan(float(loss))
+    assert int(torch.count_nonzero(gX)) == 0 and int(torch.count_nonzero(gW)) == 0
+    loss, gX, gW = _run(fl, X, W, y, "bf16", -100, 0.0, "sum", 2)
+    assert float(loss) == 0.0 and int(torch.count_nonzero(gX)) == 0
+
+
+def test_optional_gradients(fl):
+    X, W, y = _case(605, 40, 128, 2000, "bf16")
+    full = _run(fl, X, W, y, "bf16", -100, 0.0, "mean", 2)
+    only_loss = _run(fl, X, W, y, "bf16", -100, 0.0, "mean", 2, grad_input=False, grad_weight=False)
+    assert only_loss[1] is None and only_loss[2] is None
+    assert float(only_loss[0]) == float(full[0])
+    only_w = _run(fl, X, W, y, "bf16", -100, 0.0, "mean", 2, grad_input=False)
+    assert torch.equal(only_w[2].view(torch.int16), full[2].view(torch.int16))
