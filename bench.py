@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--sweep", action="store_true",
                    help="also time the 1024- and 8192-row workloads at 1, 8 and 32 chunks")
+    p.add_argument("--flce", action="store_true",
+                   help="also time the fused-linear cross-entropy at 1024..8192 rows")
     return p.parse_args()
 
 
@@ -139,6 +141,53 @@ def sweep(fljsd, steps, warmup):
             out.append(rec)
             del ws, out_t
         del X_s, W_s, X_t, W_t
+        torch.cuda.empty_cache()
+    return out
+
+
+# The pages' H100 figures for the fused-linear cross-entropy after the
+# grad_weight change (Liger-Kernel PR #1429, Details, default provider, bf16,
+# reduction mean, H = 4096, V = 128256): ms per full pass by rows. Context only.
+PAGES_FLCE_MS = {1024: 5.86, 2048: 9.75, 4096: 20.18, 8192: 37.34}
+
+
+def flce_sweep(fljsd, steps, warmup):
+    """ms per fwd+bwd pass of the fused-linear cross-entropy at the pages' sizes."""
+    import numpy as np
+    import torch
+
+    import workloads
+    H, V = 4096, 128256
+    W = workloads.draw(1101, (V, H), workloads.SIGMA_W, "bf16")
+    W = torch.from_numpy(W.view(np.int16)).view(torch.bfloat16).cuda()
+    out = []
+    for BT in (1024, 2048, 4096, 8192):
+        X = workloads.draw(1100 + BT, (BT, H), workloads.SIGMA_X, "bf16")
+        X = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).cuda()
+        labels = torch.from_numpy(np.random.default_rng(BT).integers(0, V, size=BT)).cuda()
+        nc = fljsd.fljsd_flce_plan_num_chunks(BT, H, V, fljsd.BF16, fljsd.default_budget_bytes())
+        ws = torch.empty(fljsd.fljsd_flce_workspace_size(BT, H, V, fljsd.BF16, nc),
+                         dtype=torch.uint8, device="cuda")
+        torch.cuda.reset_peak_memory_stats()
+
+        def step():
+            fljsd.fljsd_flce_forward_backward(X, W, labels, -100, 0.0, "mean", nc, workspace=ws)
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        rec = {"BT": BT, "num_chunks": nc, "ms_per_step": round(ms, 3),
+               "tokens_per_s": round(BT / ms * 1e3, 1),
+               "peak_hbm_mb": round(torch.cuda.max_memory_allocated() / 2**20, 1),
+               "pages_h100_ms": PAGES_FLCE_MS[BT]}
+        log(f"  flce BT={BT:5d} nc={nc}: {ms:7.2f} ms/step  {rec['tokens_per_s']:>10,.0f} tokens/s  "
+            f"peak {rec['peak_hbm_mb']:.0f} MB  (pages, H100: {PAGES_FLCE_MS[BT]} ms)")
+        out.append(rec)
+        del X, ws, labels
         torch.cuda.empty_cache()
     return out
 
@@ -270,6 +319,8 @@ def main():
     }
     if args.sweep:
         result["sweep"] = sweep(fljsd, max(3, args.steps // 2), 1)
+    if args.flce:
+        result["flce"] = flce_sweep(fljsd, max(3, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         del X_s, W_s, X_t, W_t, ws, gX, gW
         torch.cuda.empty_cache()
