@@ -283,6 +283,7 @@ int run_grad_weight(int dtype, const void* dZ, int64_t ldz, const void* X, int64
   g.splitk = 1;
   g.k_per_split = rows;
   g.group_m = 1;
+  g.wgrad = true;
   hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H * V, gemm_bytes(g, es),
                        [&] { return gemm(dtype, g, s); });
   return e == hipSuccess ? FLJSD_OK : fail_hip(e, "launch grad_weight GEMM");

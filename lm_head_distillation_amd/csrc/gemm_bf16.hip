@@ -4,24 +4,28 @@
 // beta*C are added in fp32 and rounded once).
 //
 // One kernel template serves the pass's three products:
-//   logits       Z[C,V]    = X[C,H] W[V,H]^T     A and B K-contiguous
-//   grad_input   gX[C,H]   = dZ[C,V] W[V,H]      A K-contiguous, B N-contiguous
-//   grad_weight  gW[V,H] (+)= dZ[C,V]^T X[C,H]   A M-contiguous, B N-contiguous
+//   logits       Z[C,V]    = X[C,H] W[V,H]^T       A and B K-contiguous
+//   grad_input   gX[C,H]   = dZ[C,V] W[V,H]        A K-contiguous, B N-contiguous
+//   grad_weight  gW[V,H] (+)= dZ^T[V,C] X^T[H,C]^T  A and B K-contiguous (the
+//                pass transposes dZ and X first; its own kernel symbol)
 // LDS always holds both operands K-contiguous ([row][k], 16-byte chunks
 // XOR-swizzled so fragment reads are bank-conflict free), so the matrix-core
 // loop is shared. A K-contiguous operand of a block inside the operands is
 // copied straight from global memory into LDS (gfx950 global_load_lds_dwordx4,
-// no registers); an M/N-contiguous one is read as 8 (m) x 4 (k) blocks of four
+// no registers); an N-contiguous one is read as 8 (n) x 4 (k) blocks of four
 // 16-byte row segments and transposed in registers into 8-byte LDS writes.
 //
 // Pipeline: K-tiles of 64 through two LDS stages (the template also builds
 // deeper pipelines of 32-wide K-tiles for two K-contiguous operands; on the
-// logits product they measured slower than two stages of 64). An
-// M/N-contiguous operand passes through registers. Edge blocks and a partial
-// last K-tile take a bounds-checked register path. Within a stage,
-// each 16-wide K step's fragments are read while the previous step's MFMAs
-// run. Workgroups are renumbered so the tiles one XCD runs together share
-// operand panels in that XCD's L2.
+// logits product they measured slower than two stages of 64). The two waves
+// sharing a SIMD issue the next tile's loads at different K steps, so one
+// keeps the matrix core busy while the other waits for its loads to be
+// accepted. Edge blocks and a partial last K-tile take a bounds-checked
+// register path. Within a stage, each 16-wide K step's fragments are read
+// while the previous step's MFMAs run. Workgroups are renumbered so the tiles
+// one XCD runs together share operand panels in that XCD's L2. Epilogues:
+// store (bf16), fp32 store (split-K partials, fp32 weight gradient), and
+// read-add-write in bf16 or fp32 for the weight gradient of later chunks.
 #include "kernels.h"
 #include "plan.h"
 
@@ -488,51 +492,13 @@ struct GemmKernel {
     }
   }
 
-  // Both operands through registers: every wave issues the next tile's
-  // loads before the stage's MFMAs (the staggered order spills registers
-  // here, and measured slower).
-  static __device__ inline void loop_regs(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
-                                          int64_t n0, int64_t kb, int nkf,
-                                          floatx16 (&acc)[TM][TN]) {
-    const uint16_t* A = static_cast<const uint16_t*>(g.A);
-    const uint16_t* B = static_cast<const uint16_t*>(g.B);
-    uint4 ra[regs(BM, false)], rb[regs(BN, false)];
-    load_tile_fast<BM, false>(A, g.lda, m0, kb, ra);
-    load_tile_fast<BN, false>(B, g.ldb, n0, kb, rb);
-    store_tile<BM, false>(lds[0], 0, ra);
-    store_tile<BN, false>(lds[0], BM, rb);
-    wait_vmem_upto(0);
-    __syncthreads();
-    for (int t = 0; t < nkf; ++t) {
-      uint4* cur = lds[t & 1];
-      uint4* nxt = lds[(t + 1) & 1];
-      const bool more = t + 1 < nkf;
-      if (more) {
-        const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
-        load_tile_fast<BM, false>(A, g.lda, m0, k0, ra);
-        load_tile_fast<BN, false>(B, g.ldb, n0, k0, rb);
-      }
-      compute_stage(cur, acc);
-      if (more) {
-        store_tile<BM, false>(nxt, 0, ra);
-        store_tile<BN, false>(nxt, BM, rb);
-      }
-      wait_vmem_upto(0);
-      __syncthreads();
-    }
-  }
-
   static __device__ inline void mainloop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                                int64_t m0, int64_t n0, int64_t kb, int nkf,
                                                floatx16 (&acc)[TM][TN]) {
-    if constexpr (A_K || B_K) {
-      if (late_wave())
-        loop_mixed<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
-      else
-        loop_mixed<0>(g, lds, m0, n0, kb, nkf, acc);
-    } else {
-      loop_regs(g, lds, m0, n0, kb, nkf, acc);
-    }
+    if (late_wave())
+      loop_mixed<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
+    else
+      loop_mixed<0>(g, lds, m0, n0, kb, nkf, acc);
   }
 
   // Bounds-checked K-tiles [t0, t1) through registers (edge blocks, and the
@@ -702,6 +668,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
                                                                        group_m);
 }
 
+// The same code under a second symbol for the weight-gradient product, whose
+// K-contiguous form (after the transposes) shares the logits product's layout.
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
+          int EPI>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_wgrad_kernel(GemmArgs g,
+                                                                                 int tiles_m,
+                                                                                 int tiles_n,
+                                                                                 int group_m) {
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI>::run(g, tiles_m, tiles_n,
+                                                                       group_m);
+}
+
 constexpr int kWavesM = 2;
 constexpr int kWavesN = 4;
 
@@ -720,8 +698,17 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   const dim3 block(kWavesM * kWavesN * 64);
   const int group_m = g.group_m > 0 ? static_cast<int>(std::min<int64_t>(g.group_m, tiles_m))
                                     : static_cast<int>(tiles_m);
-  hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, Pipe<A_K, B_K>::BK,
-                                       Pipe<A_K, B_K>::STAGES, kWavesM, kWavesN, A_K, B_K, EPI>),
+  constexpr int BK = Pipe<A_K, B_K>::BK, ST = Pipe<A_K, B_K>::STAGES;
+  if constexpr (A_K && B_K) {
+    if (g.wgrad) {
+      hipLaunchKernelGGL((gemm_bf16_wgrad_kernel<kGemmBM, kGemmBN, BK, ST, kWavesM, kWavesN, A_K,
+                                                 B_K, EPI>),
+                         grid, block, 0, s, g, static_cast<int>(tiles_m),
+                         static_cast<int>(tiles_n), group_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, BK, ST, kWavesM, kWavesN, A_K, B_K, EPI>),
                      grid, block, 0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
                      group_m);
   return hipGetLastError();
@@ -735,7 +722,7 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
     case kEpiPartialF32: return launch_cfg<A_K, B_K, kEpiPartialF32>(g, s);
     case kEpiAccumulateF32:
       // Only the weight-gradient product accumulates into an fp32 C.
-      if constexpr (A_K == B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);
+      if constexpr (A_K && B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
@@ -744,10 +731,11 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
-  // The three layouts the pass uses.
+  // The two layouts the pass uses: both operands K-contiguous (logits, and
+  // the weight gradient after its transposes), and B N-contiguous
+  // (grad_input's weight operand).
   if (g.a_kcontig && g.b_kcontig) return launch_layout<true, true>(g, s);
   if (g.a_kcontig && !g.b_kcontig) return launch_layout<true, false>(g, s);
-  if (!g.a_kcontig && !g.b_kcontig) return launch_layout<false, false>(g, s);
   return hipErrorInvalidValue;
 }
 

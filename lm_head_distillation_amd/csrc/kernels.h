@@ -113,6 +113,8 @@ struct GemmArgs {
   int splitk = 1;
   int64_t k_per_split = 0; // multiple of the K tile when splitk > 1
   int group_m = 0;         // M-tiles per tile group in the launch order (0: all)
+  bool wgrad = false;      // the weight-gradient product (its own kernel symbol, so
+                           // profiles tell it from the logits product)
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
