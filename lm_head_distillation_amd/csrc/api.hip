@@ -154,11 +154,21 @@ int check_common(int dtype, float beta, float temperature, int reduction) {
   return FLJSD_OK;
 }
 
+// The three loss passes. With `part_s` the row statistics come from the
+// logits GEMMs' partials (a merge over `tiles` per row) instead of pass 1's
+// read of both rows.
 int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int es,
-                   hipStream_t s) {
+                   hipStream_t s, const float2* part_s = nullptr, const float2* part_t = nullptr,
+                   int64_t tiles = 0) {
   const double row_bytes = static_cast<double>(ja.rows) * V * es;
-  hipError_t e = timed(s, FLJSD_KCLASS_JSD_STATS, 0.0, 2 * row_bytes,
-                       [&] { return launch_jsd_stats(ja, dtype, s); });
+  hipError_t e;
+  if (part_s) {
+    e = timed(s, FLJSD_KCLASS_JSD_STATS, 0.0, 16.0 * ja.rows * tiles,
+              [&] { return launch_jsd_stats_merge(ja, part_s, part_t, tiles, s); });
+  } else {
+    e = timed(s, FLJSD_KCLASS_JSD_STATS, 0.0, 2 * row_bytes,
+              [&] { return launch_jsd_stats(ja, dtype, s); });
+  }
   if (e != hipSuccess) return fail_hip(e, "launch jsd_stats");
   e = timed(s, FLJSD_KCLASS_JSD_LOSS, 0.0, 2 * row_bytes,
             [&] { return launch_jsd_loss(ja, dtype, s); });
@@ -176,9 +186,12 @@ int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int
 
 // ---- the per-chunk GEMMs shared by the JSD and cross-entropy passes --------
 
-// Z[rows, ldz] = X[rows, H] W[V, H]^T, rounded once to the dtype.
+// Z[rows, ldz] = X[rows, H] W[V, H]^T, rounded once to the dtype. With
+// `stat_part` (bf16), also each row's statistics per N-tile of the rounded
+// logits (max, sum 2^((z - max) stat_k)) into stat_part [rows, stat_tiles].
 int run_logits_gemm(int dtype, const void* X, const void* W, void* Z, int64_t rows, int64_t V,
-                    int64_t H, int64_t ldz, hipStream_t s) {
+                    int64_t H, int64_t ldz, hipStream_t s, float2* stat_part = nullptr,
+                    int64_t stat_tiles = 0, float stat_k = 0.f) {
   GemmArgs g;
   g.A = X;
   g.B = W;
@@ -191,7 +204,10 @@ int run_logits_gemm(int dtype, const void* X, const void* W, void* Z, int64_t ro
   g.ldc = ldz;
   g.a_kcontig = true;
   g.b_kcontig = true;
-  g.epilogue = kEpiStore;
+  g.epilogue = stat_part ? kEpiStoreStats : kEpiStore;
+  g.stat_part = stat_part;
+  g.stat_ld = stat_tiles;
+  g.stat_k = stat_k;
   g.splitk = 1;
   g.k_per_split = H;
   g.group_m = 4;
@@ -452,13 +468,18 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
     const int64_t r0 = ci * plan.C;
     const int64_t rows = std::min(plan.C, BT - r0);
 
-    rc = run_logits_gemm(dtype, Xs + r0 * H_s * es, W_s, Zs, rows, V, H_s, plan.ldz, s);
-    if (rc == FLJSD_OK) rc = run_logits_gemm(dtype, Xt + r0 * H_t * es, W_t, Zt, rows, V, H_t, plan.ldz, s);
+    float2* part_s = plan.gemm_stats ? reinterpret_cast<float2*>(ws + plan.off_spart) : nullptr;
+    float2* part_t = plan.gemm_stats ? part_s + plan.C * plan.stat_tiles : nullptr;
+    rc = run_logits_gemm(dtype, Xs + r0 * H_s * es, W_s, Zs, rows, V, H_s, plan.ldz, s, part_s,
+                         plan.stat_tiles, ja.k2);
+    if (rc == FLJSD_OK)
+      rc = run_logits_gemm(dtype, Xt + r0 * H_t * es, W_t, Zt, rows, V, H_t, plan.ldz, s, part_t,
+                           plan.stat_tiles, ja.k2);
     if (rc != FLJSD_OK) return rc;
 
     ja.rows = rows;
     ja.row_loss = row_loss + r0;
-    rc = run_jsd_passes(ja, dtype, write_grad, V, es, s);
+    rc = run_jsd_passes(ja, dtype, write_grad, V, es, s, part_s, part_t, plan.stat_tiles);
     if (rc != FLJSD_OK) return rc;
 
     if (grad_X_s) {

@@ -26,6 +26,7 @@
 // one XCD runs together share operand panels in that XCD's L2. Epilogues:
 // store (bf16), fp32 store (split-K partials, fp32 weight gradient), and
 // read-add-write in bf16 or fp32 for the weight gradient of later chunks.
+#include "elem_math.h"
 #include "kernels.h"
 #include "plan.h"
 
@@ -74,11 +75,33 @@ __device__ inline int swz(int r, int c) {
   }
 }
 
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// A lane's value after a DPP move within its 16-lane row (gfx9 encodings):
+// quad_perm [1,0,3,2] and [2,3,0,1] exchange with lane ^ 1 and lane ^ 2,
+// row_half_mirror pairs lane i with 7 - i in each group of eight, row_mirror
+// i with 15 - i in the row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Max and sum over a 32-lane half-wave, as butterflies: after each step both
+// partners hold the same value (max and two-term sums are commutative), so
+// mirror partners serve as well as xor partners. Every lane ends with the
+// result.
+__device__ inline float half_wave_max(float x) {
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp<kDppMirror>(x));
+  return fmaxf(x, __shfl_xor(x, 16, 64));
+}
+__device__ inline float half_wave_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  x += dpp<kDppMirror>(x);
+  return x + __shfl_xor(x, 16, 64);
 }
 
 __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
@@ -175,7 +198,12 @@ struct GemmKernel {
   // registers: the old values then come in as 8-byte loads, all issued
   // before any is used, so a block pays one memory latency instead of one
   // per batch of 2-byte loads.
-  static constexpr bool SWAP_D = EPI == kEpiAccumulate || EPI == kEpiAccumulateF32;
+  // The bf16 store epilogues use the same layout: a lane's four consecutive
+  // columns go to LDS as one 8-byte write (see epilogue_staged).
+  static constexpr bool SWAP_D = EPI == kEpiAccumulate || EPI == kEpiAccumulateF32 ||
+                                 EPI == kEpiStore || EPI == kEpiStoreStats;
+  static_assert(!SWAP_D || STAGES * LDS_STAGE * 16 >= BM * BN * 2,
+                "the staged epilogue holds the whole bf16 tile in LDS");
 
   // Register path: a K-contiguous tile of R rows moves in 16-byte chunks,
   // chunks(R) per thread; an M/N-contiguous one in 8 x 4 blocks, units(R) per
@@ -585,6 +613,80 @@ struct GemmKernel {
     }
   }
 
+  // bf16 store through LDS. The tile is written to LDS in 8-byte quads (a
+  // lane's four consecutive columns in the transposed accumulator layout),
+  // quad slot s of row r at s ^ (r % 16) so that the 16 rows one write
+  // instruction covers per half-wave land in distinct banks. Then each 32-lane
+  // half-wave reads one 512-byte row back in 16-byte chunks and stores it to
+  // C with 16-byte writes. STATS: the same half-wave reduces the row's
+  // rounded values to (max, sum 2^((z - max) k)) over the tile's valid
+  // columns and writes them as the row's partial for N-tile tn.
+  template <bool STATS>
+  static __device__ inline void epilogue_staged(const GemmArgs& g, int64_t m0, int64_t n0, int tn,
+                                                int lane, int wave_m, int wave_n,
+                                                floatx16 (&acc)[TM][TN], uint4* lds) {
+    constexpr int QPR = BN / 4;   // quads per row
+    constexpr int CPR16 = BN / 8; // 16-byte chunks per row
+    static_assert(CPR16 == 32, "one 32-lane half-wave per row");
+    uint2* quads = reinterpret_cast<uint2*>(lds);
+    __syncthreads();   // the stage buffers are free
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wave_m * WM + i * 32 + (lane & 31);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+          const int slot = (col >> 2) ^ (row & 15);
+          quads[row * QPR + slot] =
+              make_uint2(f32_to_bf16_bits(acc[i][j][4 * q]) | (f32_to_bf16_bits(acc[i][j][4 * q + 1]) << 16),
+                         f32_to_bf16_bits(acc[i][j][4 * q + 2]) | (f32_to_bf16_bits(acc[i][j][4 * q + 3]) << 16));
+        }
+      }
+    }
+    __syncthreads();
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    const bool vec = (g.ldc & 7) == 0;
+    const int c = threadIdx.x & 31;                 // 16-byte chunk of the row
+    const int64_t n = n0 + 8 * c;
+#pragma unroll 4
+    for (int row = threadIdx.x >> 5; row < BM; row += NT / 32) {
+      const int f = row & 15;
+      uint4 v = lds[row * CPR16 + (c ^ (f >> 1))];
+      if (f & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      const int64_t m = m0 + row;
+      if (m < g.M && n < g.N) {
+        uint16_t* dst = C + m * g.ldc + n;
+        if (vec && n + 8 <= g.N) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          for (int e = 0; e < 8; ++e)
+            if (n + e < g.N) dst[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+      if constexpr (STATS) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        float z[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          z[e] = n + e < g.N ? __uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16) : -INFINITY;
+        // The row's maximum first (exact), then one exponential per element
+        // against it; a tile row always holds at least one valid column.
+        float mx = z[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, z[e]);
+        mx = half_wave_max(mx);
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d += __builtin_amdgcn_exp2f((z[e] - mx) * g.stat_k);
+        d = half_wave_sum(d);
+        if (c == 0 && m < g.M) g.stat_part[m * g.stat_ld + tn] = make_float2(mx, d);
+      }
+    }
+  }
+
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
@@ -622,7 +724,10 @@ struct GemmKernel {
       mainloop_checked(g, lds, m0, n0, kb, ke, 0, nk, acc);
     }
 
-    if constexpr (EPI == kEpiAccumulate) {
+    if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats) {
+      epilogue_staged<EPI == kEpiStoreStats>(g, m0, n0, tn, lane, wave_m, wave_n, acc, &lds[0][0]);
+      return;
+    } else if constexpr (EPI == kEpiAccumulate) {
       epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
       return;
     } else if constexpr (EPI == kEpiAccumulateF32) {
@@ -720,6 +825,10 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
     case kEpiStore: return launch_cfg<A_K, B_K, kEpiStore>(g, s);
     case kEpiAccumulate: return launch_cfg<A_K, B_K, kEpiAccumulate>(g, s);
     case kEpiPartialF32: return launch_cfg<A_K, B_K, kEpiPartialF32>(g, s);
+    case kEpiStoreStats:
+      // Only the logits product reduces row statistics.
+      if constexpr (A_K && B_K) return launch_cfg<A_K, B_K, kEpiStoreStats>(g, s);
+      return hipErrorInvalidValue;
     case kEpiAccumulateF32:
       // Only the weight-gradient product accumulates into an fp32 C.
       if constexpr (A_K && B_K) return launch_cfg<A_K, B_K, kEpiAccumulateF32>(g, s);

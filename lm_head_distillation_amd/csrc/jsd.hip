@@ -224,6 +224,31 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   }
 }
 
+// Pass 1 from the logits GEMMs' per-N-tile partials: one wave per row merges
+// the student's and the teacher's partials in tile order into the row's
+// statistics, stored as slice 0 of the stats array (the other slices get the
+// merge identity, so the loss passes read the layout they always read).
+__global__ __launch_bounds__(256) void jsd_stats_merge_kernel(JsdArgs a, const float2* part_s,
+                                                              const float2* part_t,
+                                                              int64_t tiles) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= a.rows) return;
+  const float k = a.k2;
+  float ms = -INFINITY, ds = 0.f, mt = -INFINITY, dt = 0.f;
+  for (int64_t j = lane; j < tiles; j += 64) {
+    const float2 ps = part_s[row * tiles + j];
+    const float2 pt = part_t[row * tiles + j];
+    md_merge(ms, ds, ps.x, ps.y, k);
+    md_merge(mt, dt, pt.x, pt.y, k);
+  }
+  wave_md(ms, ds, k);
+  wave_md(mt, dt, k);
+  for (int s = lane; s < a.S; s += 64)
+    a.stats[row * a.S + s] = s == 0 ? make_float4(ms, ds, mt, dt)
+                                    : make_float4(-INFINITY, 0.f, -INFINITY, 0.f);
+}
+
 __global__ __launch_bounds__(64) void jsd_row_loss_kernel(JsdArgs a) {
   const int64_t row = blockIdx.x;
   if (threadIdx.x == 0) {
@@ -326,6 +351,13 @@ hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s) {
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>(a.S));
   return dtype == 1 ? launch_grad_t<uint16_t>(a, s, grid) : launch_grad_t<float>(a, s, grid);
+}
+
+hipError_t launch_jsd_stats_merge(const JsdArgs& a, const float2* part_s, const float2* part_t,
+                                  int64_t tiles, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
+  hipLaunchKernelGGL(jsd_stats_merge_kernel, grid, dim3(256), 0, s, a, part_s, part_t, tiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_jsd_row_loss(const JsdArgs& a, hipStream_t s) {

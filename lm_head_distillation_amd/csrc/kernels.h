@@ -82,6 +82,10 @@ hipError_t launch_loss_reduce_dev(const float* row_loss, int64_t n, const float*
 hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s);
+// Pass 1 from the logits GEMMs' row-statistic partials [rows, tiles] (student,
+// teacher): writes the row statistics the loss passes read.
+hipError_t launch_jsd_stats_merge(const JsdArgs& a, const float2* part_s, const float2* part_t,
+                                  int64_t tiles, hipStream_t s);
 // Per-row loss only (no gradient written): merges the pass-2 partials.
 hipError_t launch_jsd_row_loss(const JsdArgs& a, hipStream_t s);
 // loss[0] = scale * sum(row_loss[0..n)), deterministic order.
@@ -99,6 +103,8 @@ enum GemmEpilogue : int {
   kEpiPartialF32 = 2,   // fp32 partial sum of one K-split at C + split * M * ldc
                         // (with one split: C = A B stored in fp32)
   kEpiAccumulateF32 = 3,  // fp32 C = C + A B, no rounding (bf16 operands)
+  kEpiStoreStats = 4,     // kEpiStore, plus each row's (max, sum 2^((z-max) k)) over
+                          // the tile's columns of the rounded values, per N-tile
 };
 
 struct GemmArgs {
@@ -115,6 +121,11 @@ struct GemmArgs {
   int group_m = 0;         // M-tiles per tile group in the launch order (0: all)
   bool wgrad = false;      // the weight-gradient product (its own kernel symbol, so
                            // profiles tell it from the logits product)
+  // kEpiStoreStats: partial row statistics [M, stat_ld] float2 (max in logit
+  // units, denominator in base 2 with scale stat_k), one per N-tile.
+  float2* stat_part = nullptr;
+  int64_t stat_ld = 0;
+  float stat_k = 0.f;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);

@@ -75,6 +75,10 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H_s * 4);
   p.off_xt = off;
   if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H_s * p.ldt * es));
+  p.gemm_stats = dtype == 1;
+  p.stat_tiles = cdiv(V, kGemmBN);
+  p.off_spart = off;
+  if (p.gemm_stats) off = align256(off + static_cast<size_t>(2 * p.C * p.stat_tiles) * 8);
   p.total = off;
   return p;
 }

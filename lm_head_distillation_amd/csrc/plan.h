@@ -54,12 +54,17 @@ struct ChunkPlan {
   // region, so grad_W = dZ^T X_s reads both operands with K (rows) fastest.
   bool transposed_grad_w = false;
   int64_t ldt = 0;        // row stride of the transposed operands: C rounded up to 8
+  // bf16: the logits GEMMs reduce each row's statistics per N-tile into
+  // [C, stat_tiles] float2 partials (student, then teacher), replacing pass 1's
+  // read of both logits rows.
+  bool gemm_stats = false;
+  int64_t stat_tiles = 0;
   SlicePlan slices;       // for C rows
   int splitk = 1;         // split-K factor of grad_input = dZ W_s
   int64_t k_per_split = 0;
   // Workspace layout, byte offsets from the workspace base.
   size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0,
-         off_partial = 0, off_xt = 0, total = 0;
+         off_partial = 0, off_xt = 0, off_spart = 0, total = 0;
 };
 
 // Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).
