@@ -100,8 +100,10 @@ typedef enum fljsd_reduction {
  *   fljsd_workspace_size(BT, H_s, H_t, V, dtype, num_chunks) bytes (for
  *   num_chunks == 0, at least the size for one chunk's worth of rows that
  *   fits). It holds both logits chunks (the student chunk becomes dZ in
- *   place, PR #1352 Details), per-row loss, row statistics and split-K
- *   partial sums. Its contents on entry do not matter.
+ *   place, PR #1352 Details), per-row loss, row statistics (for bf16, per-tile
+ *   partials written by the logits products), split-K partial sums, and for
+ *   bf16 the transposed dZ and X_s chunk the weight-gradient product reads.
+ *   Its contents on entry do not matter.
  * Errors: FLJSD_EINVAL, FLJSD_EDTYPE, FLJSD_EALIGN, FLJSD_EWORKSPACE (all
  *   before any work is enqueued), FLJSD_EDEVICE, FLJSD_EHIP.
  */

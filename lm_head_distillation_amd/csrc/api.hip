@@ -159,7 +159,7 @@ int check_common(int dtype, float beta, float temperature, int reduction) {
 // read of both rows.
 int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int es,
                    hipStream_t s, const float2* part_s = nullptr, const float2* part_t = nullptr,
-                   int64_t tiles = 0) {
+                   int64_t tiles = 0, void* dzt = nullptr, int64_t ldt = 0) {
   const double row_bytes = static_cast<double>(ja.rows) * V * es;
   hipError_t e;
   if (part_s) {
@@ -173,7 +173,11 @@ int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int
   e = timed(s, FLJSD_KCLASS_JSD_LOSS, 0.0, 2 * row_bytes,
             [&] { return launch_jsd_loss(ja, dtype, s); });
   if (e != hipSuccess) return fail_hip(e, "launch jsd_loss");
-  if (write_grad) {
+  if (write_grad && dzt) {
+    e = timed(s, FLJSD_KCLASS_JSD_GRAD, 0.0, 4 * row_bytes,
+              [&] { return launch_jsd_grad_transposed(ja, dzt, ldt, s); });
+    if (e != hipSuccess) return fail_hip(e, "launch jsd_grad");
+  } else if (write_grad) {
     e = timed(s, FLJSD_KCLASS_JSD_GRAD, 0.0, 3 * row_bytes,
               [&] { return launch_jsd_grad(ja, dtype, s); });
     if (e != hipSuccess) return fail_hip(e, "launch jsd_grad");
@@ -265,14 +269,16 @@ int run_grad_input(int dtype, const void* dZ, int64_t ldz, const void* W, int64_
 // both operands are K-contiguous for the direct-copy matrix-core path.
 int run_grad_weight(int dtype, const void* dZ, int64_t ldz, const void* X, int64_t rows,
                     int64_t H, int64_t V, void* gW, bool transposed, void* dzt, void* xt,
-                    int64_t ldt, int epilogue, hipStream_t s) {
+                    int64_t ldt, int epilogue, hipStream_t s, bool dz_transposed = false) {
   const int es = dtype_size(dtype);
   GemmArgs g;
   if (transposed) {
-    const double tbytes = 2.0 * static_cast<double>(rows) * (V + H) * es;
+    const double tbytes = 2.0 * static_cast<double>(rows) * ((dz_transposed ? 0 : V) + H) * es;
     hipError_t e = timed(s, FLJSD_KCLASS_TRANSPOSE, 0.0, tbytes, [&] {
-      hipError_t t = launch_transpose_bf16(dZ, rows, V, ldz, dzt, ldt, s);
-      if (t != hipSuccess) return t;
+      if (!dz_transposed) {
+        hipError_t t = launch_transpose_bf16(dZ, rows, V, ldz, dzt, ldt, s);
+        if (t != hipSuccess) return t;
+      }
       return launch_transpose_bf16(X, rows, H, H, xt, ldt, s);
     });
     if (e != hipSuccess) return fail_hip(e, "launch transpose");
@@ -479,7 +485,10 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
 
     ja.rows = rows;
     ja.row_loss = row_loss + r0;
-    rc = run_jsd_passes(ja, dtype, write_grad, V, es, s, part_s, part_t, plan.stat_tiles);
+    // With a weight gradient on the transposed path, pass 3 also writes dZ^T.
+    void* dzt = (grad_W_s && plan.transposed_grad_w) ? ws + plan.off_dzt : nullptr;
+    rc = run_jsd_passes(ja, dtype, write_grad, V, es, s, part_s, part_t, plan.stat_tiles, dzt,
+                        plan.ldt);
     if (rc != FLJSD_OK) return rc;
 
     if (grad_X_s) {
@@ -498,8 +507,8 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
       const int epi = gw_f32_acc ? (add ? kEpiAccumulateF32 : kEpiPartialF32)
                                  : (add ? kEpiAccumulate : kEpiStore);
       rc = run_grad_weight(dtype, Zs, plan.ldz, Xs + r0 * H_s * es, rows, H_s, V, grad_W_s,
-                           plan.transposed_grad_w, ws + plan.off_zt, ws + plan.off_xt, plan.ldt,
-                           epi, s);
+                           plan.transposed_grad_w, ws + plan.off_dzt, ws + plan.off_xt, plan.ldt,
+                           epi, s, /*dz_transposed=*/true);
       if (rc != FLJSD_OK) return rc;
     }
   }

@@ -320,6 +320,119 @@ hipError_t launch_loss_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
+// Pass 3 over 64-row x 64-column tiles, bf16: dZ written in place as by
+// jsd_grad_kernel, and the same tile, transposed through LDS, to
+// dzt [V, ldt] for the weight-gradient product. A workgroup covers 64 rows and
+// kTileCols columns; threads 0..63 first merge their row's statistics and
+// pass-2 partials. In the LDS tile, 16-byte chunk c of row r sits at
+// c ^ ((r / 8) % 8), so both the row-wise writes and the column-wise reads
+// are free of bank conflicts.
+constexpr int kTileCols = 1024;
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_t* dzt,
+                                                             int64_t ldt) {
+  __shared__ float4 sh_L[64];
+  __shared__ float sh_G[64];
+  __shared__ uint4 tile[64][8];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * kTileCols;
+  const int64_t c_end = min(a.V, c_begin + kTileCols);
+  const int t = threadIdx.x;
+  if (t < 64) {
+    const int64_t row = r0 + t;
+    float4 L = make_float4(0.f, 0.f, 0.f, 0.f);
+    float G = 0.f;
+    if (row < a.rows) {
+      const float4* st = a.stats + row * a.S;
+      float4 acc = st[0];
+      for (int s = 1; s < a.S; ++s) {
+        md_merge(acc.x, acc.y, st[s].x, st[s].y, a.k2);
+        md_merge(acc.z, acc.w, st[s].z, st[s].w, a.k2);
+      }
+      L = make_float4(acc.x, hw_log2(acc.y), acc.z, hw_log2(acc.w));
+      const float2* lg = a.lg + row * a.S;
+      float2 sum = lg[0];
+      for (int j = 1; j < a.S; ++j) {
+        sum.x += lg[j].x;
+        sum.y += lg[j].y;
+      }
+      G = sum.y;
+      if (blockIdx.x == 0) a.row_loss[row] = sum.x * a.row_scale;
+    }
+    sh_L[t] = L;
+    sh_G[t] = G;
+  }
+  __syncthreads();
+  const uint16_t* zs = static_cast<const uint16_t*>(a.zs);
+  const uint16_t* zt = static_cast<const uint16_t*>(a.zt);
+  uint16_t* gr = static_cast<uint16_t*>(a.grad);
+  const float k = a.k2;
+  for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
+    // Row-major: thread -> (row, 8-column chunk), two passes of 32 rows.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = t / 8 + 32 * h;
+      const int chunk = t % 8;
+      const int64_t row = r0 + rl;
+      const int64_t v = c0 + chunk * 8;
+      uint4 packed = make_uint4(0, 0, 0, 0);
+      if (row < a.rows && v < a.V) {
+        const int n = static_cast<int>(min<int64_t>(8, a.V - v));
+        const float4 L = sh_L[rl];
+        const float G = sh_G[rl];
+        float ys[8], yt[8], out[8];
+        load8(zs + row * a.ld, v, n, a.vec_ok, ys);
+        load8(zt + row * a.ld, v, n, a.vec_ok, yt);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float Q, P, l, g, gacc;
+          jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
+                          gacc);
+          const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+          out[i] = dA * a.grad_scale;
+        }
+        store8(gr + row * a.ld, v, n, a.vec_ok, out);
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = i < n ? f32_to_bf16_bits(out[i]) : 0u;
+        packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                            b[6] | (b[7] << 16));
+      }
+      tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
+    }
+    __syncthreads();
+    // Transposed: thread -> (column, eight consecutive rows); a wave writes
+    // 8 rows of dzt, 128 contiguous bytes each.
+    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[0][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cl = t / 8 + 32 * h;
+      const int j = t % 8;
+      const int64_t v = c0 + cl;
+      const int64_t r = r0 + 8 * j;
+      if (v < a.V && r < a.rows) {
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int rl = 8 * j + i;
+          e[i] = t16[rl * 64 + ((cl >> 3) ^ ((rl >> 3) & 7)) * 8 + (cl & 7)];
+        }
+        uint16_t* q = dzt + v * ldt + r;
+        if (r + 8 <= a.rows) {
+          *reinterpret_cast<uint4*>(q) =
+              make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                         e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+        } else {
+          for (int i = 0; i < 8; ++i)
+            if (r + i < a.rows) q[i] = e[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T>
 hipError_t launch_grad_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
   const dim3 block(kThreads);
@@ -351,6 +464,19 @@ hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s) {
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>(a.S));
   return dtype == 1 ? launch_grad_t<uint16_t>(a, s, grid) : launch_grad_t<float>(a, s, grid);
+}
+
+hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.V + kTileCols - 1) / kTileCols),
+                  static_cast<unsigned>((a.rows + 63) / 64));
+  uint16_t* d = static_cast<uint16_t*>(dzt);
+  if (a.mode == kModeForwardKL)
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeForwardKL>, grid, dim3(kThreads), 0, s, a, d, ldt);
+  else if (a.mode == kModeReverseKL)
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeReverseKL>, grid, dim3(kThreads), 0, s, a, d, ldt);
+  else
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeGeneralized>, grid, dim3(kThreads), 0, s, a, d, ldt);
+  return hipGetLastError();
 }
 
 hipError_t launch_jsd_stats_merge(const JsdArgs& a, const float2* part_s, const float2* part_t,

@@ -82,6 +82,8 @@ hipError_t launch_loss_reduce_dev(const float* row_loss, int64_t n, const float*
 hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s);
+// Pass 3 for bf16 that also writes dZ^T [V, ldt] (the weight-gradient operand).
+hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, hipStream_t s);
 // Pass 1 from the logits GEMMs' row-statistic partials [rows, tiles] (student,
 // teacher): writes the row statistics the loss passes read.
 hipError_t launch_jsd_stats_merge(const JsdArgs& a, const float2* part_s, const float2* part_t,

@@ -59,7 +59,7 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   }
   p.transposed_grad_w = dtype == 1;
   p.ldt = round_up(p.C, kJsdVec);
-  const int64_t zt_elems = p.transposed_grad_w ? std::max(p.C * p.ldz, V * p.ldt) : p.C * p.ldz;
+  const int64_t zt_elems = p.C * p.ldz;
   size_t off = 0;
   p.off_zs = off;
   off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
@@ -75,6 +75,8 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H_s * 4);
   p.off_xt = off;
   if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H_s * p.ldt * es));
+  p.off_dzt = off;
+  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(V * p.ldt * es));
   p.gemm_stats = dtype == 1;
   p.stat_tiles = cdiv(V, kGemmBN);
   p.off_spart = off;
