@@ -687,6 +687,92 @@ struct GemmKernel {
     }
   }
 
+  // C = C + A B for bf16 C, staged through LDS: the fp32 products of one
+  // 128-row half of the tile at a time go to LDS (a lane's four consecutive
+  // columns as one 16-byte write, chunk c of row r at c ^ (r % 32)), then each
+  // 32-lane half-wave takes whole rows: it loads the old values with 16-byte
+  // reads (all of its rows' loads issued first), adds the fp32 products from
+  // LDS, rounds once and stores 16 bytes per lane.
+  static __device__ inline void epilogue_accumulate_staged(const GemmArgs& g, int64_t m0,
+                                                           int64_t n0, int lane, int wave_m,
+                                                           int wave_n,
+                                                           floatx16 (&acc)[TM][TN], uint4* lds) {
+    static_assert(WAVES_M == 2 && BM == 256 && BN == 256, "two 128-row halves of 1 KB rows");
+    constexpr int HALF = BM / 2;
+    constexpr int C16 = BN / 4;                  // fp32 16-byte chunks per row
+    constexpr int ROWS_PER_PASS = NT / 32;       // rows in flight per pass (one per half-wave)
+    constexpr int PASSES = HALF / ROWS_PER_PASS;
+    uint16_t* C = static_cast<uint16_t*>(g.C);
+    const bool vec = (g.ldc & 7) == 0;
+    const int c8 = threadIdx.x & 31;             // 8-column group of the row
+    const int64_t n = n0 + 8 * c8;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // Old values of this half's rows, loaded before the staging barrier.
+      uint4 old[PASSES];
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int64_t m = m0 + h * HALF + p * ROWS_PER_PASS + (threadIdx.x >> 5);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (m < g.M && n < g.N) {
+          const uint16_t* src = C + m * g.ldc + n;
+          if (vec && n + 8 <= g.N) {
+            v = *reinterpret_cast<const uint4*>(src);
+          } else {
+            uint16_t e[8];
+            for (int k = 0; k < 8; ++k) e[k] = n + k < g.N ? src[k] : uint16_t(0);
+            v = make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                           e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+          }
+        }
+        old[p] = v;
+      }
+      __syncthreads();   // the stage buffers (or the previous half) are free
+      if (wave_m == h) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int row = i * 32 + (lane & 31);  // within the half
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int chunk = (wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+              lds[row * C16 + (chunk ^ (row & 31))] =
+                  make_uint4(__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                             __float_as_uint(acc[i][j][4 * q + 2]),
+                             __float_as_uint(acc[i][j][4 * q + 3]));
+            }
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < PASSES; ++p) {
+        const int row = p * ROWS_PER_PASS + (threadIdx.x >> 5);
+        const int64_t m = m0 + h * HALF + row;
+        const uint4 a0 = lds[row * C16 + ((2 * c8) ^ (row & 31))];
+        const uint4 a1 = lds[row * C16 + ((2 * c8 + 1) ^ (row & 31))];
+        if (m >= g.M || n >= g.N) continue;
+        const float add[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z),
+                              __uint_as_float(a0.w), __uint_as_float(a1.x), __uint_as_float(a1.y),
+                              __uint_as_float(a1.z), __uint_as_float(a1.w)};
+        const uint32_t w[4] = {old[p].x, old[p].y, old[p].z, old[p].w};
+        uint32_t out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          out[e] = f32_to_bf16_bits(__uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16) + add[e]);
+        uint16_t* dst = C + m * g.ldc + n;
+        if (vec && n + 8 <= g.N) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
+                                                      out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+        } else {
+          for (int e = 0; e < 8; ++e)
+            if (n + e < g.N) dst[e] = static_cast<uint16_t>(out[e]);
+        }
+      }
+    }
+  }
+
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
@@ -728,7 +814,10 @@ struct GemmKernel {
       epilogue_staged<EPI == kEpiStoreStats>(g, m0, n0, tn, lane, wave_m, wave_n, acc, &lds[0][0]);
       return;
     } else if constexpr (EPI == kEpiAccumulate) {
-      epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
+      if constexpr (WAVES_M == 2 && BM == 256 && BN == 256)
+        epilogue_accumulate_staged(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
+      else
+        epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
       return;
     } else if constexpr (EPI == kEpiAccumulateF32) {
       epilogue_accumulate<float>(g, m0, n0, lane, wave_m, wave_n, acc);
