@@ -323,21 +323,23 @@ hipError_t launch_loss_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
 // Pass 3 over 64-row x 64-column tiles, bf16: dZ written in place as by
 // jsd_grad_kernel, and the same tile, transposed through LDS, to
 // dzt [V, ldt] for the weight-gradient product. A workgroup covers 64 rows and
-// kTileCols columns; threads 0..63 first merge their row's statistics and
-// pass-2 partials. In the LDS tile, 16-byte chunk c of row r sits at
-// c ^ ((r / 8) % 8), so both the row-wise writes and the column-wise reads
-// are free of bank conflicts.
-constexpr int kTileCols = 1024;
+// `span` columns (a multiple of 64, smaller when there are few rows so the
+// launch still fills the chip); threads 0..63 first merge their row's
+// statistics and pass-2 partials. In the LDS tile, 16-byte chunk c of row r
+// sits at c ^ ((r / 8) % 8), so both the row-wise writes and the column-wise
+// reads are free of bank conflicts.
+constexpr int64_t kTileColsMax = 1024;
+constexpr int64_t kGradTargetBlocks = 2048;
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_t* dzt,
-                                                             int64_t ldt) {
+                                                             int64_t ldt, int64_t span) {
   __shared__ float4 sh_L[64];
   __shared__ float sh_G[64];
   __shared__ uint4 tile[64][8];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
-  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * kTileCols;
-  const int64_t c_end = min(a.V, c_begin + kTileCols);
+  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * span;
+  const int64_t c_end = min(a.V, c_begin + span);
   const int t = threadIdx.x;
   if (t < 64) {
     const int64_t row = r0 + t;
@@ -467,15 +469,21 @@ hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.V + kTileCols - 1) / kTileCols),
-                  static_cast<unsigned>((a.rows + 63) / 64));
+  const int64_t row_blocks = (a.rows + 63) / 64;
+  const int64_t tiles = (a.V + 63) / 64;   // 64-column tiles per row block
+  // Columns per workgroup: as many 64-column tiles as keep kGradTargetBlocks
+  // workgroups in the launch, at most kTileColsMax.
+  int64_t per = (tiles * row_blocks + kGradTargetBlocks - 1) / kGradTargetBlocks;
+  per = std::max<int64_t>(1, std::min<int64_t>(per, kTileColsMax / 64));
+  const int64_t span = per * 64;
+  const dim3 grid(static_cast<unsigned>((a.V + span - 1) / span), static_cast<unsigned>(row_blocks));
   uint16_t* d = static_cast<uint16_t*>(dzt);
   if (a.mode == kModeForwardKL)
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeForwardKL>, grid, dim3(kThreads), 0, s, a, d, ldt);
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeForwardKL>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
   else if (a.mode == kModeReverseKL)
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeReverseKL>, grid, dim3(kThreads), 0, s, a, d, ldt);
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeReverseKL>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
   else
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeGeneralized>, grid, dim3(kThreads), 0, s, a, d, ldt);
+    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeGeneralized>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
   return hipGetLastError();
 }
 
