@@ -884,28 +884,41 @@ struct Pipe {
   static constexpr int STAGES = 2;
 };
 
-template <bool A_K, bool B_K, int EPI>
-hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
-  const int64_t tiles_m = (g.M + kGemmBM - 1) / kGemmBM;
+// Output tile (BM x 256) and wave grid (WM_ x WN_ waves) for one launch.
+template <int BM, int WM_, int WN_, bool A_K, bool B_K, int EPI>
+hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles_m = (g.M + BM - 1) / BM;
   const int64_t tiles_n = (g.N + kGemmBN - 1) / kGemmBN;
   const dim3 grid(static_cast<unsigned>(tiles_m * tiles_n), static_cast<unsigned>(g.splitk));
-  const dim3 block(kWavesM * kWavesN * 64);
+  const dim3 block(WM_ * WN_ * 64);
   const int group_m = g.group_m > 0 ? static_cast<int>(std::min<int64_t>(g.group_m, tiles_m))
                                     : static_cast<int>(tiles_m);
   constexpr int BK = Pipe<A_K, B_K>::BK, ST = Pipe<A_K, B_K>::STAGES;
   if constexpr (A_K && B_K) {
     if (g.wgrad) {
-      hipLaunchKernelGGL((gemm_bf16_wgrad_kernel<kGemmBM, kGemmBN, BK, ST, kWavesM, kWavesN, A_K,
-                                                 B_K, EPI>),
+      hipLaunchKernelGGL((gemm_bf16_wgrad_kernel<BM, kGemmBN, BK, ST, WM_, WN_, A_K, B_K, EPI>),
                          grid, block, 0, s, g, static_cast<int>(tiles_m),
                          static_cast<int>(tiles_n), group_m);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<kGemmBM, kGemmBN, BK, ST, kWavesM, kWavesN, A_K, B_K, EPI>),
-                     grid, block, 0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
-                     group_m);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, kGemmBN, BK, ST, WM_, WN_, A_K, B_K, EPI>), grid, block,
+                     0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n), group_m);
   return hipGetLastError();
+}
+
+// Products with few rows (the logits and grad_input of small chunks) take
+// 64-row tiles, one row of eight 64 x 32 wave tiles: a 256-row tile would
+// spend most of its matrix-core work on rows that do not exist, and the
+// smaller tile lets two workgroups share a CU.
+constexpr int64_t kSkinnyMaxM = 128;
+
+template <bool A_K, bool B_K, int EPI>
+hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
+  if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats || EPI == kEpiPartialF32) {
+    if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
+  }
+  return launch_tiles<kGemmBM, kWavesM, kWavesN, A_K, B_K, EPI>(g, s);
 }
 
 template <bool A_K, bool B_K>
