@@ -688,17 +688,18 @@ struct GemmKernel {
   }
 
   // C = C + A B for bf16 C, staged through LDS: the fp32 products of one
-  // 128-row half of the tile at a time go to LDS (a lane's four consecutive
-  // columns as one 16-byte write, chunk c of row r at c ^ (r % 32)), then each
-  // 32-lane half-wave takes whole rows: it loads the old values with 16-byte
-  // reads (all of its rows' loads issued first), adds the fp32 products from
-  // LDS, rounds once and stores 16 bytes per lane.
+  // wave row (WM rows of the tile) at a time go to LDS (a lane's four
+  // consecutive columns as one 16-byte write, chunk c of row r at
+  // c ^ (r % 32)), then each 32-lane half-wave takes whole rows: it loads the
+  // old values with 16-byte reads (all of its rows' loads issued first), adds
+  // the fp32 products from LDS, rounds once and stores 16 bytes per lane.
   static __device__ inline void epilogue_accumulate_staged(const GemmArgs& g, int64_t m0,
                                                            int64_t n0, int lane, int wave_m,
                                                            int wave_n,
                                                            floatx16 (&acc)[TM][TN], uint4* lds) {
-    static_assert(WAVES_M == 2 && BM == 256 && BN == 256, "two 128-row halves of 1 KB rows");
-    constexpr int HALF = BM / 2;
+    static_assert(BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16,
+                  "one wave row of 1 KB fp32 rows fits in LDS");
+    constexpr int HALF = WM;
     constexpr int C16 = BN / 4;                  // fp32 16-byte chunks per row
     constexpr int ROWS_PER_PASS = NT / 32;       // rows in flight per pass (one per half-wave)
     constexpr int PASSES = HALF / ROWS_PER_PASS;
@@ -707,8 +708,8 @@ struct GemmKernel {
     const int c8 = threadIdx.x & 31;             // 8-column group of the row
     const int64_t n = n0 + 8 * c8;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // Old values of this half's rows, loaded before the staging barrier.
+    for (int h = 0; h < WAVES_M; ++h) {
+      // Old values of this part's rows, loaded before the staging barrier.
       uint4 old[PASSES];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
@@ -814,7 +815,8 @@ struct GemmKernel {
       epilogue_staged<EPI == kEpiStoreStats>(g, m0, n0, tn, lane, wave_m, wave_n, acc, &lds[0][0]);
       return;
     } else if constexpr (EPI == kEpiAccumulate) {
-      if constexpr (WAVES_M == 2 && BM == 256 && BN == 256)
+      if constexpr (BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 &&
+                    WM % (NT / 32) == 0)
         epilogue_accumulate_staged(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
       else
         epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
@@ -913,10 +915,18 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 // smaller tile lets two workgroups share a CU.
 constexpr int64_t kSkinnyMaxM = 128;
 
+// The weight-gradient product of a small chunk (reduction over at most
+// kSkinnyMaxK rows) is bound by each tile's serial load / multiply /
+// read-add-write phases; 64-row tiles let two workgroups per CU overlap them.
+constexpr int64_t kSkinnyMaxK = 256;
+
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats || EPI == kEpiPartialF32) {
     if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
+  }
+  if constexpr (A_K && B_K && (EPI == kEpiStore || EPI == kEpiAccumulate)) {
+    if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
   }
   return launch_tiles<kGemmBM, kWavesM, kWavesN, A_K, B_K, EPI>(g, s);
 }
