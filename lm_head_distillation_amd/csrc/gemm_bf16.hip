@@ -915,17 +915,19 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 // smaller tile lets two workgroups share a CU.
 constexpr int64_t kSkinnyMaxM = 128;
 
-// The weight-gradient product of a small chunk (reduction over at most
-// kSkinnyMaxK rows) is bound by each tile's serial load / multiply /
-// read-add-write phases; 64-row tiles let two workgroups per CU overlap them.
-constexpr int64_t kSkinnyMaxK = 256;
+// The accumulating weight-gradient product of a chunk of at most kSkinnyMaxK
+// rows is bound by each tile's serial load / multiply / read-add-write
+// phases; 64-row tiles let two workgroups per CU overlap them (measured on
+// 128256 x 4096 bf16: 0.73 -> 0.46 ms at 32 rows, 1.82 -> 1.69 ms at 1024).
+// The storing first chunk keeps the 256-row tile, faster from 256 rows up.
+constexpr int64_t kSkinnyMaxK = 1024;
 
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats || EPI == kEpiPartialF32) {
     if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
   }
-  if constexpr (A_K && B_K && (EPI == kEpiStore || EPI == kEpiAccumulate)) {
+  if constexpr (A_K && B_K && EPI == kEpiAccumulate) {
     if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
   }
   return launch_tiles<kGemmBM, kWavesM, kWavesN, A_K, B_K, EPI>(g, s);
