@@ -693,46 +693,57 @@ struct GemmKernel {
   // c ^ (r % 32)), then each 32-lane half-wave takes whole rows: it loads the
   // old values with 16-byte reads (all of its rows' loads issued first), adds
   // the fp32 products from LDS, rounds once and stores 16 bytes per lane.
+  template <class Out>
   static __device__ inline void epilogue_accumulate_staged(const GemmArgs& g, int64_t m0,
                                                            int64_t n0, int lane, int wave_m,
                                                            int wave_n,
                                                            floatx16 (&acc)[TM][TN], uint4* lds) {
     static_assert(BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16,
                   "one wave row of 1 KB fp32 rows fits in LDS");
+    constexpr bool F32 = sizeof(Out) == 4;
+    constexpr int V16 = F32 ? 2 : 1;             // 16-byte vectors of old values per lane and row
     constexpr int HALF = WM;
     constexpr int C16 = BN / 4;                  // fp32 16-byte chunks per row
     constexpr int ROWS_PER_PASS = NT / 32;       // rows in flight per pass (one per half-wave)
     constexpr int PASSES = HALF / ROWS_PER_PASS;
-    uint16_t* C = static_cast<uint16_t*>(g.C);
-    const bool vec = (g.ldc & 7) == 0;
+    Out* C = static_cast<Out*>(g.C);
+    const bool vec = (g.ldc & (F32 ? 3 : 7)) == 0;
     const int c8 = threadIdx.x & 31;             // 8-column group of the row
     const int64_t n = n0 + 8 * c8;
 #pragma unroll
     for (int h = 0; h < WAVES_M; ++h) {
       // Old values of this part's rows, loaded before the staging barrier.
-      uint4 old[PASSES];
+      uint4 old[PASSES][V16];
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int64_t m = m0 + h * HALF + p * ROWS_PER_PASS + (threadIdx.x >> 5);
-        uint4 v = make_uint4(0, 0, 0, 0);
+        uint32_t w[4 * V16];
+#pragma unroll
+        for (int k = 0; k < 4 * V16; ++k) w[k] = 0;
         if (m < g.M && n < g.N) {
-          const uint16_t* src = C + m * g.ldc + n;
+          const Out* src = C + m * g.ldc + n;
           if (vec && n + 8 <= g.N) {
-            v = *reinterpret_cast<const uint4*>(src);
+#pragma unroll
+            for (int q = 0; q < V16; ++q) {
+              const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+              w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+            }
           } else {
-            uint16_t e[8];
-            for (int k = 0; k < 8; ++k) e[k] = n + k < g.N ? src[k] : uint16_t(0);
-            v = make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                           e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+            for (int k = 0; k < 8; ++k) {
+              if (n + k >= g.N) continue;
+              if constexpr (F32) w[k] = __float_as_uint(src[k]);
+              else w[k >> 1] |= static_cast<uint32_t>(src[k]) << (16 * (k & 1));
+            }
           }
         }
-        old[p] = v;
+#pragma unroll
+        for (int q = 0; q < V16; ++q) old[p][q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
       }
-      __syncthreads();   // the stage buffers (or the previous half) are free
+      __syncthreads();   // the stage buffers (or the previous part) are free
       if (wave_m == h) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-          const int row = i * 32 + (lane & 31);  // within the half
+          const int row = i * 32 + (lane & 31);  // within the part
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -757,22 +768,40 @@ struct GemmKernel {
         const float add[8] = {__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z),
                               __uint_as_float(a0.w), __uint_as_float(a1.x), __uint_as_float(a1.y),
                               __uint_as_float(a1.z), __uint_as_float(a1.w)};
-        const uint32_t w[4] = {old[p].x, old[p].y, old[p].z, old[p].w};
-        uint32_t out[8];
+        Out* dst = C + m * g.ldc + n;
+        if constexpr (F32) {
+          const uint32_t w[8] = {old[p][0].x, old[p][0].y, old[p][0].z, old[p][0].w,
+                                 old[p][1].x, old[p][1].y, old[p][1].z, old[p][1].w};
+          float out[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          out[e] = f32_to_bf16_bits(__uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16) + add[e]);
-        uint16_t* dst = C + m * g.ldc + n;
-        if (vec && n + 8 <= g.N) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
-                                                      out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+          for (int e = 0; e < 8; ++e) out[e] = __uint_as_float(w[e]) + add[e];
+          if (vec && n + 8 <= g.N) {
+            reinterpret_cast<float4*>(dst)[0] = make_float4(out[0], out[1], out[2], out[3]);
+            reinterpret_cast<float4*>(dst)[1] = make_float4(out[4], out[5], out[6], out[7]);
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (n + e < g.N) dst[e] = out[e];
+          }
         } else {
+          const uint32_t w[4] = {old[p][0].x, old[p][0].y, old[p][0].z, old[p][0].w};
+          uint32_t out[8];
+#pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (n + e < g.N) dst[e] = static_cast<uint16_t>(out[e]);
+            out[e] = f32_to_bf16_bits(__uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16) + add[e]);
+          if (vec && n + 8 <= g.N) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
+                                                        out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+          } else {
+            for (int e = 0; e < 8; ++e)
+              if (n + e < g.N) dst[e] = static_cast<uint16_t>(out[e]);
+          }
         }
       }
     }
   }
+
+  static constexpr bool kStagedAccumulate =
+      BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 && WM % (NT / 32) == 0;
 
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
@@ -815,14 +844,16 @@ struct GemmKernel {
       epilogue_staged<EPI == kEpiStoreStats>(g, m0, n0, tn, lane, wave_m, wave_n, acc, &lds[0][0]);
       return;
     } else if constexpr (EPI == kEpiAccumulate) {
-      if constexpr (BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 &&
-                    WM % (NT / 32) == 0)
-        epilogue_accumulate_staged(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
+      if constexpr (kStagedAccumulate)
+        epilogue_accumulate_staged<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
       else
         epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
       return;
     } else if constexpr (EPI == kEpiAccumulateF32) {
-      epilogue_accumulate<float>(g, m0, n0, lane, wave_m, wave_n, acc);
+      if constexpr (kStagedAccumulate)
+        epilogue_accumulate_staged<float>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
+      else
+        epilogue_accumulate<float>(g, m0, n0, lane, wave_m, wave_n, acc);
       return;
     }
     // Store epilogues. Accumulator register r of lane l in a 32x32 tile holds
@@ -927,7 +958,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats || EPI == kEpiPartialF32) {
     if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
   }
-  if constexpr (A_K && B_K && EPI == kEpiAccumulate) {
+  if constexpr (A_K && B_K && (EPI == kEpiAccumulate || EPI == kEpiAccumulateF32)) {
     if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
   }
   return launch_tiles<kGemmBM, kWavesM, kWavesN, A_K, B_K, EPI>(g, s);
