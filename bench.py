@@ -59,6 +59,8 @@ def parse():
                    help="also time the 1024- and 8192-row workloads at 1, 8 and 32 chunks")
     p.add_argument("--flce", action="store_true",
                    help="also time the fused-linear cross-entropy at 1024..8192 rows")
+    p.add_argument("--losses", action="store_true",
+                   help="also time the one-pass TVD and log-probability JSD at 4096 x 32000 bf16")
     return p.parse_args()
 
 
@@ -192,6 +194,55 @@ def flce_sweep(fljsd, steps, warmup):
     return out
 
 
+# The pages' H100 NVL figure for the TVD forward op at (4096, 32000) bf16
+# (Liger-Kernel PR #1374, Details: 0.2337 ms before and after the fix).
+PAGES_TVD_MS = 0.2337
+
+
+def losses_timing(fljsd, steps, warmup):
+    """ms per call and HBM rate of the one-pass losses at the pages' TVD shape."""
+    import numpy as np
+    import torch
+
+    import workloads
+    R, V = 4096, 32000
+    out = []
+
+    def rows(seed, logspace):
+        z = workloads.draw(seed, (R, V), 2.0, "f32")
+        z = torch.from_numpy(z).cuda()
+        t = torch.log_softmax(z, dim=-1) if logspace else torch.softmax(z, dim=-1)
+        return t.to(torch.bfloat16).contiguous()
+    for name in ("tvd", "jsd_logprob"):
+        a, b = rows(1201, name != "tvd"), rows(1202, name != "tvd")
+        grad = torch.empty_like(a)
+        ws = torch.empty(fljsd.fljsd_generalized_jsd_workspace_size(R, V, fljsd.BF16),
+                         dtype=torch.uint8, device="cuda")
+        if name == "tvd":
+            call = lambda: fljsd.fljsd_tvd(a, b, "batchmean", grad=grad, workspace=ws)
+        else:
+            call = lambda: fljsd.fljsd_jsd_logprob(a, b, 0.5, "batchmean", grad=grad, workspace=ws)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            call()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        gbps = 3.0 * R * V * 2 / (ms * 1e-3) / 1e9     # two rows read, the gradient written
+        rec = {"loss": name, "shape": [R, V], "dtype": "bf16", "ms_per_call": round(ms, 4),
+               "hbm_gbps_algorithmic": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+        if name == "tvd":
+            rec["pages_h100_ms"] = PAGES_TVD_MS
+        log(f"  {name:12s} {R}x{V} bf16: {ms:.4f} ms  {gbps:,.0f} GB/s ({100 * gbps / PEAK_HBM_GBPS:.1f}% of HBM)"
+            + (f"  (pages, H100 NVL forward: {PAGES_TVD_MS} ms)" if name == "tvd" else ""))
+        out.append(rec)
+        del a, b, grad, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(inp, w, rows):
     import numpy as np
     import threadpoolctl
@@ -321,6 +372,8 @@ def main():
         result["sweep"] = sweep(fljsd, max(3, args.steps // 2), 1)
     if args.flce:
         result["flce"] = flce_sweep(fljsd, max(3, args.steps // 2), 1)
+    if args.losses:
+        result["losses"] = losses_timing(fljsd, 20, 3)
     if not args.no_cpu_baseline:
         del X_s, W_s, X_t, W_t, ws, gX, gW
         torch.cuda.empty_cache()
