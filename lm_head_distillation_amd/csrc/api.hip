@@ -753,8 +753,11 @@ FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const
     const double row_bytes = static_cast<double>(rows) * V * es;
     e = timed(s, FLJSD_KCLASS_CE_STATS, 0.0, row_bytes, [&] { return launch_ce_stats(ca, dtype, s); });
     if (e != hipSuccess) return fail_hip(e, "launch ce_stats");
-    e = timed(s, FLJSD_KCLASS_CE_GRAD, 0.0, write_grad ? 2 * row_bytes : 0.0,
-              [&] { return launch_ce_grad(ca, dtype, write_grad, s); });
+    const bool tiled = grad_W && plan.transposed_grad_w;
+    e = timed(s, FLJSD_KCLASS_CE_GRAD, 0.0, tiled ? 3 * row_bytes : (write_grad ? 2 * row_bytes : 0.0), [&] {
+      return tiled ? launch_ce_grad_transposed(ca, ws + plan.off_zt, plan.ldt, s)
+                   : launch_ce_grad(ca, dtype, write_grad, s);
+    });
     if (e != hipSuccess) return fail_hip(e, "launch ce_grad");
     if (grad_X) {
       rc = run_grad_input(dtype, Z, plan.ldz, W, rows, H, V,
@@ -765,7 +768,7 @@ FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const
     if (grad_W) {
       rc = run_grad_weight(dtype, Z, plan.ldz, Xc + r0 * H * es, rows, H, V, grad_W,
                            plan.transposed_grad_w, ws + plan.off_zt, ws + plan.off_xt, plan.ldt,
-                           ci == 0 ? kEpiStore : kEpiAccumulate, s);
+                           ci == 0 ? kEpiStore : kEpiAccumulate, s, /*dz_transposed=*/true);
       if (rc != FLJSD_OK) return rc;
     }
   }

@@ -16,6 +16,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -148,6 +149,114 @@ __global__ __launch_bounds__(kThreads) void ce_grad_kernel(CeArgs a, bool write_
   }
 }
 
+// Pass 2 over 64-row x 64-column tiles, bf16, for a weight-gradient product:
+// dZ written in place as by ce_grad_kernel and the same tile, transposed
+// through LDS (16-byte chunk c of row r at c ^ ((r / 8) % 8)), to dzt [V, ldt].
+// A workgroup covers 64 rows and `span` columns; threads 0..63 first merge
+// their row's statistics and write its loss.
+constexpr int64_t kTileColsMax = 1024;
+constexpr int64_t kGradTargetBlocks = 2048;
+
+__global__ __launch_bounds__(kThreads) void ce_grad_t_kernel(CeArgs a, uint16_t* dzt, int64_t ldt,
+                                                            int64_t span) {
+  __shared__ float2 sh_ml[64];   // (m, log2 d)
+  __shared__ float sh_gs[64];    // gradient scale of the row (0 when it does not count)
+  __shared__ int64_t sh_y[64];
+  __shared__ uint4 tile[64][8];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * span;
+  const int64_t c_end = min(a.V, c_begin + span);
+  const int t = threadIdx.x;
+  const float Vf = static_cast<float>(a.V);
+  if (t < 64) {
+    const int64_t row = r0 + t;
+    float2 ml = make_float2(0.f, 0.f);
+    float gs = 0.f;
+    int64_t y = -1;
+    if (row < a.rows) {
+      const float4* st = a.stats + row * a.S;
+      float4 acc = st[0];
+      for (int j = 1; j < a.S; ++j) {
+        md_merge(acc.x, acc.y, st[j].x, st[j].y, kLog2e);
+        acc.z += st[j].z;
+      }
+      ml = make_float2(acc.x, hw_log2(acc.y));
+      y = a.labels[row];
+      const bool ok = counted(y, a.V, a.ignore_index);
+      gs = ok ? a.scale[0] : 0.f;
+      if (blockIdx.x == 0) {
+        const float lse = acc.x + ml.y * 0.693147180559945309f;
+        a.row_loss[row] = ok ? lse - (1.f - a.eps) * a.zy[row] - (a.eps / Vf) * acc.z : 0.f;
+      }
+    }
+    sh_ml[t] = ml;
+    sh_gs[t] = gs;
+    sh_y[t] = y;
+  }
+  __syncthreads();
+  const uint16_t* z = static_cast<const uint16_t*>(a.z);
+  uint16_t* gr = static_cast<uint16_t*>(a.grad);
+  const float off = a.eps / Vf;
+  const float hit = 1.f - a.eps;
+  for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int rl = t / 8 + 32 * h;
+      const int chunk = t % 8;
+      const int64_t row = r0 + rl;
+      const int64_t v = c0 + chunk * 8;
+      uint4 packed = make_uint4(0, 0, 0, 0);
+      if (row < a.rows && v < a.V) {
+        const int n = static_cast<int>(min<int64_t>(8, a.V - v));
+        const float2 ml = sh_ml[rl];
+        const float gs = sh_gs[rl];
+        const int64_t y = sh_y[rl];
+        float x[8], out[8];
+        load8(z + row * a.ld, v, n, a.vec_ok, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float q = hw_exp2((x[i] - ml.x) * kLog2e - ml.y);
+          out[i] = (q - off - (v + i == y ? hit : 0.f)) * gs;
+        }
+        store8(gr + row * a.ld, v, n, a.vec_ok, out);
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = i < n ? f32_to_bf16_bits(out[i]) : 0u;
+        packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
+                            b[6] | (b[7] << 16));
+      }
+      tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
+    }
+    __syncthreads();
+    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[0][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cl = t / 8 + 32 * h;
+      const int j = t % 8;
+      const int64_t v = c0 + cl;
+      const int64_t r = r0 + 8 * j;
+      if (v < a.V && r < a.rows) {
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int rl = 8 * j + i;
+          e[i] = t16[rl * 64 + ((cl >> 3) ^ ((rl >> 3) & 7)) * 8 + (cl & 7)];
+        }
+        uint16_t* q = dzt + v * ldt + r;
+        if (r + 8 <= a.rows) {
+          *reinterpret_cast<uint4*>(q) =
+              make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                         e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+        } else {
+          for (int i = 0; i < 8; ++i)
+            if (r + i < a.rows) q[i] = e[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 constexpr int kReduceThreads = 1024;
 
 __global__ __launch_bounds__(kReduceThreads) void loss_reduce_dev_kernel(const float* row_loss,
@@ -190,6 +299,18 @@ hipError_t launch_ce_grad(const CeArgs& a, int dtype, bool write_grad, hipStream
     hipLaunchKernelGGL(ce_grad_kernel<float>, grid, dim3(kThreads), 0, s, a, write_grad);
   else
     hipLaunchKernelGGL(ce_grad_kernel<uint16_t>, grid, dim3(kThreads), 0, s, a, write_grad);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_grad_transposed(const CeArgs& a, void* dzt, int64_t ldt, hipStream_t s) {
+  const int64_t row_blocks = (a.rows + 63) / 64;
+  const int64_t tiles = (a.V + 63) / 64;
+  int64_t per = (tiles * row_blocks + kGradTargetBlocks - 1) / kGradTargetBlocks;
+  per = std::max<int64_t>(1, std::min<int64_t>(per, kTileColsMax / 64));
+  const int64_t span = per * 64;
+  const dim3 grid(static_cast<unsigned>((a.V + span - 1) / span), static_cast<unsigned>(row_blocks));
+  hipLaunchKernelGGL(ce_grad_t_kernel, grid, dim3(kThreads), 0, s, a, static_cast<uint16_t*>(dzt),
+                     ldt, span);
   return hipGetLastError();
 }
 

@@ -74,6 +74,8 @@ hipError_t launch_ce_scale(const int64_t* labels, int64_t BT, int64_t V, int64_t
                            int reduction, float* scale, hipStream_t s);
 hipError_t launch_ce_stats(const CeArgs& a, int dtype, hipStream_t s);
 hipError_t launch_ce_grad(const CeArgs& a, int dtype, bool write_grad, hipStream_t s);
+// bf16 pass 2 that also writes dZ^T [V, ldt] (the weight-gradient operand).
+hipError_t launch_ce_grad_transposed(const CeArgs& a, void* dzt, int64_t ldt, hipStream_t s);
 // loss[0] = scale[1] * sum(row_loss[0..n)), deterministic order.
 hipError_t launch_loss_reduce_dev(const float* row_loss, int64_t n, const float* scale,
                                   float* loss, hipStream_t s);
