@@ -218,12 +218,8 @@ __global__ __launch_bounds__(kThreads) void ce_grad_t_kernel(CeArgs a, uint16_t*
           const float q = hw_exp2((x[i] - ml.x) * kLog2e - ml.y);
           out[i] = (q - off - (v + i == y ? hit : 0.f)) * gs;
         }
-        store8(gr + row * a.ld, v, n, a.vec_ok, out);
-        uint32_t b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = i < n ? f32_to_bf16_bits(out[i]) : 0u;
-        packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                            b[6] | (b[7] << 16));
+        packed = pack8_bf16(out, n);
+        store8_packed(gr + row * a.ld, v, n, a.vec_ok, packed);
       }
       tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
     }

@@ -19,11 +19,26 @@ __device__ inline float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                       // round to nearest even
-  return u >> 16;
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even and packed as bf16, a in the low
+// half: one gfx950 v_cvt_pk_bf16_f32. It agrees bit for bit with
+// round-to-nearest-even on every non-NaN input (all 2^32 fp32 patterns were
+// compared on the device, denormals included); a NaN stays a NaN.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+__device__ inline uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// Eight values as packed bf16; entries at or past n are zero.
+__device__ inline uint4 pack8_bf16(const float* x, int n) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = i < n ? x[i] : 0.f;
+  return make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                    pack_bf16x2(y[6], y[7]));
 }
 
 // Load up to 8 consecutive elements starting at column v; lanes at or past n
@@ -66,17 +81,18 @@ __device__ inline void store8(float* p, int64_t v, int n, bool vec, const float*
   }
 }
 
-__device__ inline void store8(uint16_t* p, int64_t v, int n, bool vec, const float* x) {
+// Up to 8 packed bf16 values (pack8_bf16) to columns v .. v + n - 1.
+__device__ inline void store8_packed(uint16_t* p, int64_t v, int n, bool vec, uint4 q) {
   if (n == 8 && vec) {
-    uint4 q;
-    q.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
-    q.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
-    q.z = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
-    q.w = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
     *reinterpret_cast<uint4*>(p + v) = q;
   } else {
-    for (int i = 0; i < n; ++i) p[v + i] = static_cast<uint16_t>(f32_to_bf16_bits(x[i]));
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    for (int i = 0; i < n; ++i) p[v + i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
   }
+}
+
+__device__ inline void store8(uint16_t* p, int64_t v, int n, bool vec, const float* x) {
+  store8_packed(p, v, n, vec, pack8_bf16(x, n));
 }
 
 __device__ inline float wave_sum(float x) {

@@ -152,8 +152,7 @@ __device__ inline void unpack_quad(float4 q, float (&v)[4]) {
 __device__ inline void store_quad(uint16_t* p, const float (&v)[4], int64_t left, bool vec) {
   if (vec && left >= 4) {
     *reinterpret_cast<uint2*>(p) =
-        make_uint2(f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
-                   f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16));
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
     return;
   }
   for (int k = 0; k < 4; ++k)
@@ -640,8 +639,8 @@ struct GemmKernel {
           const int col = wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
           const int slot = (col >> 2) ^ (row & 15);
           quads[row * QPR + slot] =
-              make_uint2(f32_to_bf16_bits(acc[i][j][4 * q]) | (f32_to_bf16_bits(acc[i][j][4 * q + 1]) << 16),
-                         f32_to_bf16_bits(acc[i][j][4 * q + 2]) | (f32_to_bf16_bits(acc[i][j][4 * q + 3]) << 16));
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
         }
       }
     }
@@ -784,16 +783,15 @@ struct GemmKernel {
           }
         } else {
           const uint32_t w[4] = {old[p][0].x, old[p][0].y, old[p][0].z, old[p][0].w};
-          uint32_t out[8];
+          uint32_t out[4];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            out[e] = f32_to_bf16_bits(__uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16) + add[e]);
+          for (int d = 0; d < 4; ++d)
+            out[d] = pack_bf16x2(bf16_lo(w[d]) + add[2 * d], bf16_hi(w[d]) + add[2 * d + 1]);
           if (vec && n + 8 <= g.N) {
-            *reinterpret_cast<uint4*>(dst) = make_uint4(out[0] | (out[1] << 16), out[2] | (out[3] << 16),
-                                                        out[4] | (out[5] << 16), out[6] | (out[7] << 16));
+            *reinterpret_cast<uint4*>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
           } else {
             for (int e = 0; e < 8; ++e)
-              if (n + e < g.N) dst[e] = static_cast<uint16_t>(out[e]);
+              if (n + e < g.N) dst[e] = static_cast<uint16_t>(out[e >> 1] >> (16 * (e & 1)));
           }
         }
       }

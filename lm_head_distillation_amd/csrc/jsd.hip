@@ -301,8 +301,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
       *reinterpret_cast<float4*>(o) = acc;
     } else {
       uint2 q;
-      q.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
-      q.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+      q.x = pack_bf16x2(acc.x, acc.y);
+      q.y = pack_bf16x2(acc.z, acc.w);
       *reinterpret_cast<uint2*>(o) = q;
     }
   }
@@ -394,12 +394,8 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
           const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
           out[i] = dA * a.grad_scale;
         }
-        store8(gr + row * a.ld, v, n, a.vec_ok, out);
-        uint32_t b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = i < n ? f32_to_bf16_bits(out[i]) : 0u;
-        packed = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16),
-                            b[6] | (b[7] << 16));
+        packed = pack8_bf16(out, n);
+        store8_packed(gr + row * a.ld, v, n, a.vec_ok, packed);
       }
       tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
     }
