@@ -157,15 +157,14 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
     float ys[8], yt[8];
     load8(zs, v, n, a.vec_ok, ys);
     load8(zt, v, n, a.vec_ok, yt);
+    // Columns past the row end load as -inf in both rows: Q = P = 0, an exact
+    // tie, which adds exactly 0 to both sums, so no per-element mask is needed.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < n) {
-        float Q, P, l, g, gacc;
-        jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
-                        gacc);
-        lsum += l;
-        gsum += gacc;
-      }
+      float Q, P, l, g, gacc;
+      jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
+      lsum += l;
+      gsum += gacc;
     }
   }
   lsum = wave_sum(lsum);

@@ -87,11 +87,13 @@ __global__ __launch_bounds__(kThreads) void logprob_jsd_kernel(ElemArgs a) {
     float x[8], y[8], out[8];
     load8(xs, v, n, a.vec_ok, x);
     load8(ys, v, n, a.vec_ok, y);
+    // Columns past the row end load as -inf in both rows (Q = P = 0): an
+    // exact tie, whose loss term is exactly 0.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float l, g;
       logprob_terms<MODE>(x[i], y[i], a.beta, l, g);
-      if (i < n) lsum += l;
+      lsum += l;
       out[i] = g * a.grad_scale;
     }
     if (gr) store8(gr, v, n, a.vec_ok, out);
