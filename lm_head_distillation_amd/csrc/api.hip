@@ -304,7 +304,7 @@ int run_grad_weight(int dtype, const void* dZ, int64_t ldz, const void* X, int64
   g.epilogue = epilogue;
   g.splitk = 1;
   g.k_per_split = rows;
-  g.group_m = 1;
+  g.group_m = 4;   // an XCD's concurrent 256 x 256 tiles: 4 M x 8 N (measured best of 1..16)
   g.wgrad = true;
   hipError_t e = timed(s, FLJSD_KCLASS_GEMM_GRAD_WEIGHT, 2.0 * rows * H * V, gemm_bytes(g, es),
                        [&] { return gemm(dtype, g, s); });
