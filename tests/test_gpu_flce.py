@@ -105,3 +105,42 @@ def test_optional_gradients(fl):
     assert float(only_loss[0]) == float(full[0])
     only_w = _run(fl, X, W, y, "bf16", -100, 0.0, "mean", 2, grad_input=False)
     assert torch.equal(only_w[2].view(torch.int16), full[2].view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_vocab_entry(fl, dtype):
+    """V = 1: the softmax is 1 at the only label, so every counted row's
+    gradient is exactly 0 and its loss is 0 up to the rounding of
+    (1 - eps) z + eps z against z."""
+    X, W, _ = _case(606, 21, 64, 1, dtype)
+    y = np.zeros(21, dtype=np.int64)
+    y[3] = -100
+    for eps in (0.0, 0.1):
+        loss, gX, gW = _run(fl, X, W, y, dtype, -100, eps, "none", 2)
+        rl, _, _ = oracle.fused_linear_cross_entropy(to_f64(X, dtype), to_f64(W, dtype), y, -100, eps,
+                                                     "none")
+        assert not np.any(rl)
+        assert np.all(np.abs(from_device(loss)) <= 1e-6), f"eps={eps}"
+        assert int(torch.count_nonzero(gX)) == 0 and int(torch.count_nonzero(gW)) == 0, f"eps={eps}"
+
+
+@pytest.mark.slow
+def test_beyond_2g_logit_elements(fl):
+    """17000 x 256 x 128256 bf16, one chunk: the logits and dZ^T hold 2.18e9
+    elements, past 2^31. Sampled rows on both sides of element 2^31 against
+    the oracle's per-row cross-entropy; all rows through
+    <grad_W, W> = <dZ, Z> = <grad_X, X>."""
+    BT, H, V = 17000, 256, 128256
+    X, W, y = _case(607, BT, H, V, "bf16")
+    rows = np.array([0, 1, 8500, 16743, 16744, 16745, BT - 1])
+    Xr = to_f64(X, "bf16")[rows]
+    Wf = to_f64(W, "bf16")
+    ref_loss, ref_dz, valid = oracle.cross_entropy_rows(Xr @ Wf.T, y[rows], -100, 0.1)
+    loss, gX, gW = _run(fl, X, W, y, "bf16", -100, 0.1, "none", 1)
+    assert_loss_close(from_device(loss)[rows], ref_loss, TOL["bf16"], "per-row loss")
+    got_rows = from_device(gX[torch.as_tensor(rows, device=gX.device)])
+    assert_tensor_close(got_rows, ref_dz @ Wf, TOL["bf16"], "grad_X rows")
+    Xd, Wd = to_device(X, "bf16"), to_device(W, "bf16")
+    lhs = float((gW.double() * Wd.double()).sum())
+    rhs = float((gX.double() * Xd.double()).sum())
+    assert abs(lhs - rhs) <= 2e-2 * max(abs(lhs), abs(rhs)), f"{lhs} vs {rhs}"

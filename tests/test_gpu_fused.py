@@ -254,3 +254,51 @@ def test_status_codes_on_device(fl):
     with pytest.raises(fl.FljsdError) as e:
         fl.fljsd_forward_backward(*dev, 1.5, 1.0, "batchmean", 1)
     assert e.value.code == -1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_vocab_entry(fl, dtype):
+    """V = 1, the method's degenerate case: both distributions are the point
+    mass on the one entry (P == Q == 1, an exact tie), so the loss and every
+    gradient are exactly 0 under every reduction and chunking."""
+    inp = _adhoc(611, 37, 64, 64, 1, dtype)
+    dev = _device_inputs(inp, dtype)
+    ref = _oracle_of(inp, dtype, 0.5, 2.0, "batchmean")
+    assert float(ref[0]) == 0.0 and not np.any(ref[1]) and not np.any(ref[2])
+    for red in ("batchmean", "sum", "mean", "none"):
+        for nc in (1, 3):
+            loss, gX, gW = _run(fl, dev, 0.5, 2.0, red, nc)
+            assert np.all(from_device(loss) == 0.0), f"{red} nc={nc}"
+            assert int(torch.count_nonzero(gX)) == 0 and int(torch.count_nonzero(gW)) == 0, f"{red} nc={nc}"
+
+
+@pytest.mark.slow
+def test_beyond_2g_logit_elements(fl):
+    """17000 x 256 x 128256 bf16, one chunk: each logits buffer (and dZ^T)
+    holds 2.18e9 elements, past 2^31, so every flat offset into them must be
+    64-bit. Sampled rows on both sides of element 2^31 (row 16744 starts past
+    it) against the oracle one by one; all rows through the identity
+    <grad_W, W_s> = <dZ, Z_s> = <grad_X, X_s>."""
+    BT, H, V = 17000, 256, 128256
+    assert BT * V > 2 ** 31
+    w = workloads.Workload("beyond_2g", 621, BT, H, H, V, "bf16", 0.5, 2.0, "batchmean",
+                           "independent")
+    inp = workloads.make_inputs(w)
+    dev = _device_inputs(inp, "bf16")
+    rows = np.array([0, 1, 8500, 16743, 16744, 16745, BT - 1])
+    ref_loss, ref_gX = oracle.fused_linear_jsd_rows(
+        *(to_f64(inp[k], "bf16") for k in ("X_s", "W_s", "X_t", "W_t")), rows, w.beta,
+        w.temperature, w.reduction)
+    loss, gX, gW = _run(fl, dev, w.beta, w.temperature, w.reduction, 1)
+    got_rows = from_device(gX[torch.as_tensor(rows, device=gX.device)])
+    assert_tensor_close(got_rows, ref_gX, TOL["bf16"], "grad_input rows")
+    lhs = float((gW.double() * dev[1].double()).sum())
+    rhs = float((gX.double() * dev[0].double()).sum())
+    assert abs(lhs - rhs) <= 2e-2 * max(abs(lhs), abs(rhs)), f"{lhs} vs {rhs}"
+    assert torch.isfinite(gW).all() and torch.isfinite(gX).all()
+    del gX, gW
+    row_loss, _, _ = _run(fl, dev, w.beta, w.temperature, "none", 1, grad_input=False,
+                          grad_weight=False)
+    rl = from_device(row_loss)
+    assert_loss_close(rl[rows], ref_loss, TOL["bf16"], "per-row loss")
+    assert_loss_close(from_device(loss), rl.mean(), {"loss_rel": 1e-5}, "batchmean = mean of rows")

@@ -135,3 +135,16 @@ def test_single_column(fl):
     loss, grad, _ = _run(fl, z, -z, 1, "f32", 0.5, 1.0, "sum")
     assert from_device(loss) == 0.0
     assert np.all(from_device(grad) == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_single_vocab_entry(fl, dtype, beta):
+    """V = 1: P == Q == 1 in every row (an exact tie), so the loss and the
+    gradient are exactly 0 in every branch; the oracle agrees."""
+    zs, _ = _logits(31, 9, 1, 2.0, dtype)
+    zt, _ = _logits(32, 9, 1, 2.0, dtype)
+    ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, dtype), to_f64(zt, dtype), beta, 2.0, "none")
+    assert not np.any(ref_loss) and not np.any(ref_grad)
+    loss, grad, _ = _run(fl, zs, zt, 1, dtype, beta, 2.0, "none")
+    assert np.all(from_device(loss) == 0.0) and int(torch.count_nonzero(grad)) == 0
