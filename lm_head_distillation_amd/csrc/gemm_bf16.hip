@@ -15,9 +15,8 @@
 // no registers); an N-contiguous one is read as 8 (n) x 4 (k) blocks of four
 // 16-byte row segments and transposed in registers into 8-byte LDS writes.
 //
-// Pipeline: K-tiles of 64 through two LDS stages (the template also builds
-// deeper pipelines of 32-wide K-tiles for two K-contiguous operands; on the
-// logits product they measured slower than two stages of 64). The two waves
+// Pipeline: K-tiles of 64 (128-byte rows, whole cache lines) through two LDS
+// stages. The two waves
 // sharing a SIMD issue the next tile's loads at different K steps, so one
 // keeps the matrix core busy while the other waits for its loads to be
 // accepted. Edge blocks and a partial last K-tile take a bounds-checked
@@ -62,17 +61,14 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int 
   tn = r / gm;
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row r, for CPR chunks per
-// row. Eight rows' chunk c (one fragment read of eight lanes) land in eight
-// distinct bank groups, and so do the transposed writes of rows 8j + i for
-// consecutive j.
+// Physical 16-byte chunk of logical chunk c in LDS row r (eight chunks, 128
+// bytes, per row). Eight rows' chunk c (one fragment read of eight lanes)
+// land in eight distinct bank groups, and so do the transposed writes of rows
+// 8j + i for consecutive j.
 template <int CPR>
 __device__ inline int swz(int r, int c) {
-  if constexpr (CPR == 8) {
-    return c ^ ((r ^ (r >> 3)) & 7);
-  } else {  // CPR == 4: two rows share one 128-byte bank line
-    return c ^ (((r >> 1) ^ (r >> 3)) & 3);
-  }
+  static_assert(CPR == 8, "64-wide K-tiles");
+  return c ^ ((r ^ (r >> 3)) & 7);
 }
 
 // A lane's value after a DPP move within its 16-lane row (gfx9 encodings):
@@ -113,69 +109,9 @@ __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
                     e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
 }
 
-// Four consecutive outputs of one row of C: bf16 (8 bytes) or fp32 (16
-// bytes). `left` is how many columns remain in the row (fewer than four only
-// at the right edge); `vec` says the row stride keeps whole quads aligned.
-template <class Out>
-struct QuadOf;
-template <>
-struct QuadOf<uint16_t> { using type = uint2; };
-template <>
-struct QuadOf<float> { using type = float4; };
-
-__device__ inline uint2 load_quad(const uint16_t* p, int64_t left, bool vec) {
-  if (vec && left >= 4) return *reinterpret_cast<const uint2*>(p);
-  uint16_t e[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) e[k] = k < left ? p[k] : uint16_t(0);
-  return make_uint2(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16));
-}
-__device__ inline float4 load_quad(const float* p, int64_t left, bool vec) {
-  if (vec && left >= 4) return *reinterpret_cast<const float4*>(p);
-  float e[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) e[k] = k < left ? p[k] : 0.f;
-  return make_float4(e[0], e[1], e[2], e[3]);
-}
-__device__ inline void unpack_quad(uint2 q, float (&v)[4]) {
-  v[0] = __uint_as_float(q.x << 16);
-  v[1] = __uint_as_float(q.x & 0xffff0000u);
-  v[2] = __uint_as_float(q.y << 16);
-  v[3] = __uint_as_float(q.y & 0xffff0000u);
-}
-__device__ inline void unpack_quad(float4 q, float (&v)[4]) {
-  v[0] = q.x;
-  v[1] = q.y;
-  v[2] = q.z;
-  v[3] = q.w;
-}
-__device__ inline void store_quad(uint16_t* p, const float (&v)[4], int64_t left, bool vec) {
-  if (vec && left >= 4) {
-    *reinterpret_cast<uint2*>(p) =
-        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    return;
-  }
-  for (int k = 0; k < 4; ++k)
-    if (k < left) p[k] = static_cast<uint16_t>(f32_to_bf16_bits(v[k]));
-}
-__device__ inline void store_quad(float* p, const float (&v)[4], int64_t left, bool vec) {
-  if (vec && left >= 4) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    return;
-  }
-  for (int k = 0; k < 4; ++k)
-    if (k < left) p[k] = v[k];
-}
-
-// Wait until at most n of this wave's vector-memory loads are outstanding
-// (loads complete in issue order). Counts this file does not use wait for all.
-__device__ inline void wait_vmem_upto(int n) {
-  switch (n) {
-    case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-  }
-}
+// Wait for all of this wave's outstanding vector-memory loads (a direct
+// copy counts until its data is in LDS).
+__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
           int EPI>
@@ -188,17 +124,13 @@ struct GemmKernel {
   static constexpr int TM = WM / 32;
   static constexpr int TN = WN / 32;
   static constexpr int LDS_STAGE = (BM + BN) * CPR;   // uint4 per stage
-  static_assert(CPR == 4 || CPR == 8, "K-tile of 32 or 64");
+  static_assert(CPR == 8, "K-tile of 64");
   static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
-  static_assert(STAGES == 2 || (A_K && B_K), "deep pipelines need two K-contiguous operands");
-  // The accumulating epilogue reads, adds to and rewrites C. It computes the
-  // transposed 32x32 products (B's fragment first), which leaves four
-  // consecutive output columns of one row in each group of four accumulator
-  // registers: the old values then come in as 8-byte loads, all issued
-  // before any is used, so a block pays one memory latency instead of one
-  // per batch of 2-byte loads.
-  // The bf16 store epilogues use the same layout: a lane's four consecutive
-  // columns go to LDS as one 8-byte write (see epilogue_staged).
+  static_assert(STAGES == 2, "two LDS stages of 64-wide K-tiles");
+  // The staged epilogues compute the transposed 32x32 products (B's fragment
+  // first), which leaves four consecutive output columns of one row in each
+  // group of four accumulator registers: a lane's four columns go to LDS as
+  // one 8-byte (bf16) or 16-byte (fp32) write.
   static constexpr bool SWAP_D = EPI == kEpiAccumulate || EPI == kEpiAccumulateF32 ||
                                  EPI == kEpiStore || EPI == kEpiStoreStats;
   static_assert(!SWAP_D || STAGES * LDS_STAGE * 16 >= BM * BN * 2,
@@ -212,7 +144,6 @@ struct GemmKernel {
   static constexpr int regs(int R, bool kcontig) { return kcontig ? chunks(R) : 4 * units(R); }
   // Direct copies: one wave instruction fills 64 / CPR rows (1 KB).
   static constexpr int dma_insts(int R) { return R / (64 / CPR) / NW; }
-  static constexpr int DMA_PER_TILE = (A_K ? dma_insts(BM) : 0) + (B_K ? dma_insts(BN) : 0);
 
   template <int R, bool KCONTIG>
   static __device__ inline void check_split() {
@@ -420,7 +351,7 @@ struct GemmKernel {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     for (int t = 0; t < nkf; ++t) {
-      wait_vmem_upto(0);
+      wait_vmem_all();
       __syncthreads();
       const bool more = t + 1 < nkf;
       uint4* st = lds[(t + 1) & 1];
@@ -437,44 +368,20 @@ struct GemmKernel {
   }
 
   // Both operands K-contiguous, interior block, whole K-tiles: every tile is
-  // copied straight into LDS, STAGES - 1 tiles ahead of the one multiplied.
-  // At the top of iteration t, tile t's copies must have landed (each wave
-  // waits for its own, the barrier for everyone's) and stage (t - 1) % STAGES
-  // is free again, so tile t + STAGES - 1 goes there.
+  // copied straight into LDS one tile ahead of the one multiplied. At the top
+  // of iteration t, tile t's copies must have landed (each wave waits for its
+  // own, the barrier for everyone's) and the other stage is free again.
   static __device__ inline void mainloop_dma(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                              int64_t m0, int64_t n0, int64_t kb, int nkf,
                                              floatx16 (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
-    if constexpr (STAGES == 2) {
-      dma_tile<BM>(A, g.lda, m0, kb, lds[0]);
-      dma_tile<BN>(B, g.ldb, n0, kb, lds[0] + BM * CPR);
-      if (late_wave())
-        loop_dma2<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
-      else
-        loop_dma2<0>(g, lds, m0, n0, kb, nkf, acc);
-      __syncthreads();
-      return;
-    }
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p) {
-      if (p < nkf) {
-        dma_tile<BM>(A, g.lda, m0, kb + static_cast<int64_t>(p) * BK, lds[p]);
-        dma_tile<BN>(B, g.ldb, n0, kb + static_cast<int64_t>(p) * BK, lds[p] + BM * CPR);
-      }
-    }
-    for (int t = 0; t < nkf; ++t) {
-      // Tiles t+1 .. min(t + STAGES - 2, nkf - 1) may still be in flight.
-      wait_vmem_upto(min(STAGES - 2, nkf - 1 - t) * DMA_PER_TILE);
-      __syncthreads();
-      const int tn = t + STAGES - 1;
-      if (tn < nkf) {
-        uint4* st = lds[tn % STAGES];
-        dma_tile<BM>(A, g.lda, m0, kb + static_cast<int64_t>(tn) * BK, st);
-        dma_tile<BN>(B, g.ldb, n0, kb + static_cast<int64_t>(tn) * BK, st + BM * CPR);
-      }
-      compute_stage(lds[t % STAGES], acc);
-    }
+    dma_tile<BM>(A, g.lda, m0, kb, lds[0]);
+    dma_tile<BN>(B, g.ldb, n0, kb, lds[0] + BM * CPR);
+    if (late_wave())
+      loop_dma2<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
+    else
+      loop_dma2<0>(g, lds, m0, n0, kb, nkf, acc);
     __syncthreads();
   }
 
@@ -502,7 +409,7 @@ struct GemmKernel {
     };
     issue(kb, lds[0]);
     finish(lds[0]);
-    wait_vmem_upto(0);
+    wait_vmem_all();
     __syncthreads();
     for (int t = 0; t < nkf; ++t) {
       uint4* cur = lds[t & 1];
@@ -514,7 +421,7 @@ struct GemmKernel {
         if (STEP > 0 && more && ks == STEP) issue(k0, nxt);
       });
       if (more) finish(nxt);
-      wait_vmem_upto(0);
+      wait_vmem_all();
       __syncthreads();
     }
   }
@@ -558,57 +465,6 @@ struct GemmKernel {
         store_tile<BN, B_K>(nxt, BM, rb);
       }
       __syncthreads();
-    }
-  }
-
-  // C = C + A B with the transposed accumulator layout (SWAP_D): register r
-  // of lane l in a 32x32 tile holds row l%32 and column 8*(r/4) + 4*(l/32) +
-  // r%4, so registers 4q..4q+3 are four consecutive columns of one row. The
-  // old values of IG row blocks are all loaded before any is used (64
-  // registers in flight), then added in fp32 and rounded once to Out.
-  template <class Out>
-  static __device__ inline void epilogue_accumulate(const GemmArgs& g, int64_t m0, int64_t n0,
-                                                    int lane, int wave_m, int wave_n,
-                                                    floatx16 (&acc)[TM][TN]) {
-    using Quad = typename QuadOf<Out>::type;
-    constexpr int IG = sizeof(Out) == 4 ? (TM >= 2 ? TM / 2 : 1) : TM;
-    static_assert(TM % IG == 0, "row groups");
-    Out* C = static_cast<Out*>(g.C);
-    const bool vec_ok = (g.ldc & 3) == 0;
-#pragma unroll
-    for (int i0 = 0; i0 < TM; i0 += IG) {
-      Quad old[IG][TN][4];
-#pragma unroll
-      for (int i = 0; i < IG; ++i) {
-        const int64_t m = m0 + wave_m * WM + (i0 + i) * 32 + (lane & 31);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-            old[i][j][q] = m < g.M ? load_quad(C + m * g.ldc + n, g.N - n, vec_ok)
-                                   : Quad{};
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < IG; ++i) {
-        const int64_t m = m0 + wave_m * WM + (i0 + i) * 32 + (lane & 31);
-        if (m >= g.M) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
-            if (n >= g.N) continue;
-            float v[4];
-            unpack_quad(old[i][j][q], v);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] += acc[i0 + i][j][4 * q + k];
-            store_quad(C + m * g.ldc + n, v, g.N - n, vec_ok);
-          }
-        }
-      }
     }
   }
 
@@ -686,7 +542,7 @@ struct GemmKernel {
     }
   }
 
-  // C = C + A B for bf16 C, staged through LDS: the fp32 products of one
+  // C = C + A B for bf16 or fp32 C, staged through LDS: the fp32 products of one
   // wave row (WM rows of the tile) at a time go to LDS (a lane's four
   // consecutive columns as one 16-byte write, chunk c of row r at
   // c ^ (r % 32)), then each 32-lane half-wave takes whole rows: it loads the
@@ -697,8 +553,8 @@ struct GemmKernel {
                                                            int64_t n0, int lane, int wave_m,
                                                            int wave_n,
                                                            floatx16 (&acc)[TM][TN], uint4* lds) {
-    static_assert(BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16,
-                  "one wave row of 1 KB fp32 rows fits in LDS");
+    static_assert(BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 && WM % (NT / 32) == 0,
+                  "one wave row of 1 KB fp32 rows fits in LDS, whole rows per half-wave");
     constexpr bool F32 = sizeof(Out) == 4;
     constexpr int V16 = F32 ? 2 : 1;             // 16-byte vectors of old values per lane and row
     constexpr int HALF = WM;
@@ -798,9 +654,6 @@ struct GemmKernel {
     }
   }
 
-  static constexpr bool kStagedAccumulate =
-      BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 && WM % (NT / 32) == 0;
-
   static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
@@ -840,42 +693,26 @@ struct GemmKernel {
 
     if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats) {
       epilogue_staged<EPI == kEpiStoreStats>(g, m0, n0, tn, lane, wave_m, wave_n, acc, &lds[0][0]);
-      return;
     } else if constexpr (EPI == kEpiAccumulate) {
-      if constexpr (kStagedAccumulate)
-        epilogue_accumulate_staged<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
-      else
-        epilogue_accumulate<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc);
-      return;
+      epilogue_accumulate_staged<uint16_t>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
     } else if constexpr (EPI == kEpiAccumulateF32) {
-      if constexpr (kStagedAccumulate)
-        epilogue_accumulate_staged<float>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
-      else
-        epilogue_accumulate<float>(g, m0, n0, lane, wave_m, wave_n, acc);
-      return;
-    }
-    // Store epilogues. Accumulator register r of lane l in a 32x32 tile holds
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+      epilogue_accumulate_staged<float>(g, m0, n0, lane, wave_m, wave_n, acc, &lds[0][0]);
+    } else {
+      // fp32 store (split-K partials, plane `split`). Accumulator register r
+      // of lane l in a 32x32 tile holds row 8*(r/4) + 4*(l/32) + r%4, column
+      // l%32.
+      static_assert(EPI == kEpiPartialF32, "epilogue");
+      float* C = static_cast<float*>(g.C) + static_cast<int64_t>(split) * g.M * g.ldc;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = n0 + wave_n * WN + j * 32 + (lane & 31);
-        if (n >= g.N) continue;
+        for (int j = 0; j < TN; ++j) {
+          const int64_t n = n0 + wave_n * WN + j * 32 + (lane & 31);
+          if (n >= g.N) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + wave_m * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m >= g.M) continue;
-          const float v = acc[i][j][r];
-          if constexpr (EPI == kEpiPartialF32) {
-            float* C = static_cast<float*>(g.C) + static_cast<int64_t>(split) * g.M * g.ldc;
-            C[m * g.ldc + n] = v;
-          } else {
-            uint16_t* C = static_cast<uint16_t*>(g.C);
-            float out = v;
-            if constexpr (EPI == kEpiAccumulate)
-              out += __uint_as_float(static_cast<uint32_t>(C[m * g.ldc + n]) << 16);
-            C[m * g.ldc + n] = static_cast<uint16_t>(f32_to_bf16_bits(out));
+          for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wave_m * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < g.M) C[m * g.ldc + n] = acc[i][j][r];
           }
         }
       }
