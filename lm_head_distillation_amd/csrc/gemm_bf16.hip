@@ -776,9 +776,11 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
 }
 
 // Products with few rows (the logits and grad_input of small chunks) take
-// 64-row tiles, one row of eight 64 x 32 wave tiles: a 256-row tile would
-// spend most of its matrix-core work on rows that do not exist, and the
-// smaller tile lets two workgroups share a CU.
+// 64-row tiles up to 64 rows and 128-row tiles up to 128, one row of eight
+// wave tiles: a 256-row tile would spend most of its matrix-core work on rows
+// that do not exist, and 64-row tiles let two workgroups share a CU. Between
+// 65 and 128 rows one 128-row tile streams each weight panel once instead of
+// twice (128 x 128256 x 4096 logits: 0.238 -> 0.221 ms).
 constexpr int64_t kSkinnyMaxM = 128;
 
 // The accumulating weight-gradient product of a chunk of at most kSkinnyMaxK
@@ -791,7 +793,8 @@ constexpr int64_t kSkinnyMaxK = 1024;
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
   if constexpr (EPI == kEpiStore || EPI == kEpiStoreStats || EPI == kEpiPartialF32) {
-    if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
+    if (g.M <= kSkinnyMaxM / 2 && !g.wgrad) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
+    if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<128, 1, 8, A_K, B_K, EPI>(g, s);
   }
   if constexpr (A_K && B_K && (EPI == kEpiAccumulate || EPI == kEpiAccumulateF32)) {
     if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);

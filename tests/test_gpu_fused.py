@@ -179,6 +179,7 @@ def _oracle_of(inp, dtype, beta, T, reduction):
 @pytest.mark.parametrize("BT,H_s,H_t,V,nc", [
     (1, 64, 64, 100, 1),          # one row
     (300, 72, 72, 1000, 1),       # ragged M, N and K tiles
+    (200, 264, 264, 5003, 2),     # 100-row chunks: 128-row tiles with ragged rows
     (300, 72, 72, 1000, 3),       # ragged chunks
     (300, 72, 72, 1000, 7),
     (64, 128, 256, 3000, 2),      # teacher hidden size differs
