@@ -26,9 +26,11 @@ SlicePlan plan_slices(int64_t rows, int64_t V) {
 
 void plan_splitk(int64_t M, int64_t N, int64_t K, int* splitk, int64_t* k_per_split) {
   const int64_t tiles = cdiv(M, kGemmBM) * cdiv(N, kGemmBN);
+  // Products of at most 64 rows run 64-row tiles, two workgroups per CU.
+  const int64_t target = M <= 64 ? 2 * kGemmTargetBlocks : kGemmTargetBlocks;
   int64_t s = 1;
-  if (tiles < kGemmTargetBlocks * 3 / 4) {
-    s = cdiv(kGemmTargetBlocks, tiles);
+  if (tiles < target * 3 / 4) {
+    s = cdiv(target, tiles);
     // Keep at least four K-tiles per split.
     s = std::min<int64_t>(s, std::max<int64_t>(1, K / (4 * kGemmBK)));
   }
