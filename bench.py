@@ -39,6 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 GEMM_CLASSES = ("gemm_logits", "gemm_grad_input", "gemm_grad_weight")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock.json")
 
 
 def log(*a):
@@ -84,11 +85,11 @@ def roofline_of(cls, k):
             "unit": "GB/s", "per_launch": per_launch, "avg_launch_ms": avg_s * 1e3}
 
 
-def traffic_for(cls):
-    """Measured HBM bytes per launch for a kernel class, if a counter summary
-    for the current kernel sources is on file; else None."""
+def _profile_entry(path, cls):
+    """The entry for a kernel class in a counter summary under profiles/, if
+    it was taken with the current kernel sources; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -98,7 +99,21 @@ def traffic_for(cls):
     from lm_head_distillation_amd.build import source_digest
     if entry.get("source_digest") != source_digest():
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry
+
+
+def traffic_for(cls):
+    """Measured HBM bytes per launch for a kernel class (rocprofv3 FETCH_SIZE
+    and WRITE_SIZE, copy-calibrated), or None."""
+    entry = _profile_entry(TRAFFIC_FILE, cls)
+    return entry.get("hbm_bytes_per_launch") if entry else None
+
+
+def clock_for(cls):
+    """Shader clock (MHz) a kernel class ran at (rocprofv3 GRBM_GUI_ACTIVE per
+    dispatch over the traced durations), or None."""
+    entry = _profile_entry(CLOCK_FILE, cls)
+    return entry.get("clock_mhz") if entry else None
 
 
 def sweep(fljsd, steps, warmup):
@@ -269,8 +284,9 @@ def cpu_baseline(inp, w, rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(every box in this setup has a single MI355X).", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the pass "
+              "runs on a single MI355X (rows would shard across GPUs with one all-reduce of "
+              "grad_W, which is not built).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -339,6 +355,12 @@ def main():
                 "unit": d["unit"], "frac": round(d["achieved"] / d["peak"], 4), "traffic": traffic,
                 "kernel": dominant, "avg_launch_ms": round(d["avg_launch_ms"], 4),
                 "per_launch": d["per_launch"]}
+    clock = clock_for(dominant)
+    if clock and d["bound"] == "mfma":
+        # The published peak assumes 2.4 GHz; the fraction at the clock the
+        # kernel held (from the committed counter summary) is reported beside it.
+        roofline["clock_mhz"] = round(clock)
+        roofline["frac_at_clock"] = round(d["achieved"] / (d["peak"] * clock / 2400.0), 4)
     gemm_ms = sum(kernels[c]["ms"] for c in GEMM_CLASSES)
     gemm_flops = sum(kernels[c]["flops"] for c in GEMM_CLASSES)
     jsd_cls = ("jsd_stats", "jsd_loss", "jsd_grad")
