@@ -369,12 +369,32 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
   const uint16_t* zt = static_cast<const uint16_t*>(a.zt);
   uint16_t* gr = static_cast<uint16_t*>(a.grad);
   const float k = a.k2;
+  // Row-major: thread -> (row, 8-column chunk) for rows t/8 and t/8 + 32.
+  // Whole 16-byte groups of both rows (and of the next 64-column tile) are
+  // loaded before any of this tile is computed: dZ goes over the student
+  // logits in place, so the compiler would otherwise keep each row's loads
+  // behind the previous row's stores. The tile hand-offs wait for LDS
+  // traffic only, so the next tile's loads stay in flight across them.
+  const int chunk = t % 8;
+  auto full = [&](int64_t row, int64_t v) { return a.vec_ok && row < a.rows && v + 8 <= a.V; };
+  auto fetch = [&](int64_t c0, uint4 (&qs)[2], uint4 (&qt)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t row = r0 + t / 8 + 32 * h;
+      const int64_t v = c0 + chunk * 8;
+      if (full(row, v)) {
+        qs[h] = *reinterpret_cast<const uint4*>(zs + row * a.ld + v);
+        qt[h] = *reinterpret_cast<const uint4*>(zt + row * a.ld + v);
+      }
+    }
+  };
+  uint4 cs[2], ct[2], ns[2], nt[2];
+  fetch(c_begin, cs, ct);
   for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
-    // Row-major: thread -> (row, 8-column chunk), two passes of 32 rows.
+    if (c0 + 64 < c_end) fetch(c0 + 64, ns, nt);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int rl = t / 8 + 32 * h;
-      const int chunk = t % 8;
       const int64_t row = r0 + rl;
       const int64_t v = c0 + chunk * 8;
       uint4 packed = make_uint4(0, 0, 0, 0);
@@ -383,8 +403,20 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         const float4 L = sh_L[rl];
         const float G = sh_G[rl];
         float ys[8], yt[8], out[8];
-        load8(zs + row * a.ld, v, n, a.vec_ok, ys);
-        load8(zt + row * a.ld, v, n, a.vec_ok, yt);
+        if (full(row, v)) {
+          const uint32_t ws[4] = {cs[h].x, cs[h].y, cs[h].z, cs[h].w};
+          const uint32_t wt[4] = {ct[h].x, ct[h].y, ct[h].z, ct[h].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ys[2 * e] = bf16_lo(ws[e]);
+            ys[2 * e + 1] = bf16_hi(ws[e]);
+            yt[2 * e] = bf16_lo(wt[e]);
+            yt[2 * e + 1] = bf16_hi(wt[e]);
+          }
+        } else {
+          load8(zs + row * a.ld, v, n, a.vec_ok, ys);
+          load8(zt + row * a.ld, v, n, a.vec_ok, yt);
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float Q, P, l, g, gacc;
@@ -398,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
       }
       tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // Transposed: thread -> (column, eight consecutive rows); a wave writes
     // 8 rows of dzt, 128 contiguous bytes each.
     const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[0][0]);
@@ -426,7 +458,12 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         }
       }
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      cs[h] = ns[h];
+      ct[h] = nt[h];
+    }
   }
 }
 
