@@ -62,7 +62,24 @@ def parse():
                    help="also time the fused-linear cross-entropy at 1024..8192 rows")
     p.add_argument("--losses", action="store_true",
                    help="also time the one-pass TVD and log-probability JSD at 4096 x 32000 bf16")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run three plain 1 GiB device copies (the reference for scaling "
+                        "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """Three device-to-device copies of 1 GiB: under `rocprofv3 --pmc FETCH_SIZE`
+    (or WRITE_SIZE) the counter per copy, against the 1 GiB it moves each way,
+    gives the factor that turns the counter into bytes."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {n} bytes three times")
 
 
 def device_inputs(inp):
@@ -291,13 +308,17 @@ def main():
 
     import torch
 
-    import workloads
-    from lm_head_distillation_amd import fljsd
-
     if not torch.cuda.is_available():
         log("no GPU visible")
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import workloads
+    from lm_head_distillation_amd import fljsd
+
     fljsd.load_library()
     w = workloads.WORKLOADS[WORKLOAD]
     t0 = time.perf_counter()
