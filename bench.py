@@ -286,16 +286,29 @@ def cpu_baseline(inp, w, rows):
     X_t = workloads.to_f64(inp["X_t"][:rows], "bf16")
     W_s = workloads.to_f64(inp["W_s"], "bf16")
     W_t = workloads.to_f64(inp["W_t"], "bf16")
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    blas_name = ", ".join(f"{i.get('internal_api', '?')} {i.get('version') or ''}".strip()
+                          for i in blas) or "no BLAS reported"
     t0 = time.perf_counter()
     oracle.fused_linear_jsd(X_s, W_s, X_t, W_t, w.beta, w.temperature, w.reduction, block_rows=256)
     dt = time.perf_counter() - t0
     del W_s, W_t
     return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"first {rows} of {w.BT} rows, full H={w.H_s} and V={w.V} weights, "
-                       f"fp64 numpy/OpenBLAS, {dt:.1f} s"),
+                       f"fp64 numpy ({blas_name}) on {cpu_model()}, {dt:.1f} s"),
             "seconds": dt}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
 
 
 def main():
@@ -346,12 +359,18 @@ def main():
     log(f"warmup {args.warmup} steps done; num_chunks={nc}, workspace {ws.numel() / 2**20:.0f} MiB")
 
     fljsd.fljsd_profile_enable(True)
+    # Events between the steps (on the stream the library launches on) give
+    # the spread of single steps; the throughput is the whole timed region.
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    marks[0].record()
     for i in range(args.steps):
         step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     kernels = fljsd.fljsd_profile_read()
     fljsd.fljsd_profile_enable(False)
     ms_per_step = elapsed / args.steps * 1e3
@@ -395,6 +414,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
+        "step_ms": {"median": round(step_ms[len(step_ms) // 2], 3), "min": round(step_ms[0], 3),
+                    "max": round(step_ms[-1], 3)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(tokens_per_s / PAGES_TOKENS_PER_S, 4),
