@@ -115,7 +115,7 @@ __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
 __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
-          int EPI, bool PRE_OLD = false>
+          int EPI, bool PRE_OLD = false, int EARLY_B = -1>
 struct GemmKernel {
   static constexpr int NT = WAVES_M * WAVES_N * 64;
   static constexpr int NW = NT / 64;
@@ -289,6 +289,24 @@ struct GemmKernel {
     }
   }
 
+  // Rows [r_begin, r_begin + 32 * NINST) of a K-contiguous tile, copied by the
+  // four waves of one half of the workgroup (wg = this wave's index in it).
+  template <int NINST>
+  static __device__ inline void dma_rows(const uint16_t* __restrict__ p, int64_t ld, int64_t row0,
+                                         int64_t k0, uint4* region, int r_begin, int wg) {
+    constexpr int ROWS = 64 / CPR;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NINST; ++i) {
+      const int rb = r_begin + (wg + i * 4) * ROWS;   // first row this instruction fills
+      const int r = rb + lane / CPR;
+      const int c = swz<CPR>(r, lane % CPR);
+      const uint16_t* src = p + (row0 + r) * ld + k0 + c * 8;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(region + rb * CPR), 16, 0, 0);
+    }
+  }
+
   // Fragments of one 16-wide K step for this wave.
   static __device__ inline void read_frags(const uint4* cur, int ks, int lane, int wave_m,
                                            int wave_n, bf16x8* fa, bf16x8* fb) {
@@ -345,6 +363,14 @@ struct GemmKernel {
   static constexpr int kLateStep = BK / 32;
   static __device__ inline bool late_wave() { return (threadIdx.x >> 6) >= NW / 2; }
 
+  // EARLY_B >= 0 (256 x 256 tiles, 8 waves): the early waves copy all of A
+  // and the first 32 * EARLY_B rows of B, the late waves the rest of B, so
+  // the late waves (whose copies are issued half a K-tile later and bound the
+  // hand-off) have 8 - EARLY_B copies each instead of 8. EARLY_B < 0: every
+  // wave copies 1/8 of each operand.
+  static constexpr bool kSplitCopies =
+      EARLY_B >= 0 && EARLY_B <= 8 && BM == 256 && BN == 256 && NW == 8;
+
   template <int STEP>
   static __device__ inline void loop_dma2(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
                                           int64_t n0, int64_t kb, int nkf,
@@ -358,8 +384,19 @@ struct GemmKernel {
       uint4* st = lds[(t + 1) & 1];
       const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
       auto issue = [&] {
-        dma_tile<BM>(A, g.lda, m0, k0, st);
-        dma_tile<BN>(B, g.ldb, n0, k0, st + BM * CPR);
+        if constexpr (kSplitCopies) {
+          constexpr int kEarlyB = kSplitCopies ? EARLY_B : 0;
+          const int wg = (threadIdx.x >> 6) % (NW / 2);
+          if constexpr (STEP == 0) {
+            dma_rows<BM / 32>(A, g.lda, m0, k0, st, 0, wg);
+            dma_rows<kEarlyB>(B, g.ldb, n0, k0, st + BM * CPR, 0, wg);
+          } else {
+            dma_rows<BN / 32 - kEarlyB>(B, g.ldb, n0, k0, st + BM * CPR, 32 * kEarlyB, wg);
+          }
+        } else {
+          dma_tile<BM>(A, g.lda, m0, k0, st);
+          dma_tile<BN>(B, g.ldb, n0, k0, st + BM * CPR);
+        }
       };
       if (STEP == 0 && more) issue();
       compute_stage(lds[t & 1], acc, [&](int ks) {
@@ -759,14 +796,21 @@ struct GemmKernel {
   }
 };
 
+// Copy split of the 256 x 256 tiles' main loop per product (see kSplitCopies),
+// measured on the 8192 x 128256 x 4096 shapes: the logits product 7.15 ->
+// 7.03 ms with 12 / 4 copies per early / late wave, grad_W 7.39 -> 7.32 ms
+// with 9 / 7 (each best among 8 / 8 .. 14 / 2 and the even split).
+constexpr int kEarlyBLogits = 4;
+constexpr int kEarlyBWgrad = 1;
+
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
           int EPI, bool PRE_OLD = false>
 __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmArgs g,
                                                                            int tiles_m,
                                                                            int tiles_n,
                                                                            int group_m) {
-  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD>::run(g, tiles_m, tiles_n,
-                                                                       group_m);
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD, kEarlyBLogits>::run(
+      g, tiles_m, tiles_n, group_m);
 }
 
 // The same code under a second symbol for the weight-gradient product, whose
@@ -777,8 +821,8 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_wgrad_kernel
                                                                                  int tiles_m,
                                                                                  int tiles_n,
                                                                                  int group_m) {
-  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD>::run(g, tiles_m, tiles_n,
-                                                                       group_m);
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD, kEarlyBWgrad>::run(
+      g, tiles_m, tiles_n, group_m);
 }
 
 constexpr int kWavesM = 2;
