@@ -185,6 +185,7 @@ def _oracle_of(inp, dtype, beta, T, reduction):
     (64, 128, 256, 3000, 2),      # teacher hidden size differs
     (10, 64, 64, 777, 100),       # more chunks asked than rows
     (513, 264, 136, 5003, 2),     # odd everything
+    (2100, 264, 264, 3000, 2),    # 1050-row chunks: 256-row read-add-write tiles, partial K-tile
 ])
 def test_shapes(fl, dtype, BT, H_s, H_t, V, nc):
     inp = _adhoc(7, BT, H_s, H_t, V, dtype)

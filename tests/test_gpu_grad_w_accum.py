@@ -111,6 +111,36 @@ def test_accumulate_into_existing_grad_w(fl, bf16_case, gw, nc):
         assert e <= 1e-5, f"added part differs from a fresh fp32 result: {e:.3e}"
 
 
+@pytest.fixture(scope="module")
+def long_chunk_case():
+    # Chunks of 1050 rows: the weight-gradient product of each chunk has
+    # K = 1050 (> 1024), so it runs on 256-row tiles with the staged
+    # read-add-write epilogue and a partial last K-tile; V = 3000 and H = 264
+    # give interior and ragged tiles in both directions.
+    return _inputs(44, 2100, 264, 136, 3000, "bf16")
+
+
+@pytest.mark.parametrize("gw", ["f32", "bf16"])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_long_chunks(fl, long_chunk_case, gw, accumulate):
+    dev, (rl, rX, rW) = long_chunk_case
+    V, H = dev[1].shape
+    kw = {"grad_w_dtype": torch.float32} if gw == "f32" else {}
+    expect = rW
+    if accumulate:
+        g0 = workloads.draw(9003, (V, H), float(np.std(rW)), gw)
+        out = (torch.empty(1, dtype=torch.float32, device="cuda"), torch.empty_like(dev[0]),
+               to_device(g0, gw))
+        kw.update(flags=fl.FLJSD_ACCUMULATE_GRAD_W, out=out)
+        expect = to_f64(g0, gw) + rW
+    loss, gX, gW = _ex(fl, dev, 2, **kw)
+    tol = TOL["bf16"]
+    assert_loss_close(from_device(loss), rl, tol)
+    assert_tensor_close(from_device(gX), rX, tol, "grad_input")
+    e = assert_tensor_close(from_device(gW), expect, tol, f"grad_weight {gw}")
+    print(f"1050-row chunks, {gw}, accumulate={accumulate}: grad_W normwise {e:.2e}", flush=True)
+
+
 def test_accumulate_fp32_inputs(fl):
     dev, (rl, rX, rW) = _inputs(43, 24, 64, 64, 700, "f32")
     V, H = dev[1].shape
