@@ -605,19 +605,28 @@ struct GemmKernel {
   static constexpr int kRowsPerPass = NT / 32;
   static constexpr int kPasses = WM / kRowsPerPass;
 
-  // Old values of part h (zero outside C), as 16-byte vectors: one per pass
-  // for bf16, two for fp32.
-  template <class Out>
-  static __device__ inline void load_old(const GemmArgs& g, int64_t m0, int64_t n0, int h,
-                                         uint4 (&old)[kPasses][sizeof(Out) / 2]) {
+  // The read-add-write stages kSub parts of WM / kSub rows per wave row, so
+  // the 256-row tile (two wave rows) keeps only half a wave row's products
+  // and four passes of old values in flight at a time: without spilling
+  // registers, which the whole 128-row wave rows did.
+  static constexpr int kSub = WAVES_M > 1 ? 2 : 1;
+  static constexpr int kPartRows = WM / kSub;
+  static constexpr int kPartPasses = kPartRows / kRowsPerPass;
+  static_assert(TM % kSub == 0 && kPartRows % kRowsPerPass == 0, "parts of whole 32-row tiles");
+
+  // Old values of the part starting at tile row r0 (zero outside C), as
+  // 16-byte vectors: one per pass for bf16, two for fp32.
+  template <class Out, int NP>
+  static __device__ inline void load_old(const GemmArgs& g, int64_t m0, int64_t n0, int r0,
+                                         uint4 (&old)[NP][sizeof(Out) / 2]) {
     constexpr bool F32 = sizeof(Out) == 4;
     constexpr int V16 = sizeof(Out) / 2;
     const Out* C = static_cast<const Out*>(g.C);
     const bool vec = (g.ldc & (F32 ? 3 : 7)) == 0;
     const int64_t n = n0 + 8 * (threadIdx.x & 31);
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int64_t m = m0 + h * WM + p * kRowsPerPass + (threadIdx.x >> 5);
+    for (int p = 0; p < NP; ++p) {
+      const int64_t m = m0 + r0 + p * kRowsPerPass + (threadIdx.x >> 5);
       uint32_t w[4 * V16];
 #pragma unroll
       for (int k = 0; k < 4 * V16; ++k) w[k] = 0;
@@ -650,37 +659,42 @@ struct GemmKernel {
                                                            int wave_n,
                                                            floatx16 (&acc)[TM][TN], uint4* lds,
                                                            const uint4 (*pre)[sizeof(Out) / 2]) {
-    static_assert(BN == 256 && WM * BN * 4 <= STAGES * LDS_STAGE * 16 && WM % (NT / 32) == 0,
-                  "one wave row of 1 KB fp32 rows fits in LDS, whole rows per half-wave");
+    static_assert(BN == 256 && kPartRows * BN * 4 <= STAGES * LDS_STAGE * 16 &&
+                      kPartRows % (NT / 32) == 0,
+                  "one part of 1 KB fp32 rows fits in LDS, whole rows per half-wave");
     constexpr bool F32 = sizeof(Out) == 4;
     constexpr int V16 = sizeof(Out) / 2;         // 16-byte vectors of old values per lane and row
-    constexpr int HALF = WM;
     constexpr int C16 = BN / 4;                  // fp32 16-byte chunks per row
     constexpr int ROWS_PER_PASS = kRowsPerPass;  // rows in flight per pass (one per half-wave)
-    constexpr int PASSES = kPasses;
+    constexpr int PASSES = kPartPasses;
+    constexpr int TMP = TM / kSub;               // 32-row tiles of a wave per part
     Out* C = static_cast<Out*>(g.C);
     const bool vec = (g.ldc & (F32 ? 3 : 7)) == 0;
     const int c8 = threadIdx.x & 31;             // 8-column group of the row
     const int64_t n = n0 + 8 * c8;
 #pragma unroll
-    for (int h = 0; h < WAVES_M; ++h) {
+    for (int part = 0; part < WAVES_M * kSub; ++part) {
+      const int h = part / kSub;                 // wave row
+      const int sub = part % kSub;               // part of that wave row
+      const int r_part = h * WM + sub * kPartRows;
       // Old values of this part's rows, loaded before the staging barrier
       // (or before the main loop).
       uint4 old[PASSES][V16];
       if constexpr (PRE) {
-        static_assert(WAVES_M == 1, "prefetched old values cover the single part");
+        static_assert(WAVES_M == 1 && kSub == 1, "prefetched old values cover the single part");
 #pragma unroll
         for (int p = 0; p < PASSES; ++p)
 #pragma unroll
           for (int q = 0; q < V16; ++q) old[p][q] = pre[p][q];
       } else {
-        load_old<Out>(g, m0, n0, h, old);
+        load_old<Out, PASSES>(g, m0, n0, r_part, old);
       }
       __syncthreads();   // the stage buffers (or the previous part) are free
       if (wave_m == h) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int row = i * 32 + (lane & 31);  // within the part
+        for (int ii = 0; ii < TMP; ++ii) {
+          const int i = sub * TMP + ii;
+          const int row = ii * 32 + (lane & 31);  // within the part
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -698,7 +712,7 @@ struct GemmKernel {
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         const int row = p * ROWS_PER_PASS + (threadIdx.x >> 5);
-        const int64_t m = m0 + h * HALF + row;
+        const int64_t m = m0 + r_part + row;
         const uint4 a0 = lds[row * C16 + ((2 * c8) ^ (row & 31))];
         const uint4 a1 = lds[row * C16 + ((2 * c8 + 1) ^ (row & 31))];
         if (m >= g.M || n >= g.N) continue;
@@ -736,7 +750,8 @@ struct GemmKernel {
     }
   }
 
-  static __device__ void run(const GemmArgs& g, int tiles_m, int tiles_n, int group_m) {
+  static __device__ __attribute__((always_inline)) void run(const GemmArgs& g, int tiles_m, int tiles_n,
+                                                           int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -767,7 +782,7 @@ struct GemmKernel {
     constexpr bool kPrefetchOld =
         PRE_OLD && (EPI == kEpiAccumulate || EPI == kEpiAccumulateF32) && WAVES_M == 1;
     uint4 pre_old[kPrefetchOld ? kPasses : 1][sizeof(AccOut) / 2];
-    if constexpr (kPrefetchOld) load_old<AccOut>(g, m0, n0, 0, pre_old);
+    if constexpr (kPrefetchOld) load_old<AccOut, kPasses>(g, m0, n0, 0, pre_old);
 
     if (m0 + BM <= g.M && n0 + BN <= g.N) {
       const int nkf = static_cast<int>((ke - kb) / BK);   // whole K-tiles
