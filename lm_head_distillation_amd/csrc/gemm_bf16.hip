@@ -897,16 +897,13 @@ constexpr int64_t kSkinnyMaxM = 128;
 
 // The accumulating weight-gradient product of a chunk of at most kSkinnyMaxK
 // rows is bound by each tile's serial load / multiply / read-add-write
-// phases; 64-row tiles let two workgroups per CU overlap them (measured on
-// 128256 x 4096 bf16: 0.73 -> 0.46 ms at 32 rows, 1.82 -> 1.69 ms at 1024).
-// The storing first chunk keeps the 256-row tile, faster from 256 rows up.
-constexpr int64_t kSkinnyMaxK = 1024;
-
-// Up to kPrefetchOldMaxK rows the read-add-write loads its old values before
-// the main loop (grad_W at 128256 x 4096: -10% at 32 rows, -8% at 128, -3% at
-// 256); at 1024 rows that measured 3% slower, so longer loops load them at the
-// end.
-constexpr int64_t kPrefetchOldMaxK = 256;
+// phases: 64-row tiles, two workgroups per CU, with the old values loaded
+// before the (short) main loop so that they arrive with the first copies.
+// From 256 rows up the 256-row tiles are faster (grad_W at 128256 x 4096 per
+// pass of 8192 rows: 19.3 -> 18.0 ms at 256-row chunks, 11.3 -> 9.3 ms at
+// 1024; at 1024 rows per pass: 3.24 against 3.63 ms at 128-row chunks,
+// 5.77 against 6.57 at 64, 10.8 against 13.7 at 32).
+constexpr int64_t kSkinnyMaxK = 128;
 
 template <bool A_K, bool B_K, int EPI>
 hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
@@ -915,8 +912,7 @@ hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
     if (g.M <= kSkinnyMaxM && !g.wgrad) return launch_tiles<128, 1, 8, A_K, B_K, EPI>(g, s);
   }
   if constexpr (A_K && B_K && (EPI == kEpiAccumulate || EPI == kEpiAccumulateF32)) {
-    if (g.wgrad && g.K <= kPrefetchOldMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI, true>(g, s);
-    if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI>(g, s);
+    if (g.wgrad && g.K <= kSkinnyMaxK) return launch_tiles<64, 1, 8, A_K, B_K, EPI, true>(g, s);
   }
   return launch_tiles<kGemmBM, kWavesM, kWavesN, A_K, B_K, EPI>(g, s);
 }
