@@ -19,7 +19,8 @@
 // stages. The two waves
 // sharing a SIMD issue the next tile's loads at different K steps, so one
 // keeps the matrix core busy while the other waits for its loads to be
-// accepted. Edge blocks and a partial last K-tile take a bounds-checked
+// accepted; on 256 x 256 tiles the later of the two issues fewer of them.
+// Edge blocks and a partial last K-tile take a bounds-checked
 // register path. Within a stage, each 16-wide K step's fragments are read
 // while the previous step's MFMAs run. Workgroups are renumbered so the tiles
 // one XCD runs together share operand panels in that XCD's L2. Epilogues:
@@ -750,6 +751,9 @@ struct GemmKernel {
     }
   }
 
+  // Always inlined into the kernel: compiled as a call (the inliner's choice
+  // for the largest variants), the body received its arguments through the
+  // stack and read them from scratch memory inside the loops.
   static __device__ __attribute__((always_inline)) void run(const GemmArgs& g, int tiles_m, int tiles_n,
                                                            int group_m) {
     __shared__ uint4 lds[STAGES][LDS_STAGE];
