@@ -21,8 +21,10 @@
 // keeps the matrix core busy while the other waits for its loads to be
 // accepted; on 256 x 256 tiles the later of the two issues fewer of them.
 // Edge blocks and a partial last K-tile take a bounds-checked
-// register path. Within a stage, each 16-wide K step's fragments are read
-// while the previous step's MFMAs run. Workgroups are renumbered so the tiles
+// register path. Within a stage the source reads each 16-wide K step's
+// fragments ahead of the previous step's MFMAs; the compiler moves the reads
+// next to their MFMAs, and the SIMD's other wave covers the LDS latency.
+// Workgroups are renumbered so the tiles
 // one XCD runs together share operand panels in that XCD's L2. Epilogues:
 // store (bf16), fp32 store (split-K partials, fp32 weight gradient), and
 // read-add-write in bf16 or fp32 for the weight gradient of later chunks.
@@ -324,9 +326,10 @@ struct GemmKernel {
     }
   }
 
-  // MFMAs over one LDS stage, with the next K step's fragments read while the
-  // current step's products run. hook(ks) runs before step ks's MFMAs (the
-  // main loops issue the next tile's global loads from it).
+  // MFMAs over one LDS stage, the next K step's fragments requested before
+  // the current step's products (the compiler may still schedule each read
+  // next to its MFMAs). hook(ks) runs before step ks's MFMAs (the main loops
+  // issue the next tile's global loads from it).
   template <class Hook>
   static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN],
                                               Hook&& hook) {
