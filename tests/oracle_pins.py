@@ -131,6 +131,20 @@ def pin_kl_endpoints_library(o):
         assert np.allclose(rev, _kl_rows(Q, P), rtol=1e-10, atol=1e-14), "beta=1 != KL(Q||P)"
 
 
+def pin_jsd_half_library(o):
+    """beta = 1/2 is the symmetric Jensen-Shannon divergence: the square of
+    scipy's Jensen-Shannon distance (natural log), per row, at two temperatures."""
+    from scipy.spatial.distance import jensenshannon
+    zs = _logits(41, 5, 37, 2.0)
+    zt = _logits(42, 5, 37, 2.0)
+    for T in (1.0, 2.0):
+        Q = sps.softmax(zs / T, axis=-1)
+        P = sps.softmax(zt / T, axis=-1)
+        ref = jensenshannon(P, Q, axis=-1) ** 2
+        got, _ = o.generalized_jsd(zs, zt, 0.5, T, "none")
+        assert np.allclose(got, ref, rtol=1e-9, atol=1e-15), f"beta=0.5 != JS distance^2 (T={T})"
+
+
 def pin_kl_limits(o):
     """JSD_b / b -> KL(P||Q) as b -> 0 and JSD_b / (1-b) -> KL(Q||P) as b -> 1."""
     zs = _logits(11, 3, 20, 1.5)
@@ -498,6 +512,7 @@ ALL_PINS = [
     pin_bounds,
     pin_role_swap,
     pin_kl_endpoints_library,
+    pin_jsd_half_library,
     pin_kl_limits,
     pin_finite_differences_logits,
     pin_finite_differences_fused,
