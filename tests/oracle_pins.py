@@ -145,6 +145,23 @@ def pin_jsd_half_library(o):
         assert np.allclose(got, ref, rtol=1e-9, atol=1e-15), f"beta=0.5 != JS distance^2 (T={T})"
 
 
+def pin_jsd_entropy_identity(o):
+    """For every beta, JSD_beta = H(M) - beta H(P) - (1-beta) H(Q) with
+    M = beta P + (1-beta) Q (Shannon entropies from scipy.stats.entropy): the
+    entropy form of the divergence, independent of the KL-sum definition."""
+    from scipy.stats import entropy
+    zs = _logits(43, 6, 29, 2.0)
+    zt = _logits(44, 6, 29, 2.0)
+    for T in (1.0, 1.7):
+        Q = sps.softmax(zs / T, axis=-1)
+        P = sps.softmax(zt / T, axis=-1)
+        for beta in (0.1, 0.3, 0.7, 0.9):
+            M = beta * P + (1.0 - beta) * Q
+            ref = entropy(M, axis=-1) - beta * entropy(P, axis=-1) - (1.0 - beta) * entropy(Q, axis=-1)
+            got, _ = o.generalized_jsd(zs, zt, beta, T, "none")
+            assert np.allclose(got, ref, rtol=1e-9, atol=1e-14), f"entropy identity beta={beta} T={T}"
+
+
 def pin_kl_limits(o):
     """JSD_b / b -> KL(P||Q) as b -> 0 and JSD_b / (1-b) -> KL(Q||P) as b -> 1."""
     zs = _logits(11, 3, 20, 1.5)
@@ -513,6 +530,7 @@ ALL_PINS = [
     pin_role_swap,
     pin_kl_endpoints_library,
     pin_jsd_half_library,
+    pin_jsd_entropy_identity,
     pin_kl_limits,
     pin_finite_differences_logits,
     pin_finite_differences_fused,
