@@ -313,6 +313,18 @@ def pin_logprob_kl_library(o):
     rev, _ = o.jsd_logprob(logq, logp, 1.0, "none")
     assert np.allclose(fwd, _kl_rows(P, Q), rtol=1e-10, atol=1e-14), "logprob beta=0 != KL(P||Q)"
     assert np.allclose(rev, _kl_rows(Q, P), rtol=1e-10, atol=1e-14), "logprob beta=1 != KL(Q||P)"
+    # beta = 1/2: the square of scipy's Jensen-Shannon distance; other betas:
+    # the entropy form H(M) - beta H(P) - (1-beta) H(Q).
+    from scipy.spatial.distance import jensenshannon
+    from scipy.stats import entropy
+    half, _ = o.jsd_logprob(logq, logp, 0.5, "none")
+    assert np.allclose(half, jensenshannon(P, Q, axis=-1) ** 2, rtol=1e-9, atol=1e-15), \
+        "logprob beta=0.5 != JS distance^2"
+    for beta in (0.2, 0.8):
+        M = beta * P + (1.0 - beta) * Q
+        ref = entropy(M, axis=-1) - beta * entropy(P, axis=-1) - (1.0 - beta) * entropy(Q, axis=-1)
+        got, _ = o.jsd_logprob(logq, logp, beta, "none")
+        assert np.allclose(got, ref, rtol=1e-9, atol=1e-14), f"logprob entropy identity beta={beta}"
 
 
 def pin_logprob_disjoint_closed_form(o):
