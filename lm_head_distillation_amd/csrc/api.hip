@@ -467,6 +467,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   ja.mode = mode_for(beta);
   ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
+  ja.peak = reinterpret_cast<float4*>(ws + plan.off_peak);
 
   const char* Xs = static_cast<const char*>(X_s);
   const char* Xt = static_cast<const char*>(X_t);
@@ -565,6 +566,7 @@ FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_
   ja.mode = mode_for(beta);
   ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
+  ja.peak = reinterpret_cast<float4*>(ws + plan.off_peak);
   ja.row_loss = row_loss;
   rc = run_jsd_passes(ja, dtype, grad_logits_s != nullptr, V, dtype_size(dtype), s);
   if (rc != FLJSD_OK) return rc;

@@ -151,26 +151,44 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
   const float4 L = row_log_norms(a, row);
   const float k = a.k2;
-  float lsum = 0.f, gsum = 0.f;
+  // fp32 rows also sum Q, P and g over the elements below the student's
+  // maximum and count the elements at it, for pass 3's peak rewrite.
+  constexpr bool kPeak = sizeof(T) == 4;
+  float lsum = 0.f, gsum = 0.f, qrest = 0.f, prest = 0.f, grest = 0.f, npeak = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8];
     load8(zs, v, n, a.vec_ok, ys);
     load8(zt, v, n, a.vec_ok, yt);
     // Columns past the row end load as -inf in both rows: Q = P = 0, an exact
-    // tie, which adds exactly 0 to both sums, so no per-element mask is needed.
+    // tie, which adds exactly 0 to every sum, so no per-element mask is needed.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
       jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
       lsum += l;
       gsum += gacc;
+      if constexpr (kPeak) {
+        const bool rest = ys[i] < L.x;
+        qrest += rest ? Q : 0.f;
+        prest += rest ? P : 0.f;
+        grest += rest ? g : 0.f;
+        npeak += rest ? 0.f : 1.f;
+      }
     }
   }
   lsum = wave_sum(lsum);
   gsum = wave_sum(gsum);
   __shared__ float2 sh[kWaves];
+  __shared__ float4 sh_pk[kWaves];
   const int wave = threadIdx.x / 64;
+  if constexpr (kPeak) {
+    qrest = wave_sum(qrest);
+    prest = wave_sum(prest);
+    grest = wave_sum(grest);
+    npeak = wave_sum(npeak);
+    if ((threadIdx.x & 63) == 0) sh_pk[wave] = make_float4(qrest, prest, grest, npeak);
+  }
   if ((threadIdx.x & 63) == 0) sh[wave] = make_float2(lsum, gsum);
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -180,6 +198,16 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
       acc.y += sh[w].y;
     }
     a.lg[row * a.S + s] = acc;
+    if (kPeak && a.peak != nullptr) {
+      float4 pk = sh_pk[0];
+      for (int w = 1; w < kWaves; ++w) {
+        pk.x += sh_pk[w].x;
+        pk.y += sh_pk[w].y;
+        pk.z += sh_pk[w].z;
+        pk.w += sh_pk[w].w;
+      }
+      a.peak[row * a.S + s] = pk;
+    }
   }
 }
 
@@ -194,7 +222,9 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   T* gr = static_cast<T*>(a.grad) + row * a.ld;
   const float4 L = row_log_norms(a, row);
   const float k = a.k2;
+  constexpr bool kPeak = sizeof(T) == 4;
   __shared__ float sh_G;
+  __shared__ float4 sh_pk;
   if (threadIdx.x == 0) {
     const float2* lg = a.lg + row * a.S;
     float2 acc = lg[0];
@@ -204,9 +234,38 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
     }
     sh_G = acc.y;
     if (s == 0) a.row_loss[row] = acc.x * a.row_scale;
+    if constexpr (kPeak) {
+      float4 pk = make_float4(0.f, 0.f, 0.f, 0.f);  // n = 0: no rewrite
+      if (a.peak != nullptr) {
+        const float4* pp = a.peak + row * a.S;
+        pk = pp[0];
+        for (int j = 1; j < a.S; ++j) {
+          pk.x += pp[j].x;
+          pk.y += pp[j].y;
+          pk.z += pp[j].z;
+          pk.w += pp[j].w;
+        }
+      }
+      sh_pk = pk;
+    }
   }
   __syncthreads();
   const float G = sh_G;
+  // Peak rewrite (fp32): when the student's row has one dominant element p
+  // with Q_p near 1, g_p - Q_p G = g_p (1 - Q_p) - Q_p G_rest, and 1 - Q_p
+  // computed from the rounded Q_p keeps only ~1e-7 / (1 - Q_p) relative
+  // accuracy. Summing the other elements instead, 1 - Q_p = Q_rest exactly
+  // (the Q sum to one), so the peak's gradient is g_p Q_rest - Q_p G_rest with
+  // G_rest the sum of g over the other elements, and for the forward KL
+  // Q_p - P_p = P_rest - Q_rest. Reverse KL's G (the row loss) equals the sum
+  // of g = -Q D, so it takes the generalized form. The sums carry the
+  // normalizers' rounding as a relative error, as Q_p and P_p do, so the
+  // rewrite is taken only where its terms are the smaller ones: Q_rest < 1/2,
+  // and for the forward KL Q_rest + P_rest < 1 (below Q_p + P_p). With a tied
+  // maximum no element dominates and the plain form stays.
+  const float4 pk = kPeak ? sh_pk : make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool rewrite = kPeak && pk.w == 1.f &&
+                       (MODE == kModeForwardKL ? pk.x + pk.y < 1.f : pk.x < 0.5f);
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8], out[8];
@@ -216,7 +275,9 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
       jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
-      const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+      float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+      if (rewrite && ys[i] == L.x)
+        dA = (MODE == kModeForwardKL) ? (pk.y - pk.x) : (g * pk.x - Q * pk.z);
       out[i] = dA * a.grad_scale;
     }
     store8(gr, v, n, a.vec_ok, out);

@@ -27,6 +27,9 @@ struct JsdArgs {
   int mode = kModeGeneralized;
   float4* stats = nullptr;      // [rows * S] partial (m_s, d_s, m_t, d_t), base 2
   float2* lg = nullptr;         // [rows * S] partial (loss, dX_sum)
+  // [rows * S] fp32 inputs only: partial (Q_rest, P_rest, g_rest, n) over the
+  // row's elements below / at the student's maximum logit (see jsd_grad_kernel)
+  float4* peak = nullptr;
   float* row_loss = nullptr;    // [rows] per-row loss out
   float row_scale = 1.f;        // multiplies the per-row losses (T^2 when asked)
 };

@@ -55,10 +55,10 @@ def _run(fl, dev, beta, T, reduction, nc, **kw):
     return loss, gX, gW
 
 
-def _compare(dtype, got, ref):
+def _compare(dtype, got, ref, tol=None):
     loss, gX, gW = got
     rl, rX, rW = ref
-    tol = TOL[dtype]
+    tol = TOL[dtype] if tol is None else tol
     e0 = assert_loss_close(from_device(loss), rl, tol)
     e1 = assert_tensor_close(from_device(gX), rX, tol, "grad_input")
     e2 = assert_tensor_close(from_device(gW), rW, tol, "grad_weight")
@@ -74,6 +74,44 @@ def test_tiny_f32(fl, beta, T, reduction, nc):
     w, inp = _inputs("tiny_f32")
     got = _run(fl, _device_inputs(inp, "f32"), beta, T, reduction, nc)
     _compare("f32", got, _oracle("tiny_f32", beta, T, reduction))
+
+
+def _scaled(inp, dtype, factor):
+    """The inputs with both hidden-state matrices times a power of two (exact in
+    fp32 and bf16), so the logits, and what the temperature makes of them, are
+    far from the default workloads' small values."""
+    out = dict(inp)
+    for k in ("X_s", "X_t"):
+        if dtype == "f32":
+            out[k] = (inp[k] * np.float32(factor)).astype(np.float32)
+        else:
+            out[k] = workloads.f32_to_bf16_bits(workloads.bf16_bits_to_f32(inp[k]) * np.float32(factor))
+    return out
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 0.9, 1.0])
+@pytest.mark.parametrize("T", [0.25, 0.5, 4.0])
+def test_temperature_extremes_f32(fl, beta, T):
+    """8 x 64 x 512 fp32 with 8x hidden states (logit std ~1.2): at T = 0.25
+    the rows are close to one-hot (std of z / T ~4.9), at T = 4 nearly flat;
+    all at the 1e-5 bar."""
+    w, inp = _inputs("tiny_f32")
+    inp = _scaled(inp, "f32", 8.0)
+    got = _run(fl, _device_inputs(inp, "f32"), beta, T, "batchmean", 1)
+    _compare("f32", got, _oracle_of(inp, "f32", beta, T, "batchmean"))
+
+
+@pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])
+@pytest.mark.parametrize("T", [0.5, 4.0])
+def test_temperature_extremes_bf16(fl, beta, T):
+    """64 x 256 x 5003 bf16 with 8x hidden states, two chunks. The logits are
+    stored in bf16, and a rounding error dz of a logit moves the distribution
+    as dz / T does, so below T = 1 the bf16 bounds widen by 1 / T."""
+    inp = _scaled(_adhoc(31, 64, 256, 256, 5003, "bf16"), "bf16", 8.0)
+    got = _run(fl, _device_inputs(inp, "bf16"), beta, T, "batchmean", 2)
+    f = max(1.0, 1.0 / T)
+    tol = {k: v * f for k, v in TOL["bf16"].items()}
+    _compare("bf16", got, _oracle_of(inp, "bf16", beta, T, "batchmean"), tol)
 
 
 @pytest.mark.parametrize("beta", [0.1, 0.5, 0.9])

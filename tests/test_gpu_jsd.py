@@ -148,3 +148,25 @@ def test_single_vocab_entry(fl, dtype, beta):
     assert not np.any(ref_loss) and not np.any(ref_grad)
     loss, grad, _ = _run(fl, zs, zt, 1, dtype, beta, 2.0, "none")
     assert np.all(from_device(loss) == 0.0) and int(torch.count_nonzero(grad)) == 0
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 0.9, 1.0])
+def test_peaked_rows_f32(fl, beta):
+    """Student rows with one dominant logit (1 - Q_peak from about 1e-2 down to
+    1e-7), the teacher peaked at the same column or another one, and two rows
+    whose maximum is tied at two columns, over several slices with a ragged
+    tail: the dominant element's gradient keeps the fp32 bar."""
+    BT, V = 12, 40997
+    zs, _ = _logits(61, BT, V, 1.0, "f32")
+    zt, _ = _logits(62, BT, V, 1.0, "f32")
+    cols = [0, 17, V // 2, V - 1]
+    for r in range(BT):
+        c = cols[r % 4]
+        zs[r, c] = np.float32(16 + r)
+        zt[r, c if r % 2 == 0 else cols[(r + 1) % 4]] = np.float32(14 + r)
+    for r in (10, 11):   # the maximum tied at two columns
+        zs[r, cols[(r + 2) % 4]] = zs[r, cols[r % 4]]
+    loss, grad, _ = _run(fl, zs, zt, V, "f32", beta, 1.0, "sum")
+    ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, "f32"), to_f64(zt, "f32"), beta, 1.0, "sum")
+    assert_loss_close(from_device(loss), ref_loss, TIGHT["f32"])
+    assert_tensor_close(from_device(grad), ref_grad, TIGHT["f32"], "grad")
