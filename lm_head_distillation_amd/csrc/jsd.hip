@@ -16,9 +16,10 @@
 //
 // Per element, with Q = 2^a_s (student), P = 2^a_t (teacher) and
 // D = ln P - ln Q = (a_t - a_s) ln 2:
-//   generalized: r = ln(beta e^D + 1 - beta), evaluated as
+//   generalized: r = ln(beta e^D + 1 - beta), evaluated for fp32 logits as
 //                  D <  0: log1p(beta expm1(D))
 //                  D >= 0: D + log1p((1-beta) expm1(-D))
+//                (bf16 logits: the direct form described at jsd_terms)
 //                ln(P/M) = D - r, ln(Q/M) = -r,
 //                l = beta P (D - r) - (1-beta) Q r,   g = -(1-beta) Q r,
 //                dA = g - Q G with G = sum_v g (dX_sum)
@@ -55,7 +56,15 @@ constexpr int kWaves = kThreads / 64;
 // Per-element terms of the divergence; see the file comment. Inputs are the
 // log2 probabilities a_s, a_t. Outputs: Q and P, the loss term l, the
 // gradient term g (dA = g - Q G) and gacc, the term summed into G.
-template <int MODE>
+//
+// DIRECT (bf16 logits): the generalized branch evaluates
+// r = ln(beta e^D + 1 - beta) as ln u plus max(D, 0), with
+// u = c e^(-|D|) + 1 - c (c = beta for D < 0, else 1 - beta) in [min(beta,
+// 1 - beta), 1], from one hardware exponential and one hardware log2 instead
+// of the expm1 and log1p series. Rounding u near 1 costs r an absolute ~4e-8;
+// a bf16 logit's own rounding moves D by up to 2^-9 |z| / T, far more, so the
+// series' extra accuracy is kept for fp32 logits only.
+template <int MODE, bool DIRECT = false>
 __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float& P, float& l,
                                  float& g, float& gacc) {
   Q = hw_exp2(as);
@@ -79,8 +88,12 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
   } else {
     // One expm1 of -|D| and one log1p serve both signs of D.
     const bool neg = D < 0.f;
-    const float e = expm1_nonpos(-fabsf(D), -fabsf(t));
-    const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
+    const float c = neg ? beta : 1.f - beta;
+    float L1;
+    if constexpr (DIRECT)
+      L1 = hw_log2(fmaf(c, hw_exp2(-fabsf(t)), 1.f - c)) * kLn2;
+    else
+      L1 = log1p_nonpos(c * expm1_nonpos(-fabsf(D), -fabsf(t)));
     const float r = neg ? L1 : D + L1;
     const float dmr = neg ? D - L1 : -L1;
     l = beta * P * dmr - (1.f - beta) * Q * r;
@@ -165,7 +178,8 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
-      jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
+      jsd_terms<MODE, sizeof(T) == 2>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta,
+                                      Q, P, l, g, gacc);
       lsum += l;
       gsum += gacc;
       if constexpr (kPeak) {
@@ -274,7 +288,8 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
-      jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g, gacc);
+      jsd_terms<MODE, sizeof(T) == 2>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta,
+                                      Q, P, l, g, gacc);
       float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
       if (rewrite && ys[i] == L.x)
         dA = (MODE == kModeForwardKL) ? (pk.y - pk.x) : (g * pk.x - Q * pk.z);
@@ -481,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           float Q, P, l, g, gacc;
-          jsd_terms<MODE>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
+          jsd_terms<MODE, true>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
                           gacc);
           const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
           out[i] = dA * a.grad_scale;

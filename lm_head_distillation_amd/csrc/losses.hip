@@ -11,7 +11,8 @@
 //                            l = beta P (D - r) - (1-beta) Q r,  g = -(1-beta) Q r
 //    with g = dl/dx, elementwise (no softmax chain rule: the inputs are the
 //    variables). r uses the same small-argument expm1 / log1p as the logit
-//    path. An exact tie P == Q gives l = 0 and, in the generalized branch,
+//    path for fp32 inputs and, like it, the direct ln(c e^-|D| + 1 - c) for
+//    bf16 inputs, whose own rounding (2^-9 |x|) outweighs the difference. An exact tie P == Q gives l = 0 and, in the generalized branch,
 //    g = 0 (PR #1374); zero-probability factors contribute 0 (0 log 0 = 0).
 //
 //  * Total variation distance (PR #1374 "Fix TVD gradient at p == q"):
@@ -30,7 +31,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.44269504088896341f;
 
-template <int MODE>
+template <int MODE, bool DIRECT>
 __device__ inline void logprob_terms(float x, float y, float beta, float& l, float& g) {
   const float Q = hw_exp2(x * kLog2e);
   const float P = hw_exp2(y * kLog2e);
@@ -49,8 +50,12 @@ __device__ inline void logprob_terms(float x, float y, float beta, float& l, flo
     g = Q - qd;
   } else {
     const bool neg = D < 0.f;
-    const float e = expm1_nonpos(-fabsf(D), -fabsf(D) * kLog2e);
-    const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
+    const float c = neg ? beta : 1.f - beta;
+    float L1;
+    if constexpr (DIRECT)
+      L1 = hw_log2(fmaf(c, hw_exp2(-fabsf(D) * kLog2e), 1.f - c)) * kLn2;
+    else
+      L1 = log1p_nonpos(c * expm1_nonpos(-fabsf(D), -fabsf(D) * kLog2e));
     const float r = neg ? L1 : D + L1;
     const float dmr = neg ? D - L1 : -L1;
     const float tp = P > 0.f ? beta * P * dmr : 0.f;
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void logprob_jsd_kernel(ElemArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float l, g;
-      logprob_terms<MODE>(x[i], y[i], a.beta, l, g);
+      logprob_terms<MODE, sizeof(T) == 2>(x[i], y[i], a.beta, l, g);
       lsum += l;
       out[i] = g * a.grad_scale;
     }
