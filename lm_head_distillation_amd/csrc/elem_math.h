@@ -134,6 +134,30 @@ __device__ inline float log1p_nonpos(float x) {
   return x >= -0.25f ? series : hw_log2(1.f + x) * kLn2;
 }
 
+// r = ln(beta e^D + 1 - beta) and D - r for 0 < beta < 1, from bf16 inputs;
+// t = D / ln 2. Away from D = 0, r = ln u + max(D, 0) with
+// u = c e^(-|D|) + 1 - c (c = beta for D < 0, else 1 - beta): u lies in
+// [min(beta, 1 - beta), 1], so nothing overflows, and rounding u costs r an
+// absolute ~4e-8. Near D = 0, where that would be a large relative error of a
+// small r, r is r(D)'s Taylor series instead: r is the cumulant generating
+// function of a Bernoulli(beta) variable, so the coefficient of D^n / n! is
+// that variable's n-th cumulant. The series runs to degree 4 below |D| = 1/16
+// (truncation below 1.3e-7 relative there).
+__device__ inline void jsd_r_direct(float D, float t, float beta, float& r, float& dmr) {
+  const bool neg = D < 0.f;
+  const float e = hw_exp2(-fabsf(t));
+  const float L1 = hw_log2(neg ? fmaf(beta, e, 1.f - beta) : fmaf(1.f - beta, e, beta)) * kLn2;
+  const float v = beta * (1.f - beta);  // the Bernoulli variance
+  float p = v * (1.f - 6.f * v) * (1.f / 24.f);
+  p = fmaf(p, D, v * (1.f - 2.f * beta) * (1.f / 6.f));
+  p = fmaf(p, D, 0.5f * v);
+  p = fmaf(p, D, beta);
+  const float rs = p * D;
+  const bool small = fabsf(D) < 0.0625f;
+  r = small ? rs : (neg ? L1 : D + L1);
+  dmr = small ? D - rs : (neg ? D - L1 : -L1);
+}
+
 // D e^D - expm1(D) for |D| < 1/4: sum over k >= 2 of (k-1) D^k / k!.
 __device__ inline float kl_fwd_series(float D) {
   float p = 1.f / 5760.f;

@@ -11,8 +11,8 @@
 //                            l = beta P (D - r) - (1-beta) Q r,  g = -(1-beta) Q r
 //    with g = dl/dx, elementwise (no softmax chain rule: the inputs are the
 //    variables). r uses the same small-argument expm1 / log1p as the logit
-//    path for fp32 inputs and, like it, the direct ln(c e^-|D| + 1 - c) for
-//    bf16 inputs, whose own rounding (2^-9 |x|) outweighs the difference. An exact tie P == Q gives l = 0 and, in the generalized branch,
+//    path for fp32 inputs and, like it, jsd_r_direct for bf16 inputs, whose
+//    own rounding (2^-9 |x|) outweighs the difference. An exact tie P == Q gives l = 0 and, in the generalized branch,
 //    g = 0 (PR #1374); zero-probability factors contribute 0 (0 log 0 = 0).
 //
 //  * Total variation distance (PR #1374 "Fix TVD gradient at p == q"):
@@ -49,15 +49,16 @@ __device__ inline void logprob_terms(float x, float y, float beta, float& l, flo
     l = -qd;
     g = Q - qd;
   } else {
-    const bool neg = D < 0.f;
-    const float c = neg ? beta : 1.f - beta;
-    float L1;
-    if constexpr (DIRECT)
-      L1 = hw_log2(fmaf(c, hw_exp2(-fabsf(D) * kLog2e), 1.f - c)) * kLn2;
-    else
-      L1 = log1p_nonpos(c * expm1_nonpos(-fabsf(D), -fabsf(D) * kLog2e));
-    const float r = neg ? L1 : D + L1;
-    const float dmr = neg ? D - L1 : -L1;
+    float r, dmr;
+    if constexpr (DIRECT) {
+      jsd_r_direct(D, D * kLog2e, beta, r, dmr);
+    } else {
+      const bool neg = D < 0.f;
+      const float e = expm1_nonpos(-fabsf(D), -fabsf(D) * kLog2e);
+      const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
+      r = neg ? L1 : D + L1;
+      dmr = neg ? D - L1 : -L1;
+    }
     const float tp = P > 0.f ? beta * P * dmr : 0.f;
     const float tq = Q > 0.f ? (1.f - beta) * Q * r : 0.f;
     l = tp - tq;
