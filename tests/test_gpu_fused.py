@@ -91,13 +91,14 @@ def _scaled(inp, dtype, factor):
 
 @pytest.mark.parametrize("beta", [0.0, 0.1, 0.5, 0.9, 1.0])
 @pytest.mark.parametrize("T", [0.25, 0.5, 4.0])
-def test_temperature_extremes_f32(fl, beta, T):
+@pytest.mark.parametrize("nc", [1, 3])
+def test_temperature_extremes_f32(fl, beta, T, nc):
     """8 x 64 x 512 fp32 with 8x hidden states (logit std ~1.2): at T = 0.25
     the rows are close to one-hot (std of z / T ~4.9), at T = 4 nearly flat;
-    all at the 1e-5 bar."""
+    all at the 1e-5 bar, in one chunk and in three (ragged: 3 + 3 + 2 rows)."""
     w, inp = _inputs("tiny_f32")
     inp = _scaled(inp, "f32", 8.0)
-    got = _run(fl, _device_inputs(inp, "f32"), beta, T, "batchmean", 1)
+    got = _run(fl, _device_inputs(inp, "f32"), beta, T, "batchmean", nc)
     _compare("f32", got, _oracle_of(inp, "f32", beta, T, "batchmean"))
 
 
