@@ -7,6 +7,7 @@ logits and dZ to the input dtype, which the bf16 tolerances cover.
 from __future__ import annotations
 
 import functools
+import time
 
 import numpy as np
 import pytest
@@ -162,6 +163,30 @@ def test_llama3_head_full(fl, llama3_device, nc):
 def large_batch():
     w, inp = _inputs("large_batch")
     return w, inp, _device_inputs(inp, "bf16")
+
+
+@pytest.fixture(scope="module")
+def large_batch_oracle(large_batch):
+    """The oracle over the whole 8192 x 4096 x 128256 workload, once per module
+    (about a minute on 16 host threads, ~20 GB of host memory at its peak)."""
+    w, _inp, _dev = large_batch
+    t0 = time.perf_counter()
+    ref = _oracle("large_batch", w.beta, w.temperature, w.reduction)
+    print(f"large_batch oracle: {time.perf_counter() - t0:.1f} s", flush=True)
+    return ref
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("nc", [1, 8, 32])
+def test_large_batch_full(fl, large_batch, large_batch_oracle, nc):
+    """8192 x 4096 x 128256 bf16, T = 2 (the pages' B*T = 8192 benchmark shape):
+    loss, every grad_input element and every grad_W element against the full
+    oracle, per chunk count."""
+    w, _inp, dev = large_batch
+    print(f"large_batch nc={nc}", flush=True)
+    got = _run(fl, dev, w.beta, w.temperature, w.reduction, nc)
+    _compare("bf16", got, large_batch_oracle)
 
 
 @pytest.mark.slow
