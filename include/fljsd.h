@@ -180,6 +180,35 @@ int fljsd_generalized_jsd(const void* logits_s, const void* logits_t,
                           void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Bytes of the device scratch array behind fljsd_generalized_jsd_noalloc
+ * (8 MiB per GPU the library runs on, held until the process ends). */
+#define FLJSD_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * fljsd_generalized_jsd_noalloc - fljsd_generalized_jsd without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs and results are those of fljsd_generalized_jsd. The
+ * workspace is a file-scope device array of FLJSD_NOALLOC_SCRATCH_BYTES inside
+ * the library, one per GPU, whose address is looked up on the first call on
+ * each device (with that device current). The call allocates nothing (no
+ * hipMalloc, no allocating library routine) and clears nothing: the loss
+ * passes write every scratch byte before they read it.
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * contents in it: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race and give wrong results.
+ * Order them on one stream.
+ * Errors: as fljsd_generalized_jsd; FLJSD_EWORKSPACE (before any HIP call)
+ * when fljsd_generalized_jsd_workspace_size(BT, V, dtype) exceeds
+ * FLJSD_NOALLOC_SCRATCH_BYTES (about 190,000 rows at any V); FLJSD_EHIP when
+ * the scratch address cannot be looked up.
+ */
+int fljsd_generalized_jsd_noalloc(const void* logits_s, const void* logits_t,
+                                  int64_t BT, int64_t V, int64_t ld, int dtype,
+                                  float beta, float temperature, int reduction,
+                                  float* loss, void* grad_logits_s, void* stream);
+
 /*
  * fljsd_jsd_logprob - generalized JSD over given log-probabilities, the
  * log-space contract of the public JSD op (PR #1352, Open question 3), in

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -522,12 +523,15 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   return FLJSD_OK;
 }
 
-FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_t, int64_t BT,
-                                       int64_t V, int64_t ld, int dtype, float beta,
-                                       float temperature, int reduction, float* loss,
-                                       void* grad_logits_s, void* workspace,
-                                       size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+namespace fljsd {
+namespace {
+
+// fljsd_generalized_jsd with the workspace already chosen (the caller's, or
+// the no-allocation entry point's file-scope scratch array).
+// Every check of fljsd_generalized_jsd's arguments except the workspace's.
+int check_generalized_jsd_args(const void* logits_s, const void* logits_t, int64_t BT, int64_t V,
+                               int64_t ld, int dtype, float beta, float temperature,
+                               int reduction, const float* loss, const void* grad_logits_s) {
   if (!logits_s || !logits_t || !loss)
     return fail(FLJSD_EINVAL, "logits_s, logits_t and loss must not be NULL");
   if (BT <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT and V must be > 0");
@@ -535,9 +539,21 @@ FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_
   if (ld < V) return fail(FLJSD_EINVAL, "ld must be >= V");
   int rc = check_common(dtype, beta, temperature, reduction);
   if (rc != FLJSD_OK) return rc;
-  const void* ptrs[] = {logits_s, logits_t, loss, grad_logits_s, workspace};
+  const void* ptrs[] = {logits_s, logits_t, loss, grad_logits_s};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
+  return FLJSD_OK;
+}
+
+int generalized_jsd_impl(const void* logits_s, const void* logits_t, int64_t BT, int64_t V,
+                         int64_t ld, int dtype, float beta, float temperature, int reduction,
+                         float* loss, void* grad_logits_s, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  int rc = check_generalized_jsd_args(logits_s, logits_t, BT, V, ld, dtype, beta, temperature,
+                                      reduction, loss, grad_logits_s);
+  if (rc != FLJSD_OK) return rc;
+  if (workspace && !aligned16(workspace))
+    return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
   const JsdPlan plan = plan_jsd(BT, V);
   if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
   if (workspace_bytes < plan.total)
@@ -576,6 +592,80 @@ FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_
     if (e != hipSuccess) return fail_hip(e, "launch loss reduce");
   }
   return FLJSD_OK;
+}
+
+}  // namespace
+}  // namespace fljsd
+
+// ---- scratch of the no-allocation entry point -------------------------------
+// One file-scope device array per GPU (each device that loads the library
+// holds its own copy until the process ends). In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address is looked
+// up once per device with hipGetSymbolAddress and only that address is used.
+// The loss passes write every byte they later read (row statistics, per-slice
+// partial sums, row losses), so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[FLJSD_NOALLOC_SCRATCH_BYTES];
+
+namespace fljsd {
+namespace {
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call per device, with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLJSD_EDEVICE, "device index out of range");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+      if (p == nullptr) return fail(FLJSD_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FLJSD_OK;
+}
+
+}  // namespace
+}  // namespace fljsd
+
+FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_t, int64_t BT,
+                                       int64_t V, int64_t ld, int dtype, float beta,
+                                       float temperature, int reduction, float* loss,
+                                       void* grad_logits_s, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  return generalized_jsd_impl(logits_s, logits_t, BT, V, ld, dtype, beta, temperature, reduction,
+                              loss, grad_logits_s, workspace, workspace_bytes, stream);
+}
+
+FLJSD_EXPORT int fljsd_generalized_jsd_noalloc(const void* logits_s, const void* logits_t,
+                                               int64_t BT, int64_t V, int64_t ld, int dtype,
+                                               float beta, float temperature, int reduction,
+                                               float* loss, void* grad_logits_s, void* stream) {
+  g_last_error.clear();
+  // Arguments and the scratch bound are checked before any HIP call.
+  int rc = check_generalized_jsd_args(logits_s, logits_t, BT, V, ld, dtype, beta, temperature,
+                                      reduction, loss, grad_logits_s);
+  if (rc != FLJSD_OK) return rc;
+  const size_t need = plan_jsd(BT, V).total;
+  if (need > FLJSD_NOALLOC_SCRATCH_BYTES)
+    return fail(FLJSD_EWORKSPACE, "this shape needs " + std::to_string(need) +
+                                      " bytes of scratch; the no-allocation entry point holds " +
+                                      std::to_string(static_cast<size_t>(FLJSD_NOALLOC_SCRATCH_BYTES)));
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FLJSD_OK) return rc;
+  return generalized_jsd_impl(logits_s, logits_t, BT, V, ld, dtype, beta, temperature, reduction,
+                              loss, grad_logits_s, ws, FLJSD_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 namespace fljsd {

@@ -59,6 +59,9 @@ def load_library() -> ctypes.CDLL:
     lib.fljsd_generalized_jsd.argtypes = [vp, vp, i64, i64, i64, cint, f32, f32, cint, vp, vp,
                                           vp, sz, vp]
     lib.fljsd_generalized_jsd.restype = cint
+    lib.fljsd_generalized_jsd_noalloc.argtypes = [vp, vp, i64, i64, i64, cint, f32, f32, cint,
+                                                  vp, vp, vp]
+    lib.fljsd_generalized_jsd_noalloc.restype = cint
     lib.fljsd_jsd_logprob.argtypes = [vp, vp, i64, i64, i64, cint, f32, cint, vp, vp, vp, sz, vp]
     lib.fljsd_jsd_logprob.restype = cint
     lib.fljsd_tvd.argtypes = [vp, vp, i64, i64, i64, cint, cint, vp, vp, vp, sz, vp]
@@ -118,6 +121,19 @@ def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def _check_out(t: torch.Tensor, dtype: torch.dtype, numel: int, device, what: str) -> None:
+    """A caller-supplied output: its dtype, element count, device and layout
+    must be what the library writes, or the kernels would write past it."""
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{what} must hold {numel} elements, got {t.numel()}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{what} must live on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
 
 
 def _require_device(*tensors: torch.Tensor) -> None:
@@ -271,6 +287,32 @@ def fljsd_generalized_jsd(logits_s: torch.Tensor, logits_t: torch.Tensor, beta: 
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc)
     return (loss if red == 3 else loss[0]), grad
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def fljsd_generalized_jsd_noalloc(logits_s: torch.Tensor, logits_t: torch.Tensor, beta: float,
+                                  temperature: float, reduction: str = "batchmean", *,
+                                  loss: torch.Tensor, grad: Optional[torch.Tensor] = None,
+                                  stream=None):
+    """fljsd_generalized_jsd through the entry point that allocates nothing:
+    the caller passes the outputs (``loss``: 1 fp32 value, or BT for "none";
+    ``grad`` shaped and strided like logits_s, may be logits_s itself, or None)
+    and the library uses its per-GPU scratch array. Calls that overlap on one
+    GPU race. Returns (loss, grad)."""
+    lib = load_library()
+    dt, BT, V, ld = _pair_2d(logits_s, logits_t, "logits")
+    red = _reduction_code(reduction)
+    _check_out(loss, torch.float32, BT if red == 3 else 1, logits_s.device, "loss")
+    if grad is not None and (grad.dtype != logits_s.dtype or grad.shape != logits_s.shape
+                             or grad.stride() != logits_s.stride() or grad.device != logits_s.device):
+        raise ValueError("grad must match logits_s in dtype, shape, strides and device")
+    rc = lib.fljsd_generalized_jsd_noalloc(
+        logits_s.data_ptr(), logits_t.data_ptr(), BT, V, ld, dt, float(beta), float(temperature),
+        red, loss.data_ptr(), _ptr(grad), _stream(stream))
+    _check(rc)
+    return loss, grad
 
 
 def _pair_2d(a: torch.Tensor, b: torch.Tensor, what: str):

@@ -43,7 +43,8 @@ def test_header_declares_the_entry_points():
               "fljsd_jsd_logprob", "fljsd_tvd", "fljsd_flce_forward_backward",
               "fljsd_flce_workspace_size", "fljsd_flce_plan_num_chunks", "fljsd_workspace_size",
               "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
-              "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read"):
+              "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read",
+              "fljsd_generalized_jsd_noalloc"):
         assert n in names
 
 
@@ -216,6 +217,41 @@ def jsd(lib, **over):
 ])
 def test_generalized_jsd_rejects(lib, over, code):
     assert jsd(lib, **over) == code
+
+
+def jsd_noalloc(lib, **over):
+    a = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
+             loss=FAKE, grad=FAKE, stream=None)
+    a.update(over)
+    return lib.fljsd_generalized_jsd_noalloc(a["zs"], a["zt"], a["BT"], a["V"], a["ld"], a["dtype"],
+                                             a["beta"], a["T"], a["reduction"], a["loss"], a["grad"],
+                                             a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
+    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
+    (dict(grad=FAKE + 2), EALIGN),
+    # Past the 8 MiB scratch array: 400,000 rows need 17.6 MB of row statistics.
+    (dict(BT=400_000, V=1000, ld=1000), EWORKSPACE),
+])
+def test_generalized_jsd_noalloc_rejects(lib, over, code):
+    """The no-allocation entry point checks everything, its scratch bound
+    included, before any HIP call (so these run without a GPU)."""
+    assert jsd_noalloc(lib, **over) == code
+    assert lib.fljsd_last_error()
+
+
+def test_noalloc_scratch_bound_matches_header(lib):
+    text = open(HEADER).read()
+    m = re.search(r"#define FLJSD_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == 8 << 20
+    from lm_head_distillation_amd import fljsd
+    assert fljsd.NOALLOC_SCRATCH_BYTES == 8 << 20
+    # The largest batch of a bf16 / fp32 row stride that fits, and the next one out.
+    assert lib.fljsd_generalized_jsd_workspace_size(190_000, 1000, BF16) <= 8 << 20
+    assert jsd_noalloc(lib, BT=191_000, V=1000, ld=1000) == EWORKSPACE
 
 
 def elem(lib, fn, **over):
