@@ -130,10 +130,15 @@ def _check_out(t: torch.Tensor, dtype: torch.dtype, numel: int, device, what: st
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
     if t.numel() != numel:
         raise ValueError(f"{what} must hold {numel} elements, got {t.numel()}")
-    if not t.is_cuda or t.device != device:
-        raise ValueError(f"{what} must live on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{what} must live on {device}")
+
+
+def _check_workspace(ws: torch.Tensor, device) -> None:
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
 
 
 def _require_device(*tensors: torch.Tensor) -> None:
@@ -142,6 +147,8 @@ def _require_device(*tensors: torch.Tensor) -> None:
             raise ValueError("tensors must live in GPU memory")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if t.device != tensors[0].device:
+            raise ValueError("tensors must live on one device")
 
 
 def fljsd_workspace_size(BT: int, H_s: int, H_t: int, V: int, dtype: int, num_chunks: int) -> int:
@@ -229,8 +236,15 @@ def fljsd_forward_backward_ex(X_s: torch.Tensor, W_s: torch.Tensor, X_t: torch.T
     need = fljsd_workspace_size(BT, H_s, H_t, V, dt, nc)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=X_s.device)
+    if workspace is not None:
+        _check_workspace(workspace, X_s.device)
     if out is not None:
         loss, gX, gW = out
+        _check_out(loss, torch.float32, BT if red == 3 else 1, X_s.device, "loss")
+        if gX is not None:
+            _check_out(gX, X_s.dtype, BT * H_s, X_s.device, "grad_X_s")
+        if gW is not None:
+            _check_out(gW, gw_torch, V * H_s, X_s.device, "grad_W_s")
     else:
         loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X_s.device)
         gX = torch.empty_like(X_s) if grad_input else None
@@ -267,10 +281,13 @@ def fljsd_generalized_jsd(logits_s: torch.Tensor, logits_t: torch.Tensor, beta: 
     ld = logits_s.stride(0)
     if logits_t.shape != (BT, V) or logits_t.stride(0) != ld:
         raise ValueError("logits_t must match logits_s in shape and row stride")
+    if logits_t.device != logits_s.device:
+        raise ValueError("logits must live on one device")
     red = _reduction_code(reduction)
     need = fljsd_generalized_jsd_workspace_size(BT, V, dt)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=logits_s.device)
+    _check_workspace(workspace, logits_s.device)
     loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=logits_s.device)
     if in_place:
         grad = logits_s
@@ -279,8 +296,9 @@ def fljsd_generalized_jsd(logits_s: torch.Tensor, logits_t: torch.Tensor, beta: 
                                    device=logits_s.device)
     elif not want_grad:
         grad = None
-    if grad is not None and (grad.stride() != logits_s.stride() or grad.shape != logits_s.shape):
-        raise ValueError("grad must match logits_s in shape and strides")
+    if grad is not None and (grad.stride() != logits_s.stride() or grad.shape != logits_s.shape
+                             or grad.dtype != logits_s.dtype or grad.device != logits_s.device):
+        raise ValueError("grad must match logits_s in dtype, shape, strides and device")
     rc = lib.fljsd_generalized_jsd(
         logits_s.data_ptr(), logits_t.data_ptr(), BT, V, ld, dt, float(beta), float(temperature),
         red, loss.data_ptr(), _ptr(grad), workspace.data_ptr(),
@@ -326,6 +344,8 @@ def _pair_2d(a: torch.Tensor, b: torch.Tensor, what: str):
     ld = a.stride(0)
     if b.shape != (BT, V) or b.stride(0) != ld:
         raise ValueError(f"{what}: second input must match the first in shape and row stride")
+    if b.device != a.device:
+        raise ValueError(f"{what} must live on one device")
     return dt, BT, V, ld
 
 
@@ -336,8 +356,9 @@ def _grad_like(a: torch.Tensor, grad, in_place: bool, want_grad: bool):
         return None
     if grad is None:
         grad = torch.empty_strided(a.shape, a.stride(), dtype=a.dtype, device=a.device)
-    if grad.stride() != a.stride() or grad.shape != a.shape:
-        raise ValueError("grad must match the input in shape and strides")
+    if (grad.stride() != a.stride() or grad.shape != a.shape or grad.dtype != a.dtype
+            or grad.device != a.device):
+        raise ValueError("grad must match the input in dtype, shape, strides and device")
     return grad
 
 
@@ -353,6 +374,7 @@ def fljsd_jsd_logprob(logq_s: torch.Tensor, logp_t: torch.Tensor, beta: float,
     if workspace is None:
         workspace = torch.empty(fljsd_generalized_jsd_workspace_size(BT, V, dt), dtype=torch.uint8,
                                 device=logq_s.device)
+    _check_workspace(workspace, logq_s.device)
     loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=logq_s.device)
     grad = _grad_like(logq_s, grad, in_place, want_grad)
     rc = lib.fljsd_jsd_logprob(logq_s.data_ptr(), logp_t.data_ptr(), BT, V, ld, dt, float(beta), red,
@@ -373,6 +395,7 @@ def fljsd_tvd(p: torch.Tensor, q: torch.Tensor, reduction: str = "batchmean", *,
     if workspace is None:
         workspace = torch.empty(fljsd_generalized_jsd_workspace_size(BT, V, dt), dtype=torch.uint8,
                                 device=p.device)
+    _check_workspace(workspace, p.device)
     loss = torch.empty((BT, V) if red == 3 else (1,), dtype=torch.float32, device=p.device)
     grad = _grad_like(p, grad, in_place, want_grad)
     rc = lib.fljsd_tvd(p.data_ptr(), q.data_ptr(), BT, V, ld, dt, red, loss.data_ptr(), _ptr(grad),
@@ -419,6 +442,7 @@ def fljsd_flce_forward_backward(X: torch.Tensor, W: torch.Tensor, labels: torch.
     if workspace is None:
         workspace = torch.empty(fljsd_flce_workspace_size(BT, H, V, dt, nc), dtype=torch.uint8,
                                 device=X.device)
+    _check_workspace(workspace, X.device)
     loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X.device)
     gX = torch.empty_like(X) if grad_input else None
     gW = torch.empty_like(W) if grad_weight else None

@@ -342,6 +342,26 @@ def test_binding_rejects_host_tensors(lib):
         fljsd.fljsd_generalized_jsd(w, w, 0.5, 1.0)
 
 
+def test_binding_checks_caller_outputs():
+    """Outputs the caller passes in must be what the kernels write (dtype,
+    element count, layout, device), or the binding refuses them before the
+    library sees a pointer: a bf16 tensor where fp32 grad_W is asked for, a
+    one-element loss for reduction "none", a strided gradient."""
+    import torch
+    from lm_head_distillation_amd import fljsd
+    dev = torch.device("cpu")
+    with pytest.raises(ValueError, match="float32"):
+        fljsd._check_out(torch.empty(16, 8, dtype=torch.bfloat16), torch.float32, 128, dev, "grad_W_s")
+    with pytest.raises(ValueError, match="hold 8 elements"):
+        fljsd._check_out(torch.empty(1, dtype=torch.float32), torch.float32, 8, dev, "loss")
+    with pytest.raises(ValueError, match="contiguous"):
+        fljsd._check_out(torch.empty(8, 16, dtype=torch.float32).t(), torch.float32, 128, dev, "grad")
+    with pytest.raises(ValueError, match="live on"):
+        fljsd._check_out(torch.empty(4, dtype=torch.float32), torch.float32, 4, dev, "loss")
+    with pytest.raises(ValueError, match="contiguous tensor"):
+        fljsd._check_workspace(torch.empty(64, dtype=torch.uint8), dev)
+
+
 def test_binding_fails_loudly_without_library(tmp_path):
     code = ("import lm_head_distillation_amd.fljsd as f; f._LIB_PATH = '/nonexistent/libfljsd.so'\n"
             "try:\n    f.load_library()\nexcept ImportError as e:\n    print('IMPORTERROR', e)\n")

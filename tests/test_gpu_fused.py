@@ -368,3 +368,31 @@ def test_beyond_2g_logit_elements(fl):
     rl = from_device(row_loss)
     assert_loss_close(rl[rows], ref_loss, TOL["bf16"], "per-row loss")
     assert_loss_close(from_device(loss), rl.mean(), {"loss_rel": 1e-5}, "batchmean = mean of rows")
+
+
+def test_binding_rejects_mismatched_outputs(fl):
+    """Caller-supplied outputs whose dtype, size or layout differ from what the
+    kernels write are refused before any launch: an fp32 grad_W asked for into
+    a bf16 tensor, a one-element loss for reduction "none", a gradient tensor
+    of another dtype with the logits' strides."""
+    inp = _adhoc(13, 16, 64, 64, 300, "bf16")
+    dev = _device_inputs(inp, "bf16")
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    gX = torch.empty_like(dev[0])
+    gW_bf16 = torch.empty_like(dev[1])
+    with pytest.raises(ValueError, match="grad_W_s"):
+        fl.fljsd_forward_backward_ex(*dev, 0.5, 1.0, "batchmean", 1, grad_w_dtype=torch.float32,
+                                     out=(loss, gX, gW_bf16))
+    with pytest.raises(ValueError, match="loss"):
+        fl.fljsd_forward_backward(*dev, 0.5, 1.0, "none", 1, out=(loss, gX, gW_bf16))
+    with pytest.raises(ValueError, match="grad_X_s"):
+        fl.fljsd_forward_backward(*dev, 0.5, 1.0, "batchmean", 1,
+                                  out=(loss, gX[:8], gW_bf16))
+    zs = torch.randn(16, 300, device="cuda")
+    zt = torch.randn(16, 300, device="cuda")
+    bad = torch.empty_strided(zs.shape, zs.stride(), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="dtype"):
+        fl.fljsd_generalized_jsd(zs, zt, 0.5, 1.0, grad=bad)
+    with pytest.raises(ValueError, match="dtype"):
+        fl.fljsd_jsd_logprob(zs, zt, 0.5, grad=bad)
+    torch.cuda.synchronize()
