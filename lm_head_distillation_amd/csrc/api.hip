@@ -469,6 +469,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
   ja.peak = reinterpret_cast<float4*>(ws + plan.off_peak);
+  ja.ref = reinterpret_cast<float*>(ws + plan.off_ref);
 
   const char* Xs = static_cast<const char*>(X_s);
   const char* Xt = static_cast<const char*>(X_t);
@@ -583,6 +584,7 @@ int generalized_jsd_impl(const void* logits_s, const void* logits_t, int64_t BT,
   ja.stats = reinterpret_cast<float4*>(ws + plan.off_stats);
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
   ja.peak = reinterpret_cast<float4*>(ws + plan.off_peak);
+  ja.ref = reinterpret_cast<float*>(ws + plan.off_ref);
   ja.row_loss = row_loss;
   rc = run_jsd_passes(ja, dtype, grad_logits_s != nullptr, V, dtype_size(dtype), s);
   if (rc != FLJSD_OK) return rc;

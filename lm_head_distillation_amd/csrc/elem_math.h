@@ -1,6 +1,7 @@
 // fp32 element math shared by the loss kernels: hardware transcendentals,
-// 8-wide row loads and stores with bf16 conversion, wave sums, and the
-// small-argument expm1 / log1p / Bregman-term series of the divergence terms.
+// 8-wide row loads and stores with bf16 conversion, wave sums, expm1 / log1p
+// with full relative accuracy, the mixture log ln(w e^x + 1 - w) built on
+// them, and the Bregman-term series of the KL branches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -101,28 +102,26 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// expm1(w) for w <= 0: Taylor polynomial on (-1/2, 0], 2^(w log2 e) - 1 below.
-// `t` is w / ln 2 (the same value in base 2).
-__device__ inline float expm1_nonpos(float w, float t) {
+// expm1(x) for |x| <= 80, either sign (xt = x / ln 2): the degree-9 Taylor
+// polynomial below |x| = 1/2, 2^xt - 1 beyond (e^x >= 1.65 or <= 0.61 there,
+// so the subtraction costs at most a few ulp).
+__device__ inline float expm1_f32(float x, float xt) {
   float p = 1.f / 362880.f;
-  p = fmaf(p, w, 1.f / 40320.f);
-  p = fmaf(p, w, 1.f / 5040.f);
-  p = fmaf(p, w, 1.f / 720.f);
-  p = fmaf(p, w, 1.f / 120.f);
-  p = fmaf(p, w, 1.f / 24.f);
-  p = fmaf(p, w, 1.f / 6.f);
-  p = fmaf(p, w, 0.5f);
-  p = fmaf(p, w, 1.f);
-  const float poly = p * w;
-  return w > -0.5f ? poly : hw_exp2(t) - 1.f;
+  p = fmaf(p, x, 1.f / 40320.f);
+  p = fmaf(p, x, 1.f / 5040.f);
+  p = fmaf(p, x, 1.f / 720.f);
+  p = fmaf(p, x, 1.f / 120.f);
+  p = fmaf(p, x, 1.f / 24.f);
+  p = fmaf(p, x, 1.f / 6.f);
+  p = fmaf(p, x, 0.5f);
+  p = fmaf(p, x, 1.f);
+  return fabsf(x) < 0.5f ? p * x : hw_exp2(xt) - 1.f;
 }
 
-// log1p(x) for x in (-1, 0]. Near 0 (x >= -1/4): 2 atanh(s) with
-// s = x / (2 + x) in [-1/7, 0], an odd series whose truncation error is below
-// 1e-10 relative; further out, ln(1 + x) from the hardware log2, whose result
-// is then at least 0.41 in magnitude.
-__device__ inline float log1p_nonpos(float x) {
-  const float s = x * hw_rcp(2.f + x);
+// log1p(y) for y >= -1/2: the atanh series for |y| <= 1/4, the hardware log2
+// of 1 + y beyond (1 + y then lies in [1/2, 3/4] or above 5/4).
+__device__ inline float log1p_f32(float y) {
+  const float s = y * hw_rcp(2.f + y);
   const float s2 = s * s;
   float p = 1.f / 11.f;
   p = fmaf(p, s2, 1.f / 9.f);
@@ -130,8 +129,56 @@ __device__ inline float log1p_nonpos(float x) {
   p = fmaf(p, s2, 1.f / 5.f);
   p = fmaf(p, s2, 1.f / 3.f);
   p = fmaf(p, s2, 1.f);
-  const float series = 2.f * s * p;
-  return x >= -0.25f ? series : hw_log2(1.f + x) * kLn2;
+  return fabsf(y) <= 0.25f ? 2.f * s * p : hw_log2(1.f + y) * kLn2;
+}
+
+// Mixture weights of the fp32 gradient terms: for a reference log-ratio
+// D_c = tc ln 2 (tc in base 2), w = beta e^Dc / (beta e^Dc + 1 - beta) and
+// cw = 1 - w, each to full relative accuracy, with lw = ln w and lc = ln cw
+// finite even where w or cw underflows.
+struct MixWeights {
+  float w, cw, lw, lc;
+};
+__device__ inline MixWeights mix_weights(float tc, float beta) {
+  const float cb = 1.f - beta;
+  const bool neg = tc < 0.f;
+  const float E = hw_exp2(-fabsf(tc));
+  const float den = neg ? fmaf(beta, E, cb) : fmaf(cb, E, beta);
+  const float rden = 1.f / den;
+  const float lden = hw_log2(den) * kLn2;
+  const float dabs = fabsf(tc) * kLn2;
+  MixWeights m;
+  m.w = (neg ? beta * E : beta) * rden;
+  m.cw = (neg ? cb : cb * E) * rden;
+  m.lw = hw_log2(beta) * kLn2 - (neg ? dabs : 0.f) - lden;
+  m.lc = hw_log2(cb) * kLn2 - (neg ? 0.f : dabs) - lden;
+  return m;
+}
+
+// rho(x) = ln(w e^x + cw) for the weights above (xt = x / ln 2), with full
+// relative accuracy at every x: log1p(w expm1(x)) while w expm1(x) >= -1/2
+// (no cancellation in the argument or the result), the direct log of the two
+// positive terms below that (the result is then below ln(1/2)), and beyond
+// |x| = 80 the log-sum-exp of ln w + x and ln cw.
+__device__ inline float mix_log(float x, float xt, const MixWeights& m) {
+  const float xc = fminf(fmaxf(x, -80.f), 80.f);
+  const float xtc = fminf(fmaxf(xt, -115.f), 115.f);
+  const float y = m.w * expm1_f32(xc, xtc);
+  const float r_near = y >= -0.5f ? log1p_f32(y) : hw_log2(fmaf(m.w, hw_exp2(xtc), m.cw)) * kLn2;
+  const float s = x + m.lw;
+  const float hi = fmaxf(s, m.lc), lo = fminf(s, m.lc);
+  const float r_far = hi + log1p_f32(hw_exp2((lo - hi) * 1.4426950408889634f));
+  return fabsf(x) > 80.f ? r_far : r_near;
+}
+
+// Weights of the fp32 generalized terms: (beta, 1 - beta) for r = ln(beta
+// e^D + 1 - beta), and the mirrored pair for D - r = -ln((1 - beta) e^-D +
+// beta), both evaluated by mix_log.
+struct BetaWeights {
+  MixWeights r, dmr;
+};
+__device__ inline BetaWeights beta_weights(float beta) {
+  return {mix_weights(0.f, beta), mix_weights(0.f, 1.f - beta)};
 }
 
 // r = ln(beta e^D + 1 - beta) and D - r for 0 < beta < 1, from bf16 inputs;
@@ -184,7 +231,10 @@ __device__ inline float kl_rev_series(float D) {
 
 // Merge of two (max, denominator) pairs; maxima in logit units, denominators
 // in base 2 with scale k. Commutative bit for bit (max and a two-term IEEE
-// sum are), so both butterfly partners agree.
+// sum are), so both butterfly partners agree. The multiply-adds are written
+// as explicit fmaf: the compiler may otherwise contract either product into
+// the sum, differently at different call sites, and equal inputs (a teacher
+// identical to the student) must give bit-identical statistics.
 __device__ inline void md_merge(float& m, float& d, float mo, float dof, float k) {
   const float M = fmaxf(m, mo);
   if (M == -INFINITY) {
@@ -192,7 +242,9 @@ __device__ inline void md_merge(float& m, float& d, float mo, float dof, float k
     d = 0.f;
     return;
   }
-  d = d * hw_exp2((m - M) * k) + dof * hw_exp2((mo - M) * k);
+  const float a = d * hw_exp2((m - M) * k);
+  const float b = dof * hw_exp2((mo - M) * k);
+  d = fmaxf(a, b) + fminf(a, b);
   m = M;
 }
 
@@ -202,14 +254,12 @@ __device__ inline void md_update8(float& m, float& d, const float* z, float k) {
 #pragma unroll
   for (int i = 1; i < 8; ++i) mx = fmaxf(mx, z[i]);
   if (mx == -INFINITY) return;
-  if (mx > m) {
-    d *= hw_exp2((m - mx) * k);
-    m = mx;
-  }
   float acc = 0.f;
+  const float mn = fmaxf(m, mx);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc += hw_exp2((z[i] - m) * k);
-  d += acc;
+  for (int i = 0; i < 8; ++i) acc += hw_exp2((z[i] - mn) * k);
+  d = fmaf(d, hw_exp2((m - mn) * k), acc);
+  m = mn;
 }
 
 __device__ inline void wave_md(float& m, float& d, float k) {

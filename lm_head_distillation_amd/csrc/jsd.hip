@@ -16,13 +16,16 @@
 //
 // Per element, with Q = 2^a_s (student), P = 2^a_t (teacher) and
 // D = ln P - ln Q = (a_t - a_s) ln 2:
-//   generalized: r = ln(beta e^D + 1 - beta), evaluated for fp32 logits as
-//                  D <  0: log1p(beta expm1(D))
-//                  D >= 0: D + log1p((1-beta) expm1(-D))
-//                (bf16 logits: the direct form described at jsd_terms)
+//   generalized: r = ln(beta e^D + 1 - beta), for fp32 logits from mix_log
+//                (full relative accuracy at every D and beta; bf16 logits:
+//                the direct form described at jsd_terms),
 //                ln(P/M) = D - r, ln(Q/M) = -r,
 //                l = beta P (D - r) - (1-beta) Q r,   g = -(1-beta) Q r,
-//                dA = g - Q G with G = sum_v g (dX_sum)
+//                dA = g - Q G with G = sum_v g (dX_sum); for fp32 logits
+//                the gradient terms are taken relative to the student's most
+//                probable element (RowShift), which leaves dA unchanged and
+//                keeps it accurate where it is a small difference of large
+//                terms
 //   forward KL:  l = P D - P + Q,  dA = Q - P          (sum_v P = 1 exactly)
 //   reverse KL:  l = P - Q - Q D,  G = sum_v l,  dA = -Q D - Q G
 // and an exact tie P == Q gives l = g = 0 (PR #1374 "Fix TVD gradient at
@@ -35,9 +38,9 @@
 // respect to a normalizer error is itself O(loss)).
 //
 // Transcendentals use the hardware instructions (v_exp_f32 = 2^x, v_log_f32 =
-// log2, v_rcp_f32). expm1 on (-1/2, 0] is a degree-9 Taylor polynomial and
-// log1p on [-1/4, 0] the atanh series, so both keep full relative accuracy as
-// their argument goes to 0.
+// log2, v_rcp_f32). expm1 below |x| = 1/2 is a degree-9 Taylor polynomial and
+// log1p below |y| = 1/4 the atanh series, so both keep full relative accuracy
+// as their argument goes to 0.
 #include "elem_math.h"
 #include "kernels.h"
 
@@ -64,7 +67,7 @@ constexpr int kWaves = kThreads / 64;
 // own rounding moves D by up to 2^-9 |z| / T.
 template <int MODE, bool DIRECT = false>
 __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float& P, float& l,
-                                 float& g, float& gacc) {
+                                 float& g, float& gacc, const BetaWeights* bw = nullptr) {
   Q = hw_exp2(as);
   P = hw_exp2(at);
   if constexpr (DIRECT && MODE == kModeGeneralized) {
@@ -98,12 +101,11 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
     g = -Q * D;
     gacc = l;    // G = KL(Q||P), the row loss
   } else {
-    // One expm1 of -|D| and one log1p serve both signs of D.
-    const bool neg = D < 0.f;
-    const float e = expm1_nonpos(-fabsf(D), -fabsf(t));
-    const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
-    const float r = neg ? L1 : D + L1;
-    const float dmr = neg ? D - L1 : -L1;
+    // r and D - r each from mix_log, which keeps full relative accuracy at
+    // every D and beta (no D + log1p(...) form whose two terms cancel when r
+    // is much smaller than D, as for small beta).
+    const float r = mix_log(D, t, bw->r);
+    const float dmr = -mix_log(-D, -t, bw->dmr);
     l = beta * P * dmr - (1.f - beta) * Q * r;
     g = -(1.f - beta) * Q * r;
     gacc = g;
@@ -128,6 +130,15 @@ __device__ inline float4 row_log_norms(const JsdArgs& a, int64_t row) {
   return sh_L;
 }
 
+// The teacher logit at the student's maximum, carried beside the student's
+// (max, denominator): of two partial results the one with the larger maximum
+// wins, and at equal maxima the larger teacher logit, so the merge is
+// commutative (butterfly partners agree) and the result does not depend on
+// the merge order.
+__device__ inline float ref_merge(float m, float z, float mo, float zo) {
+  return m > mo ? z : (mo > m ? zo : fmaxf(z, zo));
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void jsd_stats_kernel(JsdArgs a) {
   const int64_t row = blockIdx.x;
@@ -137,28 +148,127 @@ __global__ __launch_bounds__(kThreads) void jsd_stats_kernel(JsdArgs a) {
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
   const float k = a.k2;
-  float ms = -INFINITY, ds = 0.f, mt = -INFINITY, dt = 0.f;
+  // fp32 rows also track the teacher logit at the student's maximum.
+  constexpr bool kRef = sizeof(T) == 4;
+  float ms = -INFINITY, ds = 0.f, mt = -INFINITY, dt = 0.f, zr = -INFINITY;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8];
     load8(zs, v, n, a.vec_ok, ys);
     load8(zt, v, n, a.vec_ok, yt);
+    if constexpr (kRef) {
+      float mx = ys[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, ys[i]);
+      float zx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) zx = ys[i] == mx ? fmaxf(zx, yt[i]) : zx;
+      if (mx != -INFINITY) zr = ref_merge(ms, zr, mx, zx);
+    }
     md_update8(ms, ds, ys, k);
     md_update8(mt, dt, yt, k);
   }
-  wave_md(ms, ds, k);
+  if constexpr (kRef) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float mo = __shfl_xor(ms, o, 64);
+      const float dof = __shfl_xor(ds, o, 64);
+      const float zo = __shfl_xor(zr, o, 64);
+      zr = ref_merge(ms, zr, mo, zo);
+      md_merge(ms, ds, mo, dof, k);
+    }
+  } else {
+    wave_md(ms, ds, k);
+  }
   wave_md(mt, dt, k);
   __shared__ float4 sh[kWaves];
+  __shared__ float sh_ref[kWaves];
   const int wave = threadIdx.x / 64;
-  if ((threadIdx.x & 63) == 0) sh[wave] = make_float4(ms, ds, mt, dt);
+  if ((threadIdx.x & 63) == 0) {
+    sh[wave] = make_float4(ms, ds, mt, dt);
+    sh_ref[wave] = zr;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
     float4 acc = sh[0];
+    float ref = sh_ref[0];
     for (int w = 1; w < kWaves; ++w) {
+      ref = ref_merge(acc.x, ref, sh[w].x, sh_ref[w]);
       md_merge(acc.x, acc.y, sh[w].x, sh[w].y, k);
       md_merge(acc.z, acc.w, sh[w].z, sh[w].w, k);
     }
     a.stats[row * a.S + s] = acc;
+    if (kRef && a.ref != nullptr) a.ref[row * a.S + s] = ref;
+  }
+}
+
+// fp32 gradient terms relative to a reference element (the student's most
+// probable one). With Q summing to one over the row, dA = g - Q G is
+// unchanged when every r_v is replaced by rho_v = r_v - r_c for any row
+// constant r_c, and r(D_v; beta) - r(D_c; beta) = ln(w e^x + 1 - w) with
+// x = D_v - D_c and w the mixture weight at D_c (mix_weights). Taking the
+// reference at the student's maximum gives x from logit differences alone
+// (the normalizers cancel), x = 0 exactly at that element, and small rho
+// wherever the element's log-ratio is close to the reference's: a row whose
+// probable elements all have P << Q (the divergence near its maximum, the
+// gradient a small difference of O(Q) terms) keeps full relative accuracy,
+// which the plain r_v - sum Q r loses to cancellation. Reverse KL takes the
+// same shift with rho = x (its g is -Q D). When the reference is not finite
+// (a -inf teacher logit there), the plain terms are used (D_c = 0).
+struct RowShift {
+  float4 L;        // (m_s, log2 d_s, m_t, log2 d_t)
+  float zr;        // teacher logit at the student's maximum
+  MixWeights mw;   // weights at the reference (beta, 1 - beta when unshifted)
+  float rc;        // r at the reference (0 when unshifted)
+  bool shifted;
+};
+
+// Row statistics and the reference, merged over the S slices by one thread
+// and broadcast through LDS.
+__device__ inline RowShift row_shift(const JsdArgs& a, int64_t row, bool generalized) {
+  __shared__ RowShift sh;
+  if (threadIdx.x == 0) {
+    const float4* st = a.stats + row * a.S;
+    const float* rf = a.ref + row * a.S;
+    float4 acc = st[0];
+    float zr = rf[0];
+    for (int s = 1; s < a.S; ++s) {
+      const float4 o = st[s];
+      zr = ref_merge(acc.x, zr, o.x, rf[s]);
+      md_merge(acc.x, acc.y, o.x, o.y, a.k2);
+      md_merge(acc.z, acc.w, o.z, o.w, a.k2);
+    }
+    RowShift r;
+    r.L = make_float4(acc.x, hw_log2(acc.y), acc.z, hw_log2(acc.w));
+    r.zr = zr;
+    // D_c in base 2: a_t - a_s at the reference, where a_s = -log2 d_s.
+    const float tc = (zr - r.L.z) * a.k2 - r.L.w + r.L.y;
+    r.shifted = isfinite(tc);
+    const MixWeights plain = mix_weights(0.f, a.beta);
+    r.mw = (generalized && r.shifted) ? mix_weights(tc, a.beta) : plain;
+    r.rc = (generalized && r.shifted) ? mix_log(tc * kLn2, tc, plain) : 0.f;
+    sh = r;
+  }
+  __syncthreads();
+  return sh;
+}
+
+// The shifted gradient term of one element (fp32 generalized and reverse KL):
+// returns g' with dA = g' - Q G', G' the row sum of g'. t = a_t - a_s.
+template <int MODE>
+__device__ inline float shifted_g(const RowShift& rs, float ys, float yt, float t, float Q, float P,
+                                  float k, float beta) {
+  const float xt = rs.shifted ? ((yt - rs.zr) - (ys - rs.L.x)) * k : t;
+  const float x = xt * kLn2;
+  float rho;
+  if constexpr (MODE == kModeReverseKL) {
+    rho = x;
+    return Q > 0.f ? -Q * rho : 0.f;
+  } else {
+    rho = mix_log(x, xt, rs.mw);
+    // A tie (P == Q) has r = 0 exactly (PR #1374), i.e. rho = -r_c.
+    rho = P == Q ? -rs.rc : rho;
+    return Q > 0.f ? -(1.f - beta) * Q * rho : 0.f;
   }
 }
 
@@ -170,12 +280,23 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   const int64_t v1 = min(a.V, v0 + a.slice_w);
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
-  const float4 L = row_log_norms(a, row);
+  // fp32: the gradient terms relative to the student's most probable element
+  // (RowShift), except for the forward KL, whose dA = Q - P has no row sum.
+  constexpr bool kShift = sizeof(T) == 4 && MODE != kModeForwardKL;
+  RowShift rs{};
+  float4 L;
+  if constexpr (kShift) {
+    rs = row_shift(a, row, MODE == kModeGeneralized);
+    L = rs.L;
+  } else {
+    L = row_log_norms(a, row);
+  }
   const float k = a.k2;
-  // fp32 rows also sum Q, P and g over the elements below the student's
-  // maximum and count the elements at it, for pass 3's peak rewrite.
-  constexpr bool kPeak = sizeof(T) == 4;
-  float lsum = 0.f, gsum = 0.f, qrest = 0.f, prest = 0.f, grest = 0.f, npeak = 0.f;
+  const BetaWeights bw = beta_weights(a.beta);
+  // fp32 forward KL also sums Q and P over the elements below the student's
+  // maximum and counts the elements at it, for pass 3's peak rewrite.
+  constexpr bool kPeak = sizeof(T) == 4 && MODE == kModeForwardKL;
+  float lsum = 0.f, gsum = 0.f, qrest = 0.f, prest = 0.f, npeak = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8];
@@ -186,15 +307,15 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
-      jsd_terms<MODE, sizeof(T) == 2>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta,
-                                      Q, P, l, g, gacc);
+      const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
+      jsd_terms<MODE, sizeof(T) == 2>(as, at, a.beta, Q, P, l, g, gacc, &bw);
+      if constexpr (kShift) gacc = shifted_g<MODE>(rs, ys[i], yt[i], at - as, Q, P, k, a.beta);
       lsum += l;
       gsum += gacc;
       if constexpr (kPeak) {
         const bool rest = ys[i] < L.x;
         qrest += rest ? Q : 0.f;
         prest += rest ? P : 0.f;
-        grest += rest ? g : 0.f;
         npeak += rest ? 0.f : 1.f;
       }
     }
@@ -207,9 +328,8 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   if constexpr (kPeak) {
     qrest = wave_sum(qrest);
     prest = wave_sum(prest);
-    grest = wave_sum(grest);
     npeak = wave_sum(npeak);
-    if ((threadIdx.x & 63) == 0) sh_pk[wave] = make_float4(qrest, prest, grest, npeak);
+    if ((threadIdx.x & 63) == 0) sh_pk[wave] = make_float4(qrest, prest, 0.f, npeak);
   }
   if ((threadIdx.x & 63) == 0) sh[wave] = make_float2(lsum, gsum);
   __syncthreads();
@@ -242,9 +362,18 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   const T* zs = static_cast<const T*>(a.zs) + row * a.ld;
   const T* zt = static_cast<const T*>(a.zt) + row * a.ld;
   T* gr = static_cast<T*>(a.grad) + row * a.ld;
-  const float4 L = row_log_norms(a, row);
+  constexpr bool kShift = sizeof(T) == 4 && MODE != kModeForwardKL;
+  RowShift rs{};
+  float4 L;
+  if constexpr (kShift) {
+    rs = row_shift(a, row, MODE == kModeGeneralized);
+    L = rs.L;
+  } else {
+    L = row_log_norms(a, row);
+  }
   const float k = a.k2;
-  constexpr bool kPeak = sizeof(T) == 4;
+  const BetaWeights bw = beta_weights(a.beta);
+  constexpr bool kPeak = sizeof(T) == 4 && MODE == kModeForwardKL;
   __shared__ float sh_G;
   __shared__ float4 sh_pk;
   if (threadIdx.x == 0) {
@@ -273,21 +402,17 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   }
   __syncthreads();
   const float G = sh_G;
-  // Peak rewrite (fp32): when the student's row has one dominant element p
-  // with Q_p near 1, g_p - Q_p G = g_p (1 - Q_p) - Q_p G_rest, and 1 - Q_p
-  // computed from the rounded Q_p keeps only ~1e-7 / (1 - Q_p) relative
-  // accuracy. Summing the other elements instead, 1 - Q_p = Q_rest exactly
-  // (the Q sum to one), so the peak's gradient is g_p Q_rest - Q_p G_rest with
-  // G_rest the sum of g over the other elements, and for the forward KL
-  // Q_p - P_p = P_rest - Q_rest. Reverse KL's G (the row loss) equals the sum
-  // of g = -Q D, so it takes the generalized form. The sums carry the
-  // normalizers' rounding as a relative error, as Q_p and P_p do, so the
-  // rewrite is taken only where its terms are the smaller ones: Q_rest < 1/2,
-  // and for the forward KL Q_rest + P_rest < 1 (below Q_p + P_p). With a tied
-  // maximum no element dominates and the plain form stays.
+  // Peak rewrite (fp32 forward KL): when the student's row has one dominant
+  // element p with Q_p near 1, Q_p - P_p computed from the rounded Q_p and P_p
+  // keeps only ~1e-7 / |Q_p - P_p| relative accuracy. Summing the other
+  // elements instead (the Q and the P each sum to one), Q_p - P_p =
+  // P_rest - Q_rest. The sums carry the normalizers' rounding as a relative
+  // error, as Q_p and P_p do, so the rewrite is taken only where its terms are
+  // the smaller ones: Q_rest + P_rest < 1 (below Q_p + P_p). With a tied
+  // maximum no element dominates and the plain form stays. (The other
+  // branches need no rewrite: with the shifted terms the peak's g' is 0.)
   const float4 pk = kPeak ? sh_pk : make_float4(0.f, 0.f, 0.f, 0.f);
-  const bool rewrite = kPeak && pk.w == 1.f &&
-                       (MODE == kModeForwardKL ? pk.x + pk.y < 1.f : pk.x < 0.5f);
+  const bool rewrite = kPeak && pk.w == 1.f && pk.x + pk.y < 1.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float ys[8], yt[8], out[8];
@@ -296,11 +421,11 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float Q, P, l, g, gacc;
-      jsd_terms<MODE, sizeof(T) == 2>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta,
-                                      Q, P, l, g, gacc);
+      const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
+      jsd_terms<MODE, sizeof(T) == 2>(as, at, a.beta, Q, P, l, g, gacc, &bw);
+      if constexpr (kShift) g = shifted_g<MODE>(rs, ys[i], yt[i], at - as, Q, P, k, a.beta);
       float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
-      if (rewrite && ys[i] == L.x)
-        dA = (MODE == kModeForwardKL) ? (pk.y - pk.x) : (g * pk.x - Q * pk.z);
+      if (rewrite && ys[i] == L.x) dA = pk.y - pk.x;
       out[i] = dA * a.grad_scale;
     }
     store8(gr, v, n, a.vec_ok, out);

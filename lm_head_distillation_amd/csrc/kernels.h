@@ -30,6 +30,10 @@ struct JsdArgs {
   // [rows * S] fp32 inputs only: partial (Q_rest, P_rest, g_rest, n) over the
   // row's elements below / at the student's maximum logit (see jsd_grad_kernel)
   float4* peak = nullptr;
+  // [rows * S] fp32 inputs only: pass 1's teacher logit at the student's
+  // maximum logit (the largest, if the maximum is tied), the reference element
+  // of the gradient terms (see jsd_loss_kernel)
+  float* ref = nullptr;
   float* row_loss = nullptr;    // [rows] per-row loss out
   float row_scale = 1.f;        // multiplies the per-row losses (T^2 when asked)
 };

@@ -10,9 +10,9 @@
 //      generalized:          r = ln(beta e^D + 1 - beta),
 //                            l = beta P (D - r) - (1-beta) Q r,  g = -(1-beta) Q r
 //    with g = dl/dx, elementwise (no softmax chain rule: the inputs are the
-//    variables). r uses the same small-argument expm1 / log1p as the logit
-//    path for fp32 inputs and, like it, jsd_r_direct for bf16 inputs, whose
-//    own rounding (2^-9 |x|) outweighs the difference. An exact tie P == Q gives l = 0 and, in the generalized branch,
+//    variables). r and D - r come from mix_log for fp32 inputs, as in the
+//    logit path, and from jsd_r_direct for bf16 inputs, whose own rounding
+//    (2^-9 |x|) outweighs the difference. An exact tie P == Q gives l = 0 and, in the generalized branch,
 //    g = 0 (PR #1374); zero-probability factors contribute 0 (0 log 0 = 0).
 //
 //  * Total variation distance (PR #1374 "Fix TVD gradient at p == q"):
@@ -32,7 +32,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.44269504088896341f;
 
 template <int MODE, bool DIRECT>
-__device__ inline void logprob_terms(float x, float y, float beta, float& l, float& g) {
+__device__ inline void logprob_terms(float x, float y, float beta, const BetaWeights& bw, float& l,
+                                     float& g) {
   const float Q = hw_exp2(x * kLog2e);
   const float P = hw_exp2(y * kLog2e);
   if (P == Q) {  // exact tie (also both zero): D = 0
@@ -53,11 +54,8 @@ __device__ inline void logprob_terms(float x, float y, float beta, float& l, flo
     if constexpr (DIRECT) {
       jsd_r_direct(D, D * kLog2e, beta, r, dmr);
     } else {
-      const bool neg = D < 0.f;
-      const float e = expm1_nonpos(-fabsf(D), -fabsf(D) * kLog2e);
-      const float L1 = log1p_nonpos((neg ? beta : 1.f - beta) * e);
-      r = neg ? L1 : D + L1;
-      dmr = neg ? D - L1 : -L1;
+      r = mix_log(D, D * kLog2e, bw.r);
+      dmr = -mix_log(-D, -D * kLog2e, bw.dmr);
     }
     const float tp = P > 0.f ? beta * P * dmr : 0.f;
     const float tq = Q > 0.f ? (1.f - beta) * Q * r : 0.f;
@@ -87,6 +85,7 @@ __global__ __launch_bounds__(kThreads) void logprob_jsd_kernel(ElemArgs a) {
   const T* xs = static_cast<const T*>(a.a) + row * a.ld;
   const T* ys = static_cast<const T*>(a.b) + row * a.ld;
   T* gr = a.grad ? static_cast<T*>(a.grad) + row * a.ld : nullptr;
+  const BetaWeights bw = beta_weights(a.beta);
   float lsum = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
@@ -98,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void logprob_jsd_kernel(ElemArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       float l, g;
-      logprob_terms<MODE, sizeof(T) == 2>(x[i], y[i], a.beta, l, g);
+      logprob_terms<MODE, sizeof(T) == 2>(x[i], y[i], a.beta, bw, l, g);
       lsum += l;
       out[i] = g * a.grad_scale;
     }

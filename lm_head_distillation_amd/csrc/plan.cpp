@@ -75,6 +75,8 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 8);
   p.off_peak = off;
   off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 16);
+  p.off_ref = off;
+  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 4);
   p.off_partial = off;
   if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H_s * 4);
   p.off_xt = off;
@@ -101,6 +103,8 @@ JsdPlan plan_jsd(int64_t BT, int64_t V) {
   off = align256(off + static_cast<size_t>(BT * p.slices.S) * 8);
   p.off_peak = off;
   off = align256(off + static_cast<size_t>(BT * p.slices.S) * 16);
+  p.off_ref = off;
+  off = align256(off + static_cast<size_t>(BT * p.slices.S) * 4);
   p.total = off;
   return p;
 }

@@ -64,7 +64,7 @@ struct ChunkPlan {
   int64_t k_per_split = 0;
   // Workspace layout, byte offsets from the workspace base.
   size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0, off_peak = 0,
-         off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0, total = 0;
+         off_ref = 0, off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0, total = 0;
 };
 
 // Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).
@@ -76,7 +76,7 @@ void plan_splitk(int64_t M, int64_t N, int64_t K, int* splitk, int64_t* k_per_sp
 
 struct JsdPlan {
   SlicePlan slices;
-  size_t off_row_loss = 0, off_stats = 0, off_lg = 0, off_peak = 0, total = 0;
+  size_t off_row_loss = 0, off_stats = 0, off_lg = 0, off_peak = 0, off_ref = 0, total = 0;
 };
 
 JsdPlan plan_jsd(int64_t BT, int64_t V);

@@ -63,6 +63,22 @@ def test_logprob_tiny_f32(fl, beta, reduction):
     assert_tensor_close(from_device(grad), rg, TOL["f32"], "grad_logq")
 
 
+@pytest.mark.parametrize("beta", [0.001, 0.01, 0.99, 0.999])
+@pytest.mark.parametrize("scale", [0.25, 2.0, 8.0])
+def test_logprob_extreme_beta_f32(fl, beta, scale):
+    """fp32 at mixture weights near 0 and 1, over near-flat (logit std 0.25)
+    to sharp (std 8) rows: r = ln(beta e^D + 1 - beta) is then much smaller
+    than D, or close to D + ln(beta), where forms that add D to a logarithm
+    lose digits. The oracle takes beta as the fp32 value the library gets."""
+    x = _logprobs(511, 8, 512, "f32", scale)
+    y = _logprobs(512, 8, 512, "f32", scale)
+    loss, grad = fl.fljsd_jsd_logprob(to_device(x, "f32"), to_device(y, "f32"), beta, "none")
+    torch.cuda.synchronize()
+    rl, rg = oracle.jsd_logprob(to_f64(x, "f32"), to_f64(y, "f32"), float(np.float32(beta)), "none")
+    assert_loss_close(from_device(loss), rl, TOL["f32"])
+    assert_tensor_close(from_device(grad), rg, TOL["f32"], "grad_logq")
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
 @pytest.mark.parametrize("R,V", [(64, 40960 + 37), (3, 100), (300, 1000)])
 def test_logprob_bf16_shapes(fl, beta, R, V):
