@@ -15,8 +15,20 @@ Fields beyond the throughput:
                 events the library records around each launch during the
                 timed steps, against MI355X's published peak.
   kernels       the same tally for every kernel class.
+  mfma_util_counter / mfma_counters
+                matrix-core utilisation of the three products from rocprofv3
+                counters (profiles/mfma.json, used only when it was taken with
+                the current sources): busy fraction at the held clock, and
+                counted matrix flops against the nominal peak.
+  sweep         the 1024- and 8192-row workloads at 1, 8 and 32 chunks: ms,
+                tokens/s, peak HBM of the pass and its roofline floor (each
+                kernel class at the larger of its bytes at 8 TB/s and its
+                flops at 2.5 PFLOP/s); small chunks are bound by weight and
+                grad_W read-add-write traffic.
   cpu_baseline  the CPU oracle (numpy fp64) timed on the first rows of the
-                same workload, in tokens/s.
+                same workload, in tokens/s, on all host threads.
+  oracle_one_thread
+                the oracle on one thread over the three small workloads.
 """
 from __future__ import annotations
 
@@ -56,8 +68,10 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="rows of the workload the CPU oracle is timed on")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--sweep", action="store_true",
-                   help="also time the 1024- and 8192-row workloads at 1, 8 and 32 chunks")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the 1024- and 8192-row workloads at 1, 8 and 32 chunks")
+    p.add_argument("--no-oracle-1thread", action="store_true",
+                   help="skip the one-thread oracle times of the three small workloads")
     p.add_argument("--flce", action="store_true",
                    help="also time the fused-linear cross-entropy at 1024..8192 rows")
     p.add_argument("--losses", action="store_true",
@@ -133,16 +147,69 @@ def clock_for(cls):
     return entry.get("clock_mhz") if entry else None
 
 
-def sweep(fljsd, steps, warmup):
-    """ms per step and tokens/s of the two H=4096, V=128256 workloads per chunk count."""
+def pass_floor(kernels, steps):
+    """Roofline floor of one pass from the library's per-class tallies: each
+    kernel class is bound by the larger of its algorithmic bytes at the HBM
+    peak and its flops at the bf16 matrix peak; the pass's floor is the sum
+    (the kernels run one after another). Returns ms per step:
+    (floor, all bytes at the HBM peak, all flops at the matrix peak)."""
+    floor = hbm = mfma = 0.0
+    for k in kernels.values():
+        if not k["launches"]:
+            continue
+        t_hbm = k["bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e3 / steps
+        t_mfma = k["flops"] / (PEAK_BF16_TFLOPS * 1e12) * 1e3 / steps
+        floor += max(t_hbm, t_mfma)
+        hbm += t_hbm
+        mfma += t_mfma
+    return floor, hbm, mfma
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
+
+
+def mfma_counters():
+    """Matrix-core utilisation of the three products from rocprofv3 counters
+    (the committed summary, if it was taken with the current sources): the
+    busy fraction of the matrix cores over the cycles the kernel ran
+    (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), at the clock the
+    chip held) and the counted bf16 matrix flops (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    x 512) over the traced kernel time against the nominal 2.5 PFLOP/s."""
+    out = {}
+    for cls in GEMM_CLASSES:
+        entry = _profile_entry(MFMA_FILE, cls)
+        if entry:
+            out[cls] = {k: entry[k] for k in ("mfma_busy_frac", "frac_nominal", "counted_flops_per_launch",
+                                              "avg_ms", "launches_per_pass", "clock_mhz") if k in entry}
+    if len(out) != len(GEMM_CLASSES):
+        return {}
+    # The three products together, weighted by their time in one pass.
+    ms = sum(e["avg_ms"] * e["launches_per_pass"] for e in out.values())
+    flops = sum(e["counted_flops_per_launch"] * e["launches_per_pass"] for e in out.values())
+    busy = sum(e["mfma_busy_frac"] * e["avg_ms"] * e["launches_per_pass"] for e in out.values())
+    out["gemms"] = {"mfma_busy_frac": round(busy / ms, 4),
+                    "frac_nominal": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
+def sweep(fljsd, steps, warmup, large_batch_dev):
+    """ms per step, tokens/s, peak HBM and roofline floor of the two
+    H=4096, V=128256 workloads (1024 and 8192 rows) per chunk count."""
     import torch
 
     import workloads
     out = []
     for key in ("llama3_head", "large_batch"):
         w = workloads.WORKLOADS[key]
-        X_s, W_s, X_t, W_t = device_inputs(workloads.make_inputs(w))
+        if key == "large_batch":
+            X_s, W_s, X_t, W_t = large_batch_dev
+        else:
+            X_s, W_s, X_t, W_t = device_inputs(workloads.make_inputs(w))
+        in_bytes = sum(t.numel() * t.element_size() for t in (X_s, W_s, X_t, W_t))
         for nc in (1, 8, 32):
+            # Peak HBM of the pass: its inputs, outputs and workspace (buffers
+            # other parts of this run still hold are left out).
+            base = torch.cuda.memory_allocated()
             ws = torch.empty(fljsd.fljsd_workspace_size(w.BT, w.H_s, w.H_t, w.V, fljsd.BF16, nc),
                              dtype=torch.uint8, device="cuda")
             out_t = (torch.empty(1, dtype=torch.float32, device="cuda"), torch.empty_like(X_s),
@@ -163,14 +230,21 @@ def sweep(fljsd, steps, warmup):
             ms = (time.perf_counter() - t0) / steps * 1e3
             kernels = fljsd.fljsd_profile_read()
             fljsd.fljsd_profile_enable(False)
+            floor, hbm, mfma = pass_floor(kernels, steps)
+            alg_bytes = sum(k["bytes"] for k in kernels.values()) / steps
             rec = {"workload": key, "BT": w.BT, "num_chunks": nc, "ms_per_step": round(ms, 3),
                    "tokens_per_s": round(w.BT / ms * 1e3, 1),
-                   "peak_hbm_mb": round(torch.cuda.max_memory_allocated() / 2**20, 1),
+                   "peak_hbm_mb": round((torch.cuda.max_memory_allocated() - base + in_bytes) / 2**20, 1),
                    "workspace_mb": round(ws.numel() / 2**20, 1),
+                   "alg_hbm_gb": round(alg_bytes / 1e9, 2),
+                   "hbm_floor_ms": round(hbm, 3), "mfma_floor_ms": round(mfma, 3),
+                   "floor_ms": round(floor, 3), "bound": "hbm" if hbm > mfma else "mfma",
+                   "roofline_frac": round(floor / ms, 4),
                    "kernel_ms_per_step": {c: round(k["ms"] / steps, 3) for c, k in kernels.items()
                                           if k["launches"]}}
             log(f"  sweep {key:12s} nc={nc:2d}: {ms:8.2f} ms/step  {rec['tokens_per_s']:>10,.0f} tokens/s  "
-                f"peak {rec['peak_hbm_mb']:.0f} MB  " +
+                f"peak {rec['peak_hbm_mb']:.0f} MB  floor {floor:.2f} ms ({rec['bound']}, "
+                f"{100 * floor / ms:.0f}%)  " +
                 " ".join(f"{c}={v:.2f}" for c, v in rec["kernel_ms_per_step"].items()))
             out.append(rec)
             del ws, out_t
@@ -298,6 +372,28 @@ def cpu_baseline(inp, w, rows):
             "sample": (f"first {rows} of {w.BT} rows, full H={w.H_s} and V={w.V} weights, "
                        f"fp64 numpy ({blas_name}) on {cpu_model()}, {dt:.1f} s"),
             "seconds": dt}
+
+
+def oracle_one_thread():
+    """The oracle on one host thread over the three small workloads in full
+    (tiny fp32, multi-block tail, ties): seconds and tokens/s each."""
+    import threadpoolctl
+
+    import oracle
+    import workloads
+    out = []
+    with threadpoolctl.threadpool_limits(limits=1):
+        for key in ("tiny_f32", "multiblock_tail", "ties_padded"):
+            w = workloads.WORKLOADS[key]
+            inp = workloads.make_inputs(w)
+            args = [workloads.to_f64(inp[k], w.dtype) for k in ("X_s", "W_s", "X_t", "W_t")]
+            t0 = time.perf_counter()
+            oracle.fused_linear_jsd(*args, w.beta, w.temperature, w.reduction)
+            dt = time.perf_counter() - t0
+            out.append({"workload": f"{key}: BT={w.BT} H={w.H_s} V={w.V} {w.dtype}",
+                        "seconds": round(dt, 3), "tokens_per_s": round(w.BT / dt, 2), "cores": 1})
+            log(f"cpu oracle, one thread: {key:16s} {dt:8.3f} s  {w.BT / dt:10.1f} tokens/s")
+    return out
 
 
 def cpu_model():
@@ -432,13 +528,19 @@ def main():
                         "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4)}
                     for c, r in per_class.items()},
     }
-    if args.sweep:
-        result["sweep"] = sweep(fljsd, max(3, args.steps // 2), 1)
+    mfma = mfma_counters()
+    result["mfma_util_counter"] = mfma.get("gemms")
+    if mfma:
+        result["mfma_counters"] = mfma
+    if not args.no_sweep:
+        result["sweep"] = sweep(fljsd, max(3, args.steps // 4), 1, (X_s, W_s, X_t, W_t))
     if args.flce:
         result["flce"] = flce_sweep(fljsd, max(3, args.steps // 2), 1)
     if args.losses:
         result["losses"] = losses_timing(fljsd, 20, 3)
     if not args.no_cpu_baseline:
+        if not args.no_oracle_1thread:
+            result["oracle_one_thread"] = oracle_one_thread()
         del X_s, W_s, X_t, W_t, ws, gX, gW
         torch.cuda.empty_cache()
         cb = cpu_baseline(inp, w, args.cpu_rows)

@@ -201,7 +201,7 @@ int fljsd_generalized_jsd(const void* logits_s, const void* logits_t,
  * Order them on one stream.
  * Errors: as fljsd_generalized_jsd; FLJSD_EWORKSPACE (before any HIP call)
  * when fljsd_generalized_jsd_workspace_size(BT, V, dtype) exceeds
- * FLJSD_NOALLOC_SCRATCH_BYTES (about 190,000 rows at any V); FLJSD_EHIP when
+ * FLJSD_NOALLOC_SCRATCH_BYTES (about 174,000 rows at any V); FLJSD_EHIP when
  * the scratch address cannot be looked up.
  */
 int fljsd_generalized_jsd_noalloc(const void* logits_s, const void* logits_t,

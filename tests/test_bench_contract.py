@@ -75,3 +75,39 @@ def test_pages_reference_throughput():
     # The pages' H100 figure for 8192 rows, one chunk: 60.62 ms per pass.
     assert bench.PAGES_TOKENS_PER_S == pytest.approx(8192 / 60.62e-3)
     assert round(bench.PAGES_TOKENS_PER_S) == 135137
+
+
+def test_pass_floor_takes_each_class_at_its_bound():
+    # One step: a product of 2.5 TFLOP (1 ms at the matrix peak, 0.1 ms of
+    # bytes) and a streaming pass of 8 GB (1 ms at the HBM peak, no flops).
+    k = {"gemm_logits": {"ms": 3.0, "launches": 1, "flops": 2.5e12, "bytes": 0.8e9},
+         "jsd_loss": {"ms": 1.5, "launches": 1, "flops": 0.0, "bytes": 8e9},
+         "splitk_reduce": {"ms": 0.0, "launches": 0, "flops": 0.0, "bytes": 0.0}}
+    floor, hbm, mfma = bench.pass_floor(k, 1)
+    assert floor == pytest.approx(2.0)
+    assert hbm == pytest.approx(1.1)
+    assert mfma == pytest.approx(1.0)
+    floor2, _, _ = bench.pass_floor(k, 2)      # the same tallies over two steps
+    assert floor2 == pytest.approx(1.0)
+
+
+def test_mfma_counters_combine_by_time(tmp_path, monkeypatch):
+    from lm_head_distillation_amd.build import source_digest
+    d = source_digest()
+    rec = {"kernels": {
+        "gemm_logits": {"source_digest": d, "mfma_busy_frac": 0.8, "frac_nominal": 0.5,
+                        "counted_flops_per_launch": 5e12, "avg_ms": 4.0, "launches_per_pass": 2},
+        "gemm_grad_input": {"source_digest": d, "mfma_busy_frac": 0.6, "frac_nominal": 0.4,
+                            "counted_flops_per_launch": 4e12, "avg_ms": 4.0, "launches_per_pass": 1},
+        "gemm_grad_weight": {"source_digest": d, "mfma_busy_frac": 0.7, "frac_nominal": 0.3,
+                             "counted_flops_per_launch": 3e12, "avg_ms": 4.0, "launches_per_pass": 1}}}
+    path = tmp_path / "mfma.json"
+    path.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(path))
+    out = bench.mfma_counters()
+    # 16 ms of products, 17 TFLOP: 1062.5 TFLOP/s of 2500.
+    assert out["gemms"]["frac_nominal"] == pytest.approx(17e12 / 16e-3 / 2.5e15, abs=1e-4)
+    assert out["gemms"]["mfma_busy_frac"] == pytest.approx((0.8 * 8 + 0.6 * 4 + 0.7 * 4) / 16, abs=1e-4)
+    rec["kernels"]["gemm_grad_weight"]["source_digest"] = "0" * 16
+    path.write_text(json.dumps(rec))
+    assert bench.mfma_counters() == {}

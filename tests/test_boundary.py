@@ -233,7 +233,7 @@ def jsd_noalloc(lib, **over):
     (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
     (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
     (dict(grad=FAKE + 2), EALIGN),
-    # Past the 8 MiB scratch array: 400,000 rows need 17.6 MB of row statistics.
+    # Past the 8 MiB scratch array: 400,000 rows need 19.2 MB of row statistics.
     (dict(BT=400_000, V=1000, ld=1000), EWORKSPACE),
 ])
 def test_generalized_jsd_noalloc_rejects(lib, over, code):
@@ -250,8 +250,8 @@ def test_noalloc_scratch_bound_matches_header(lib):
     from lm_head_distillation_amd import fljsd
     assert fljsd.NOALLOC_SCRATCH_BYTES == 8 << 20
     # The largest batch of a bf16 / fp32 row stride that fits, and the next one out.
-    assert lib.fljsd_generalized_jsd_workspace_size(190_000, 1000, BF16) <= 8 << 20
-    assert jsd_noalloc(lib, BT=191_000, V=1000, ld=1000) == EWORKSPACE
+    assert lib.fljsd_generalized_jsd_workspace_size(174_000, 1000, BF16) <= 8 << 20
+    assert jsd_noalloc(lib, BT=175_000, V=1000, ld=1000) == EWORKSPACE
 
 
 def elem(lib, fn, **over):
