@@ -65,7 +65,9 @@ typedef enum fljsd_reduction {
   FLJSD_NONE = 3
 } fljsd_reduction;
 
-/* Status codes. */
+/* Status codes. The pages give no error convention for this op; negative
+ * C status codes checked before any work is enqueued are this library's
+ * reading. */
 #define FLJSD_OK 0
 #define FLJSD_EINVAL (-1)      /* null required pointer, size <= 0, beta outside [0,1],
                                   temperature <= 0 or not finite, ld < V, num_chunks < 0 */
@@ -291,8 +293,13 @@ int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
                                size_t budget_bytes);
 
 /* Workspace bytes fljsd_forward_backward needs for this shape with
- * num_chunks >= 1 chunks. Pure host arithmetic; no device is touched.
- * Returns 0 for invalid arguments (sizes <= 0, num_chunks < 1, bad dtype). */
+ * num_chunks >= 1 chunks, after the pages' per-chunk memory model (PR #1352,
+ * Details, memory table: a chunk of C rows holds both logits tensors, and only
+ * the per-row loss grows with BT): for bf16 about 3 * C * V * 2 bytes (student
+ * logits / dZ, teacher logits, dZ^T) plus C * H_s * 2 (X_s^T) and small
+ * per-row arrays; for fp32 2 * C * V * 4 plus the per-row arrays. Pure host
+ * arithmetic; no device is touched. Returns 0 for invalid arguments (sizes
+ * <= 0, num_chunks < 1, bad dtype). */
 size_t fljsd_workspace_size(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
                             int dtype, int num_chunks);
 
@@ -308,7 +315,8 @@ size_t fljsd_generalized_jsd_workspace_size(int64_t BT, int64_t V, int dtype);
 int fljsd_plan_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
                           int dtype, size_t budget_bytes);
 
-/* Static description of a status code. */
+/* Static description of a status code (the codes are this library's reading;
+ * the pages define none). */
 const char* fljsd_strerror(int code);
 
 /* Details of the calling thread's most recent failure ("" if none). */

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfljsd.so")
 
-SOURCES = ["api.hip", "jsd.hip", "gemm_bf16.hip", "gemm_f32.hip", "transpose.hip", "losses.hip", "ce.hip", "plan.cpp"]
+SOURCES = ["api.hip", "jsd.hip", "gemm_bf16.hip", "gemm_f32.hip", "transpose.hip", "losses.hip", "ce.hip",
+           "plan.cpp", "validate.cpp"]
 ARCH = "gfx950"
 
 

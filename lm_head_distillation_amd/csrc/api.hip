@@ -10,6 +10,7 @@
 #include "fljsd.h"
 #include "kernels.h"
 #include "plan.h"
+#include "validate.h"
 
 #include <hip/hip_runtime.h>
 
@@ -21,23 +22,13 @@
 #include <string>
 #include <vector>
 
-#define FLJSD_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace fljsd {
 namespace {
 
-thread_local std::string g_last_error;
-
-int fail(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
-
 int fail_hip(hipError_t e, const char* what) {
   return fail(FLJSD_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 double reduction_scale(int reduction, int64_t rows, int64_t V) {
   switch (reduction) {
@@ -142,17 +133,6 @@ double gemm_bytes(const GemmArgs& g, int es) {
   const bool rmw = g.epilogue == kEpiAccumulate || g.epilogue == kEpiAccumulateF32;
   const double out = static_cast<double>(g.M) * g.N * (f32_out ? 4.0 : es) * (rmw ? 2 : 1);
   return in + out;
-}
-
-// Checks shared by both compute entry points.
-int check_common(int dtype, float beta, float temperature, int reduction) {
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
-  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
-    return fail(FLJSD_EDTYPE, "unknown reduction");
-  if (!(beta >= 0.0f && beta <= 1.0f)) return fail(FLJSD_EINVAL, "beta must be in [0, 1]");
-  if (!(temperature > 0.0f) || !std::isfinite(temperature))
-    return fail(FLJSD_EINVAL, "temperature must be finite and > 0");
-  return FLJSD_OK;
 }
 
 // The three loss passes. With `part_s` the row statistics come from the
@@ -317,45 +297,6 @@ int run_grad_weight(int dtype, const void* dZ, int64_t ldz, const void* X, int64
 
 using namespace fljsd;
 
-FLJSD_EXPORT size_t fljsd_workspace_size(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
-                                         int dtype, int num_chunks) {
-  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0 || num_chunks < 1) return 0;
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
-  return plan_chunks(BT, H_s, H_t, V, dtype, num_chunks).total;
-}
-
-FLJSD_EXPORT size_t fljsd_generalized_jsd_workspace_size(int64_t BT, int64_t V, int dtype) {
-  if (BT <= 0 || V <= 0) return 0;
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
-  return plan_jsd(BT, V).total;
-}
-
-FLJSD_EXPORT int fljsd_plan_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
-                                       int dtype, size_t budget_bytes) {
-  g_last_error.clear();
-  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0) return fail(FLJSD_EINVAL, "sizes must be > 0");
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
-  const int64_t nc = policy_num_chunks(BT, H_s, H_t, V, dtype, budget_bytes);
-  if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the budget");
-  if (nc > INT32_MAX) return fail(FLJSD_EINVAL, "chunk count overflows int");
-  return static_cast<int>(nc);
-}
-
-FLJSD_EXPORT const char* fljsd_strerror(int code) {
-  switch (code) {
-    case FLJSD_OK: return "success";
-    case FLJSD_EINVAL: return "invalid argument";
-    case FLJSD_EDTYPE: return "unsupported dtype or reduction";
-    case FLJSD_EWORKSPACE: return "workspace too small";
-    case FLJSD_EALIGN: return "misaligned pointer or leading dimension";
-    case FLJSD_EHIP: return "HIP runtime error";
-    case FLJSD_EDEVICE: return "device is not an MI355X (gfx950)";
-    default: return "unknown status code";
-  }
-}
-
-FLJSD_EXPORT const char* fljsd_last_error(void) { return g_last_error.c_str(); }
-
 FLJSD_EXPORT int fljsd_profile_enable(int enable) {
   g_prof.enabled = enable != 0;
   g_prof.clear();
@@ -404,37 +345,14 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
                                            float* loss, void* grad_X_s, void* grad_W_s,
                                            int grad_w_dtype, unsigned flags, void* workspace,
                                            size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  if (!X_s || !W_s || !X_t || !W_t || !loss)
-    return fail(FLJSD_EINVAL, "X_s, W_s, X_t, W_t and loss must not be NULL");
-  if (BT <= 0 || H_s <= 0 || H_t <= 0 || V <= 0)
-    return fail(FLJSD_EINVAL, "BT, H_s, H_t and V must be > 0");
-  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
-  int rc = check_common(dtype, beta, temperature, reduction);
+  clear_last_error();
+  ChunkPlan plan;
+  int rc = check_forward_backward(X_s, W_s, X_t, W_t, BT, H_s, H_t, V, dtype, beta, temperature,
+                                  reduction, num_chunks, loss, grad_X_s, grad_W_s, grad_w_dtype,
+                                  flags, workspace, workspace_bytes, &plan);
   if (rc != FLJSD_OK) return rc;
-  if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
-  if (grad_w_dtype != dtype && !(dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32))
-    return fail(FLJSD_EDTYPE, "grad_w_dtype must equal dtype, or be F32 with BF16 inputs");
-  if (flags & ~static_cast<unsigned>(FLJSD_ACCUMULATE_GRAD_W | FLJSD_TEMPERATURE_SQUARED))
-    return fail(FLJSD_EINVAL, "unknown flag bits");
   const bool gw_f32_acc = dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32;
   const bool gw_add_existing = (flags & FLJSD_ACCUMULATE_GRAD_W) != 0;
-  const int vec = dtype_vec(dtype);
-  const void* ptrs[] = {X_s, W_s, X_t, W_t, loss, grad_X_s, grad_W_s, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
-  if (H_s % vec != 0 || H_t % vec != 0)
-    return fail(FLJSD_EALIGN, "H_s and H_t must be multiples of 16 bytes of elements");
-
-  int64_t nc = num_chunks;
-  if (nc == 0) {
-    nc = policy_num_chunks(BT, H_s, H_t, V, dtype, workspace_bytes);
-    if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
-  }
-  const ChunkPlan plan = plan_chunks(BT, H_s, H_t, V, dtype, nc);
-  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
-  if (workspace_bytes < plan.total)
-    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
   rc = check_device();
   if (rc != FLJSD_OK) return rc;
 
@@ -505,7 +423,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
       // Chunk 0 overwrites unless the caller asked to add to grad_W's
       // contents; later chunks add. An fp32 grad_W takes the bf16 product
       // unrounded (one-split fp32 store, or fp32 read-add-write). With bf16
-      // inputs dZ^T goes over the teacher logits, dead after the loss passes.
+      // inputs pass 3 has already written dZ^T (its own workspace region).
       const bool add = ci > 0 || gw_add_existing;
       const int epi = gw_f32_acc ? (add ? kEpiAccumulateF32 : kEpiPartialF32)
                                  : (add ? kEpiAccumulate : kEpiStore);
@@ -529,23 +447,6 @@ namespace {
 
 // fljsd_generalized_jsd with the workspace already chosen (the caller's, or
 // the no-allocation entry point's file-scope scratch array).
-// Every check of fljsd_generalized_jsd's arguments except the workspace's.
-int check_generalized_jsd_args(const void* logits_s, const void* logits_t, int64_t BT, int64_t V,
-                               int64_t ld, int dtype, float beta, float temperature,
-                               int reduction, const float* loss, const void* grad_logits_s) {
-  if (!logits_s || !logits_t || !loss)
-    return fail(FLJSD_EINVAL, "logits_s, logits_t and loss must not be NULL");
-  if (BT <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT and V must be > 0");
-  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
-  if (ld < V) return fail(FLJSD_EINVAL, "ld must be >= V");
-  int rc = check_common(dtype, beta, temperature, reduction);
-  if (rc != FLJSD_OK) return rc;
-  const void* ptrs[] = {logits_s, logits_t, loss, grad_logits_s};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
-  return FLJSD_OK;
-}
-
 int generalized_jsd_impl(const void* logits_s, const void* logits_t, int64_t BT, int64_t V,
                          int64_t ld, int dtype, float beta, float temperature, int reduction,
                          float* loss, void* grad_logits_s, void* workspace,
@@ -553,12 +454,9 @@ int generalized_jsd_impl(const void* logits_s, const void* logits_t, int64_t BT,
   int rc = check_generalized_jsd_args(logits_s, logits_t, BT, V, ld, dtype, beta, temperature,
                                       reduction, loss, grad_logits_s);
   if (rc != FLJSD_OK) return rc;
-  if (workspace && !aligned16(workspace))
-    return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
-  const JsdPlan plan = plan_jsd(BT, V);
-  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
-  if (workspace_bytes < plan.total)
-    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
+  JsdPlan plan;
+  rc = check_jsd_workspace(BT, V, workspace, workspace_bytes, &plan);
+  if (rc != FLJSD_OK) return rc;
   rc = check_device();
   if (rc != FLJSD_OK) return rc;
 
@@ -644,7 +542,7 @@ FLJSD_EXPORT int fljsd_generalized_jsd(const void* logits_s, const void* logits_
                                        float temperature, int reduction, float* loss,
                                        void* grad_logits_s, void* workspace,
                                        size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
+  clear_last_error();
   return generalized_jsd_impl(logits_s, logits_t, BT, V, ld, dtype, beta, temperature, reduction,
                               loss, grad_logits_s, workspace, workspace_bytes, stream);
 }
@@ -653,16 +551,13 @@ FLJSD_EXPORT int fljsd_generalized_jsd_noalloc(const void* logits_s, const void*
                                                int64_t BT, int64_t V, int64_t ld, int dtype,
                                                float beta, float temperature, int reduction,
                                                float* loss, void* grad_logits_s, void* stream) {
-  g_last_error.clear();
+  clear_last_error();
   // Arguments and the scratch bound are checked before any HIP call.
   int rc = check_generalized_jsd_args(logits_s, logits_t, BT, V, ld, dtype, beta, temperature,
                                       reduction, loss, grad_logits_s);
   if (rc != FLJSD_OK) return rc;
-  const size_t need = plan_jsd(BT, V).total;
-  if (need > FLJSD_NOALLOC_SCRATCH_BYTES)
-    return fail(FLJSD_EWORKSPACE, "this shape needs " + std::to_string(need) +
-                                      " bytes of scratch; the no-allocation entry point holds " +
-                                      std::to_string(static_cast<size_t>(FLJSD_NOALLOC_SCRATCH_BYTES)));
+  rc = check_noalloc_scratch(BT, V, FLJSD_NOALLOC_SCRATCH_BYTES);
+  if (rc != FLJSD_OK) return rc;
   void* ws = nullptr;
   rc = scratch_address(&ws);
   if (rc != FLJSD_OK) return rc;
@@ -678,23 +573,13 @@ namespace {
 template <class Launch>
 int run_elem_loss(const void* a_ptr, const void* b_ptr, int64_t BT, int64_t V, int64_t ld,
                   int dtype, int reduction, float* loss, void* grad, bool elementwise_none,
-                  float beta, int mode, void* workspace, size_t workspace_bytes, void* stream,
-                  int kclass, Launch&& launch) {
-  if (!a_ptr || !b_ptr || !loss) return fail(FLJSD_EINVAL, "inputs and loss must not be NULL");
-  if (BT <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT and V must be > 0");
-  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
-  if (ld < V) return fail(FLJSD_EINVAL, "ld must be >= V");
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
-  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
-    return fail(FLJSD_EDTYPE, "unknown reduction");
-  const void* ptrs[] = {a_ptr, b_ptr, loss, grad, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
-  const JsdPlan plan = plan_jsd(BT, V);
-  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
-  if (workspace_bytes < plan.total)
-    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
-  int rc = check_device();
+                  bool check_beta, float beta, int mode, void* workspace, size_t workspace_bytes,
+                  void* stream, int kclass, Launch&& launch) {
+  JsdPlan plan;
+  int rc = check_elem_loss(a_ptr, b_ptr, BT, V, ld, dtype, reduction, check_beta, beta, loss, grad,
+                           workspace, workspace_bytes, &plan);
+  if (rc != FLJSD_OK) return rc;
+  rc = check_device();
   if (rc != FLJSD_OK) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -744,38 +629,19 @@ FLJSD_EXPORT int fljsd_jsd_logprob(const void* logq_s, const void* logp_t, int64
                                    int64_t ld, int dtype, float beta, int reduction, float* loss,
                                    void* grad_logq_s, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  g_last_error.clear();
-  if (!(beta >= 0.0f && beta <= 1.0f)) return fail(FLJSD_EINVAL, "beta must be in [0, 1]");
+  clear_last_error();
   return run_elem_loss(logq_s, logp_t, BT, V, ld, dtype, reduction, loss, grad_logq_s, false,
-                       beta, mode_for(beta), workspace, workspace_bytes, stream,
+                       true, beta, mode_for(beta), workspace, workspace_bytes, stream,
                        FLJSD_KCLASS_ELEM_LOSS, launch_logprob_jsd);
 }
 
 FLJSD_EXPORT int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, int64_t ld,
                            int dtype, int reduction, float* loss, void* grad_p, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  return run_elem_loss(p, q, BT, V, ld, dtype, reduction, loss, grad_p, true, 0.0f,
+  clear_last_error();
+  return run_elem_loss(p, q, BT, V, ld, dtype, reduction, loss, grad_p, true, false, 0.0f,
                        kModeGeneralized, workspace, workspace_bytes, stream,
                        FLJSD_KCLASS_ELEM_LOSS, launch_tvd);
-}
-
-FLJSD_EXPORT size_t fljsd_flce_workspace_size(int64_t BT, int64_t H, int64_t V, int dtype,
-                                              int num_chunks) {
-  if (BT <= 0 || H <= 0 || V <= 0 || num_chunks < 1) return 0;
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return 0;
-  return plan_ce_chunks(BT, H, V, dtype, num_chunks).total;
-}
-
-FLJSD_EXPORT int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
-                                            size_t budget_bytes) {
-  g_last_error.clear();
-  if (BT <= 0 || H <= 0 || V <= 0) return fail(FLJSD_EINVAL, "sizes must be > 0");
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
-  const int64_t nc = policy_num_chunks_ce(BT, H, V, dtype, budget_bytes);
-  if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the budget");
-  if (nc > INT32_MAX) return fail(FLJSD_EINVAL, "chunk count overflows int");
-  return static_cast<int>(nc);
 }
 
 FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const int64_t* labels,
@@ -784,32 +650,12 @@ FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const
                                              int reduction, int num_chunks, float* loss,
                                              void* grad_X, void* grad_W, void* workspace,
                                              size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  if (!X || !W || !labels || !loss) return fail(FLJSD_EINVAL, "X, W, labels and loss must not be NULL");
-  if (BT <= 0 || H <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT, H and V must be > 0");
-  if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
-  if (dtype != FLJSD_F32 && dtype != FLJSD_BF16) return fail(FLJSD_EDTYPE, "unknown dtype");
-  if (reduction < FLJSD_BATCHMEAN || reduction > FLJSD_NONE)
-    return fail(FLJSD_EDTYPE, "unknown reduction");
-  if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
-    return fail(FLJSD_EINVAL, "label_smoothing must be in [0, 1]");
-  if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
-  const void* ptrs[] = {X, W, loss, grad_X, grad_W, workspace};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return fail(FLJSD_EALIGN, "pointers must be 16-byte aligned");
-  if ((reinterpret_cast<uintptr_t>(labels) & 7u) != 0)
-    return fail(FLJSD_EALIGN, "labels must be 8-byte aligned");
-  if (H % dtype_vec(dtype) != 0) return fail(FLJSD_EALIGN, "H must be a multiple of 16 bytes of elements");
-  int64_t nc = num_chunks;
-  if (nc == 0) {
-    nc = policy_num_chunks_ce(BT, H, V, dtype, workspace_bytes);
-    if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
-  }
-  const CePlan plan = plan_ce_chunks(BT, H, V, dtype, nc);
-  if (!workspace) return fail(FLJSD_EINVAL, "workspace must not be NULL");
-  if (workspace_bytes < plan.total)
-    return fail(FLJSD_EWORKSPACE, "workspace needs " + std::to_string(plan.total) + " bytes");
-  int rc = check_device();
+  clear_last_error();
+  CePlan plan;
+  int rc = check_flce(X, W, labels, BT, H, V, dtype, label_smoothing, reduction, num_chunks, loss,
+                      grad_X, grad_W, workspace, workspace_bytes, &plan);
+  if (rc != FLJSD_OK) return rc;
+  rc = check_device();
   if (rc != FLJSD_OK) return rc;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

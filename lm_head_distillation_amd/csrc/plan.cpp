@@ -2,9 +2,12 @@
 //
 // Chunking follows the pages' per-chunk memory model (Liger-Kernel PR #1352,
 // Details, memory table): one chunk of C rows holds both logits tensors,
-// 2 * C * V * s bytes, and only the per-row loss scales with BT. The policy
-// replaces the cdiv(V, H) heuristic that the same page (Open question 4)
-// calls mis-tuned for JSD: it takes the largest chunk that fits.
+// 2 * C * V * s bytes, and only the per-row loss scales with BT. For bf16 with
+// a weight gradient a third logits-sized region holds dZ^T (written by pass 3,
+// read by the weight-gradient product), 3 * C * V * s in all, plus X_s^T and
+// the per-row statistics. The policy replaces the cdiv(V, H) heuristic that
+// the same page (Open question 4) calls mis-tuned for JSD: it takes the
+// largest chunk that fits.
 #include "plan.h"
 
 #include <algorithm>
@@ -25,7 +28,9 @@ SlicePlan plan_slices(int64_t rows, int64_t V) {
 }
 
 void plan_splitk(int64_t M, int64_t N, int64_t K, int* splitk, int64_t* k_per_split) {
-  const int64_t tiles = cdiv(M, kGemmBM) * cdiv(N, kGemmBN);
+  // Output tiles, capped: only whether they fill the chip matters.
+  const int64_t tm = cdiv(M, kGemmBM), tn = cdiv(N, kGemmBN);
+  const int64_t tiles = tm > (int64_t(1) << 20) || tn > (int64_t(1) << 20) ? (int64_t(1) << 40) : tm * tn;
   // Products of at most 64 rows run 64-row tiles, two workgroups per CU.
   const int64_t target = M <= 64 ? 2 * kGemmTargetBlocks : kGemmTargetBlocks;
   int64_t s = 1;
@@ -61,51 +66,36 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   }
   p.transposed_grad_w = dtype == 1;
   p.ldt = round_up(p.C, kJsdVec);
-  const int64_t zt_elems = p.C * p.ldz;
-  size_t off = 0;
-  p.off_zs = off;
-  off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
-  p.off_zt = off;
-  off = align256(off + static_cast<size_t>(zt_elems * es));
-  p.off_row_loss = off;
-  off = align256(off + static_cast<size_t>(BT) * 4);
-  p.off_stats = off;
-  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 16);
-  p.off_lg = off;
-  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 8);
-  p.off_peak = off;
-  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 16);
-  p.off_ref = off;
-  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 4);
-  p.off_partial = off;
-  if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H_s * 4);
-  p.off_xt = off;
-  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H_s * p.ldt * es));
-  p.off_dzt = off;
-  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(V * p.ldt * es));
+  const int64_t rs = p.C * p.slices.S;   // row-slice pairs of one chunk
+  Layout L;
+  p.off_zs = L.take(p.C, p.ldz, es);
+  p.off_zt = L.take(p.C, p.ldz, es);
+  p.off_row_loss = L.take(BT, 1, 4);
+  p.off_stats = L.take(rs, 1, 16);
+  p.off_lg = L.take(rs, 1, 8);
+  p.off_peak = L.take(rs, 1, 16);
+  p.off_ref = L.take(rs, 1, 4);
+  p.off_partial = L.take(p.splitk > 1 ? p.splitk * p.C : 0, H_s, 4);
+  p.off_xt = L.take(p.transposed_grad_w ? H_s : 0, p.ldt, es);
+  p.off_dzt = L.take(p.transposed_grad_w ? V : 0, p.ldt, es);
   p.gemm_stats = dtype == 1;
   p.stat_tiles = cdiv(V, kGemmBN);
-  p.off_spart = off;
-  if (p.gemm_stats) off = align256(off + static_cast<size_t>(2 * p.C * p.stat_tiles) * 8);
-  p.total = off;
+  p.off_spart = L.take(p.gemm_stats ? 2 * p.C : 0, p.stat_tiles, 8);
+  p.total = L.off;
   return p;
 }
 
 JsdPlan plan_jsd(int64_t BT, int64_t V) {
   JsdPlan p;
   p.slices = plan_slices(BT, V);
-  size_t off = 0;
-  p.off_row_loss = off;
-  off = align256(off + static_cast<size_t>(BT) * 4);
-  p.off_stats = off;
-  off = align256(off + static_cast<size_t>(BT * p.slices.S) * 16);
-  p.off_lg = off;
-  off = align256(off + static_cast<size_t>(BT * p.slices.S) * 8);
-  p.off_peak = off;
-  off = align256(off + static_cast<size_t>(BT * p.slices.S) * 16);
-  p.off_ref = off;
-  off = align256(off + static_cast<size_t>(BT * p.slices.S) * 4);
-  p.total = off;
+  const int64_t rs = BT * p.slices.S;
+  Layout L;
+  p.off_row_loss = L.take(BT, 1, 4);
+  p.off_stats = L.take(rs, 1, 16);
+  p.off_lg = L.take(rs, 1, 8);
+  p.off_peak = L.take(rs, 1, 16);
+  p.off_ref = L.take(rs, 1, 4);
+  p.total = L.off;
   return p;
 }
 
@@ -124,24 +114,16 @@ CePlan plan_ce_chunks(int64_t BT, int64_t H, int64_t V, int dtype, int64_t num_c
     p.k_per_split = V;
   }
   p.transposed_grad_w = dtype == 1;
-  size_t off = 0;
-  p.off_z = off;
-  off = align256(off + static_cast<size_t>(p.C * p.ldz * es));
-  p.off_zt = off;
-  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(V * p.ldt * es));
-  p.off_xt = off;
-  if (p.transposed_grad_w) off = align256(off + static_cast<size_t>(H * p.ldt * es));
-  p.off_row_loss = off;
-  off = align256(off + static_cast<size_t>(BT) * 4);
-  p.off_stats = off;
-  off = align256(off + static_cast<size_t>(p.C * p.slices.S) * 16);
-  p.off_zy = off;
-  off = align256(off + static_cast<size_t>(p.C) * 4);
-  p.off_scale = off;
-  off = align256(off + 16);
-  p.off_partial = off;
-  if (p.splitk > 1) off = align256(off + static_cast<size_t>(p.splitk) * p.C * H * 4);
-  p.total = off;
+  Layout L;
+  p.off_z = L.take(p.C, p.ldz, es);
+  p.off_zt = L.take(p.transposed_grad_w ? V : 0, p.ldt, es);
+  p.off_xt = L.take(p.transposed_grad_w ? H : 0, p.ldt, es);
+  p.off_row_loss = L.take(BT, 1, 4);
+  p.off_stats = L.take(p.C * p.slices.S, 1, 16);
+  p.off_zy = L.take(p.C, 1, 4);
+  p.off_scale = L.take(16, 1, 1);
+  p.off_partial = L.take(p.splitk > 1 ? p.splitk * p.C : 0, H, 4);
+  p.total = L.off;
   return p;
 }
 
@@ -149,7 +131,7 @@ int64_t policy_num_chunks_ce(int64_t BT, int64_t H, int64_t V, int dtype, size_t
   int64_t nc = 1;
   while (nc <= BT) {
     const CePlan p = plan_ce_chunks(BT, H, V, dtype, nc);
-    if (p.total <= budget) return nc;
+    if (p.total != kSizeOverflow && p.total <= budget) return nc;
     if (p.C == 1) break;
     nc = cdiv(BT, p.C - 1);
   }
@@ -162,7 +144,7 @@ int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int d
   int64_t nc = 1;
   while (nc <= BT) {
     ChunkPlan p = plan_chunks(BT, H_s, H_t, V, dtype, nc);
-    if (p.total <= budget) return nc;
+    if (p.total != kSizeOverflow && p.total <= budget) return nc;
     // Next nc that gives a smaller chunk.
     const int64_t C = p.C;
     if (C == 1) break;

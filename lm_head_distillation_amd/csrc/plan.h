@@ -5,6 +5,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <climits>
 
 namespace fljsd {
 
@@ -26,9 +27,33 @@ constexpr int64_t kJsdMinSlice = 4096;
 // Aim for at least this many workgroups in the grad_input GEMM.
 constexpr int64_t kGemmTargetBlocks = 256;
 
-inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+// Largest BT, H or V the planner takes (2^40): with every size at most this,
+// no intermediate of the plan arithmetic overflows int64; workspace totals
+// are summed with saturation at kSizeOverflow.
+constexpr int64_t kMaxPlanDim = int64_t(1) << 40;
+constexpr size_t kSizeOverflow = SIZE_MAX;
+
+// a / b rounded up, for a >= 0, b > 0 (no a + b - 1 that could overflow).
+inline int64_t cdiv(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 inline int64_t round_up(int64_t a, int64_t b) { return cdiv(a, b) * b; }
-inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Workspace layout: regions of n * m * es bytes, each starting 256-byte
+// aligned; the total saturates at kSizeOverflow instead of wrapping.
+struct Layout {
+  size_t off = 0;
+  size_t take(int64_t n, int64_t m, int64_t es) {
+    const size_t at = off;
+    size_t bytes = 0;
+    if (off == kSizeOverflow || __builtin_mul_overflow(static_cast<size_t>(n), static_cast<size_t>(m), &bytes) ||
+        __builtin_mul_overflow(bytes, static_cast<size_t>(es), &bytes) ||
+        __builtin_add_overflow(off, bytes, &off) || off > kSizeOverflow - 255) {
+      off = kSizeOverflow;
+      return kSizeOverflow;
+    }
+    off = (off + 255) & ~size_t(255);
+    return at;
+  }
+};
 
 inline int dtype_size(int dtype) { return dtype == 0 ? 4 : 2; }
 // Elements per 16-byte vector for the dtype.
@@ -49,9 +74,9 @@ struct ChunkPlan {
   int64_t C = 0;          // rows per chunk
   int64_t n_chunks = 0;   // chunks actually run: ceil(BT / C)
   int64_t ldz = 0;        // row stride (elements) of the logits chunk buffers
-  // bf16 with a weight gradient: dZ^T [V, ldt] reuses the teacher-logits
-  // buffer once the loss passes are done, and X_s^T [H_s, ldt] has its own
-  // region, so grad_W = dZ^T X_s reads both operands with K (rows) fastest.
+  // bf16: dZ^T [V, ldt] and X_s^T [H_s, ldt] have regions of their own, so
+  // grad_W = dZ^T X_s reads both operands with K (rows) fastest. dZ^T cannot
+  // share the teacher-logits buffer: pass 3 writes it while it still reads Z_t.
   bool transposed_grad_w = false;
   int64_t ldt = 0;        // row stride of the transposed operands: C rounded up to 8
   // bf16: the logits GEMMs reduce each row's statistics per N-tile into

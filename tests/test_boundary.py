@@ -144,20 +144,25 @@ def test_policy_smallest_count_that_fits(lib):
 
 # ---- argument checks before any device work --------------------------------------------
 
-def fb(lib, **over):
-    """A call to fljsd_forward_backward with fake pointers; callers always
-    override at least one argument to make it invalid."""
-    a = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
+# Valid arguments of each entry point (fake, never dereferenced pointers).
+FB_ARGS = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
              beta=0.5, T=1.0, reduction=0, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, ws=FAKE,
              ws_bytes=1 << 30, stream=None)
-    a.update(over)
-    return lib.fljsd_forward_backward(a["X_s"], a["W_s"], a["X_t"], a["W_t"], a["BT"], a["H_s"],
-                                      a["H_t"], a["V"], a["dtype"], a["beta"], a["T"],
-                                      a["reduction"], a["nc"], a["loss"], a["gX"], a["gW"], a["ws"],
-                                      a["ws_bytes"], a["stream"])
+FBX_ARGS = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
+             beta=0.5, T=1.0, reduction=0, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, gw_dtype=BF16,
+             flags=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+JSD_ARGS = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
+             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+NOALLOC_ARGS = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
+             loss=FAKE, grad=FAKE, stream=None)
+ELEM_ARGS = dict(a=FAKE, b=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, reduction=0,
+             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+FLCE_ARGS = dict(X=FAKE, W=FAKE, labels=FAKE, BT=8, H=64, V=512, dtype=BF16, ignore=-100, eps=0.0,
+             reduction=2, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
 
-
-@pytest.mark.parametrize("over,code", [
+# Invalid-argument cases: (overrides of a valid call, status code). The host-only
+# sanitizer test runs the same cases through the checks built under ASan/UBSan.
+FB_CASES = [
     (dict(X_s=None), EINVAL), (dict(W_t=None), EINVAL), (dict(loss=None), EINVAL),
     (dict(BT=0), EINVAL), (dict(V=-3), EINVAL), (dict(H_t=0), EINVAL),
     (dict(beta=1.5), EINVAL), (dict(beta=-0.1), EINVAL), (dict(beta=float("nan")), EINVAL),
@@ -168,7 +173,61 @@ def fb(lib, **over):
     (dict(H_s=60), EALIGN), (dict(dtype=F32, H_t=66), EALIGN),
     (dict(ws_bytes=100), EWORKSPACE), (dict(nc=0, ws_bytes=100), EWORKSPACE),
     (dict(ws=None), EINVAL),
-])
+]
+
+FBX_CASES = [
+    (dict(gw_dtype=2), EDTYPE), (dict(gw_dtype=-1), EDTYPE),
+    (dict(dtype=F32, gw_dtype=BF16), EDTYPE),
+    (dict(flags=4), EINVAL), (dict(flags=0x80000001), EINVAL), (dict(flags=3, X_s=None), EINVAL),
+    (dict(gw_dtype=F32, X_s=None), EINVAL), (dict(gw_dtype=F32, flags=1, ws_bytes=100), EWORKSPACE),
+    (dict(gw_dtype=F32, gW=FAKE + 8), EALIGN),
+]
+
+JSD_CASES = [
+    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
+    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
+    (dict(grad=FAKE + 2), EALIGN), (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
+]
+
+NOALLOC_CASES = [
+    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
+    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
+    (dict(grad=FAKE + 2), EALIGN),
+    # Past the 8 MiB scratch array: 400,000 rows need 19.2 MB of row statistics.
+    (dict(BT=400_000, V=1000, ld=1000), EWORKSPACE),
+]
+
+ELEM_CASES = [
+    (dict(a=None), EINVAL), (dict(b=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
+    (dict(V=-1), EINVAL), (dict(ld=100), EINVAL), (dict(dtype=3), EDTYPE),
+    (dict(reduction=9), EDTYPE), (dict(b=FAKE + 2), EALIGN), (dict(grad=FAKE + 4), EALIGN),
+    (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
+]
+
+FLCE_CASES = [
+    (dict(X=None), EINVAL), (dict(labels=None), EINVAL), (dict(loss=None), EINVAL),
+    (dict(BT=0), EINVAL), (dict(H=-1), EINVAL), (dict(V=0), EINVAL), (dict(eps=-0.1), EINVAL),
+    (dict(eps=1.5), EINVAL), (dict(eps=float("nan")), EINVAL), (dict(nc=-2), EINVAL),
+    (dict(dtype=5), EDTYPE), (dict(reduction=4), EDTYPE), (dict(X=FAKE + 8), EALIGN),
+    (dict(labels=FAKE + 4), EALIGN), (dict(gW=FAKE + 2), EALIGN), (dict(H=60), EALIGN),
+    (dict(ws_bytes=64), EWORKSPACE), (dict(nc=0, ws_bytes=64), EWORKSPACE), (dict(ws=None), EINVAL),
+]
+
+
+def fb(lib, **over):
+    """A call to fljsd_forward_backward with fake pointers; callers always
+    override at least one argument to make it invalid."""
+    a = dict(FB_ARGS)
+    a.update(over)
+    return lib.fljsd_forward_backward(a["X_s"], a["W_s"], a["X_t"], a["W_t"], a["BT"], a["H_s"],
+                                      a["H_t"], a["V"], a["dtype"], a["beta"], a["T"],
+                                      a["reduction"], a["nc"], a["loss"], a["gX"], a["gW"], a["ws"],
+                                      a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", FB_CASES)
 def test_forward_backward_rejects(lib, over, code):
     assert fb(lib, **over) == code
     assert lib.fljsd_last_error()
@@ -177,9 +236,7 @@ def test_forward_backward_rejects(lib, over, code):
 def fbx(lib, **over):
     """fljsd_forward_backward_ex with fake pointers; always at least one
     invalid argument."""
-    a = dict(X_s=FAKE, W_s=FAKE, X_t=FAKE, W_t=FAKE, BT=8, H_s=64, H_t=64, V=512, dtype=BF16,
-             beta=0.5, T=1.0, reduction=0, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, gw_dtype=BF16,
-             flags=0, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a = dict(FBX_ARGS)
     a.update(over)
     return lib.fljsd_forward_backward_ex(a["X_s"], a["W_s"], a["X_t"], a["W_t"], a["BT"], a["H_s"],
                                          a["H_t"], a["V"], a["dtype"], a["beta"], a["T"],
@@ -188,54 +245,34 @@ def fbx(lib, **over):
                                          a["stream"])
 
 
-@pytest.mark.parametrize("over,code", [
-    (dict(gw_dtype=2), EDTYPE), (dict(gw_dtype=-1), EDTYPE),
-    (dict(dtype=F32, gw_dtype=BF16), EDTYPE),
-    (dict(flags=4), EINVAL), (dict(flags=0x80000001), EINVAL), (dict(flags=3, X_s=None), EINVAL),
-    (dict(gw_dtype=F32, X_s=None), EINVAL), (dict(gw_dtype=F32, flags=1, ws_bytes=100), EWORKSPACE),
-    (dict(gw_dtype=F32, gW=FAKE + 8), EALIGN),
-])
+@pytest.mark.parametrize("over,code", FBX_CASES)
 def test_forward_backward_ex_rejects(lib, over, code):
     assert fbx(lib, **over) == code
     assert lib.fljsd_last_error()
 
 
 def jsd(lib, **over):
-    a = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
-             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a = dict(JSD_ARGS)
     a.update(over)
     return lib.fljsd_generalized_jsd(a["zs"], a["zt"], a["BT"], a["V"], a["ld"], a["dtype"],
                                      a["beta"], a["T"], a["reduction"], a["loss"], a["grad"],
                                      a["ws"], a["ws_bytes"], a["stream"])
 
 
-@pytest.mark.parametrize("over,code", [
-    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
-    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
-    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
-    (dict(grad=FAKE + 2), EALIGN), (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
-])
+@pytest.mark.parametrize("over,code", JSD_CASES)
 def test_generalized_jsd_rejects(lib, over, code):
     assert jsd(lib, **over) == code
 
 
 def jsd_noalloc(lib, **over):
-    a = dict(zs=FAKE, zt=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, T=1.0, reduction=0,
-             loss=FAKE, grad=FAKE, stream=None)
+    a = dict(NOALLOC_ARGS)
     a.update(over)
     return lib.fljsd_generalized_jsd_noalloc(a["zs"], a["zt"], a["BT"], a["V"], a["ld"], a["dtype"],
                                              a["beta"], a["T"], a["reduction"], a["loss"], a["grad"],
                                              a["stream"])
 
 
-@pytest.mark.parametrize("over,code", [
-    (dict(zs=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
-    (dict(V=0), EINVAL), (dict(ld=511), EINVAL), (dict(beta=2.0), EINVAL), (dict(T=0.0), EINVAL),
-    (dict(dtype=9), EDTYPE), (dict(reduction=7), EDTYPE), (dict(zt=FAKE + 1), EALIGN),
-    (dict(grad=FAKE + 2), EALIGN),
-    # Past the 8 MiB scratch array: 400,000 rows need 19.2 MB of row statistics.
-    (dict(BT=400_000, V=1000, ld=1000), EWORKSPACE),
-])
+@pytest.mark.parametrize("over,code", NOALLOC_CASES)
 def test_generalized_jsd_noalloc_rejects(lib, over, code):
     """The no-allocation entry point checks everything, its scratch bound
     included, before any HIP call (so these run without a GPU)."""
@@ -255,8 +292,7 @@ def test_noalloc_scratch_bound_matches_header(lib):
 
 
 def elem(lib, fn, **over):
-    a = dict(a=FAKE, b=FAKE, BT=8, V=512, ld=512, dtype=BF16, beta=0.5, reduction=0,
-             loss=FAKE, grad=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a = dict(ELEM_ARGS)
     a.update(over)
     if fn == "logprob":
         return lib.fljsd_jsd_logprob(a["a"], a["b"], a["BT"], a["V"], a["ld"], a["dtype"], a["beta"],
@@ -267,20 +303,14 @@ def elem(lib, fn, **over):
 
 
 @pytest.mark.parametrize("fn", ["logprob", "tvd"])
-@pytest.mark.parametrize("over,code", [
-    (dict(a=None), EINVAL), (dict(b=None), EINVAL), (dict(loss=None), EINVAL), (dict(BT=0), EINVAL),
-    (dict(V=-1), EINVAL), (dict(ld=100), EINVAL), (dict(dtype=3), EDTYPE),
-    (dict(reduction=9), EDTYPE), (dict(b=FAKE + 2), EALIGN), (dict(grad=FAKE + 4), EALIGN),
-    (dict(ws_bytes=8), EWORKSPACE), (dict(ws=None), EINVAL),
-])
+@pytest.mark.parametrize("over,code", ELEM_CASES)
 def test_elementwise_losses_reject(lib, fn, over, code):
     assert elem(lib, fn, **over) == code
     assert lib.fljsd_last_error()
 
 
 def flce(lib, **over):
-    a = dict(X=FAKE, W=FAKE, labels=FAKE, BT=8, H=64, V=512, dtype=BF16, ignore=-100, eps=0.0,
-             reduction=2, nc=1, loss=FAKE, gX=FAKE, gW=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a = dict(FLCE_ARGS)
     a.update(over)
     return lib.fljsd_flce_forward_backward(a["X"], a["W"], a["labels"], a["BT"], a["H"], a["V"],
                                            a["dtype"], a["ignore"], a["eps"], a["reduction"], a["nc"],
@@ -288,14 +318,7 @@ def flce(lib, **over):
                                            a["stream"])
 
 
-@pytest.mark.parametrize("over,code", [
-    (dict(X=None), EINVAL), (dict(labels=None), EINVAL), (dict(loss=None), EINVAL),
-    (dict(BT=0), EINVAL), (dict(H=-1), EINVAL), (dict(V=0), EINVAL), (dict(eps=-0.1), EINVAL),
-    (dict(eps=1.5), EINVAL), (dict(eps=float("nan")), EINVAL), (dict(nc=-2), EINVAL),
-    (dict(dtype=5), EDTYPE), (dict(reduction=4), EDTYPE), (dict(X=FAKE + 8), EALIGN),
-    (dict(labels=FAKE + 4), EALIGN), (dict(gW=FAKE + 2), EALIGN), (dict(H=60), EALIGN),
-    (dict(ws_bytes=64), EWORKSPACE), (dict(nc=0, ws_bytes=64), EWORKSPACE), (dict(ws=None), EINVAL),
-])
+@pytest.mark.parametrize("over,code", FLCE_CASES)
 def test_flce_rejects(lib, over, code):
     assert flce(lib, **over) == code
     assert lib.fljsd_last_error()

@@ -1,0 +1,185 @@
+"""The library's argument checks and planning arithmetic, built host-only
+(plain g++, no HIP) under AddressSanitizer and UndefinedBehaviorSanitizer and
+run on the CPU: every invalid-argument case of the boundary tests gives the
+status code the real library gives, and the workspace and chunk-policy
+arithmetic stays defined (no signed overflow, no wrap) at extreme sizes.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+from tests import test_boundary as tb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "lm_head_distillation_amd", "csrc")
+SOURCES = [os.path.join(CSRC, "validate.cpp"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(ROOT, "tests", "host_checks", "validate_driver.cpp")]
+BIG = 1 << 40            # the planner's largest size
+U64 = (1 << 64) - 1
+
+
+@pytest.fixture(scope="module")
+def driver(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not found")
+    out = str(tmp_path_factory.mktemp("host") / "validate_driver")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-Wall", "-Wextra", "-Werror",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC] + SOURCES + ["-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    return out
+
+
+def run(driver, lines):
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:halt_on_error=1",
+               UBSAN_OPTIONS="print_stacktrace=1:halt_on_error=1")
+    res = subprocess.run([driver], input="\n".join(lines) + "\n", capture_output=True, text=True,
+                         env=env, timeout=120)
+    if "LeakSanitizer has encountered a fatal error" in res.stderr:
+        env["ASAN_OPTIONS"] = "detect_leaks=0:halt_on_error=1"
+        res = subprocess.run([driver], input="\n".join(lines) + "\n", capture_output=True,
+                             text=True, env=env, timeout=120)
+    assert res.returncode == 0, res.stderr[-4000:]
+    assert "runtime error" not in res.stderr and "Sanitizer" not in res.stderr, res.stderr[-4000:]
+    out = [int(x) for x in res.stdout.split()]
+    assert len(out) == len(lines)
+    return out
+
+
+def _p(x):
+    return 0 if x is None else int(x)
+
+
+def _f(x):
+    return repr(float(x))
+
+
+def fb_line(a, ex):
+    gwd = a.get("gw_dtype", a["dtype"])
+    flags = a.get("flags", 0)
+    return " ".join(["fb"] + [str(_p(a[k])) for k in ("X_s", "W_s", "X_t", "W_t")] +
+                    [str(a[k]) for k in ("BT", "H_s", "H_t", "V", "dtype")] +
+                    [_f(a["beta"]), _f(a["T"]), str(a["reduction"]), str(a["nc"])] +
+                    [str(_p(a[k])) for k in ("loss", "gX", "gW")] +
+                    [str(gwd), str(flags), str(_p(a["ws"])), str(a["ws_bytes"])])
+
+
+def jsd_line(a, op="jsd"):
+    words = [op, str(_p(a["zs"])), str(_p(a["zt"])), str(a["BT"]), str(a["V"]), str(a["ld"]),
+             str(a["dtype"]), _f(a["beta"]), _f(a["T"]), str(a["reduction"]), str(_p(a["loss"])),
+             str(_p(a["grad"]))]
+    if op == "jsd":
+        words += [str(_p(a["ws"])), str(a["ws_bytes"])]
+    return " ".join(words)
+
+
+def elem_line(a, fn):
+    return " ".join(["elem", "0" if fn == "logprob" else "1", str(_p(a["a"])), str(_p(a["b"])),
+                     str(a["BT"]), str(a["V"]), str(a["ld"]), str(a["dtype"]), _f(a["beta"]),
+                     str(a["reduction"]), str(_p(a["loss"])), str(_p(a["grad"])), str(_p(a["ws"])),
+                     str(a["ws_bytes"])])
+
+
+def flce_line(a):
+    return " ".join(["flce", str(_p(a["X"])), str(_p(a["W"])), str(_p(a["labels"])), str(a["BT"]),
+                     str(a["H"]), str(a["V"]), str(a["dtype"]), _f(a["eps"]), str(a["reduction"]),
+                     str(a["nc"]), str(_p(a["loss"])), str(_p(a["gX"])), str(_p(a["gW"])),
+                     str(_p(a["ws"])), str(a["ws_bytes"])])
+
+
+def test_boundary_cases_match_the_library(driver):
+    """Every invalid-argument case of the boundary tests, through the
+    sanitized checks: the same status code as the library's entry point."""
+    from lm_head_distillation_amd import fljsd
+    lib = fljsd.load_library()
+    lines, expect = [], []
+    for over, code in tb.FB_CASES:
+        lines.append(fb_line(dict(tb.FB_ARGS, **over), False))
+        expect.append(code)
+        assert tb.fb(lib, **over) == code
+    for over, code in tb.FBX_CASES:
+        lines.append(fb_line(dict(tb.FBX_ARGS, **over), True))
+        expect.append(code)
+        assert tb.fbx(lib, **over) == code
+    for over, code in tb.JSD_CASES:
+        lines.append(jsd_line(dict(tb.JSD_ARGS, **over)))
+        expect.append(code)
+        assert tb.jsd(lib, **over) == code
+    for over, code in tb.NOALLOC_CASES:
+        lines.append(jsd_line(dict(tb.NOALLOC_ARGS, **over), "noalloc"))
+        expect.append(code)
+        assert tb.jsd_noalloc(lib, **over) == code
+    for fn in ("logprob", "tvd"):
+        for over, code in tb.ELEM_CASES:
+            lines.append(elem_line(dict(tb.ELEM_ARGS, **over), fn))
+            expect.append(code)
+            assert tb.elem(lib, fn, **over) == code
+    lines.append(elem_line(dict(tb.ELEM_ARGS, beta=1.5), "logprob"))
+    expect.append(tb.EINVAL)
+    for over, code in tb.FLCE_CASES:
+        lines.append(flce_line(dict(tb.FLCE_ARGS, **over)))
+        expect.append(code)
+        assert tb.flce(lib, **over) == code
+    # And the valid calls themselves pass every check.
+    lines += [fb_line(tb.FB_ARGS, False), jsd_line(tb.JSD_ARGS), jsd_line(tb.NOALLOC_ARGS, "noalloc"),
+              elem_line(tb.ELEM_ARGS, "tvd"), flce_line(tb.FLCE_ARGS)]
+    expect += [tb.OK] * 5
+    assert run(driver, lines) == expect
+
+
+def test_planning_arithmetic_at_extreme_sizes(driver):
+    """Workspace sizes and chunk policies at the edges of what the planner
+    takes: sizes up to 2^40 per dimension, products far past 2^64 bytes (the
+    total saturates and is reported as 0 / no fit), budgets of 0 and 2^64 - 1.
+    Each answer equals the library's, and the sanitizers see no overflow."""
+    from lm_head_distillation_amd import fljsd
+    lib = fljsd.load_library()
+    ws_cases = [
+        (8192, 4096, 4096, 128256, 1, 1), (8192, 4096, 4096, 128256, 1, 32),
+        (2**31 - 1, 8, 8, 2**31 - 1, 1, 1), (2**31 - 1, 8, 8, 2**31 - 1, 0, 7),
+        (BIG, BIG, BIG, BIG, 1, 1), (BIG, 8, 8, BIG, 0, 2**31 - 1), (BIG + 1, 8, 8, 8, 1, 1),
+        (1, 1, 1, 1, 0, 1), (1, BIG, 1, BIG, 1, 1), (2**62, 8, 8, 8, 1, 1), (8, 8, 8, 2**63 - 1, 1, 1),
+        (5, 8, 8, 9, 1, 2**31 - 1),
+    ]
+    gws_cases = [(2**31 - 1, 2**31 - 1, 1), (BIG, BIG, 0), (BIG + 1, 5, 1), (1, 1, 1), (2**63 - 1, 2, 1)]
+    plan_cases = [
+        (8192, 4096, 4096, 128256, 1, U64), (8192, 4096, 4096, 128256, 1, 0),
+        (8192, 4096, 4096, 128256, 1, 1 << 33), (BIG, 8, 8, 8, 1, U64), (BIG, BIG, BIG, BIG, 1, U64),
+        (2**62, 8, 8, 8, 1, U64), (1000003, 8, 8, 1000003, 0, 1 << 30),
+    ]
+    flce_ws = [(8192, 4096, 128256, 1, 1), (BIG, BIG, BIG, 1, 1), (2**31 - 1, 8, 2**31 - 1, 0, 3)]
+    flce_plan = [(8192, 4096, 128256, 1, 1 << 33), (BIG, BIG, BIG, 1, U64), (100000, 8, 100000, 0, 1 << 26)]
+    lines, expect = [], []
+    for c in ws_cases:
+        lines.append("ws " + " ".join(map(str, c)))
+        expect.append(lib.fljsd_workspace_size(*c))
+    for c in gws_cases:
+        lines.append("gws " + " ".join(map(str, c)))
+        expect.append(lib.fljsd_generalized_jsd_workspace_size(*c))
+    for c in plan_cases:
+        lines.append("plan " + " ".join(map(str, c)))
+        expect.append(lib.fljsd_plan_num_chunks(*c))
+    for c in flce_ws:
+        lines.append("flcews " + " ".join(map(str, c)))
+        expect.append(lib.fljsd_flce_workspace_size(*c))
+    for c in flce_plan:
+        lines.append("flceplan " + " ".join(map(str, c)))
+        expect.append(lib.fljsd_flce_plan_num_chunks(*c))
+    got = run(driver, lines)
+    assert got == expect
+    ws = dict(zip(lines, got))
+    assert ws["ws 8192 4096 4096 128256 1 1"] > 6e9
+    assert ws[f"ws {BIG} {BIG} {BIG} {BIG} 1 1"] == 0          # saturated: does not fit
+    assert ws[f"ws {BIG + 1} 8 8 8 1 1"] == 0                  # past the planner's sizes
+    assert ws["plan 8192 4096 4096 128256 1 0"] == tb.EWORKSPACE
+    # 2^40 rows of a 2^40 vocabulary: one chunk overflows size_t, but a count
+    # of ~5e5 chunks fits in a 2^64 - 1 byte budget.
+    assert ws[f"plan {BIG} {BIG} {BIG} {BIG} 1 {U64}"] > 1
+    assert ws[f"ws {BIG} {BIG} {BIG} {BIG} 1 1"] == 0
+    assert ws[f"plan {2**62} 8 8 8 1 {U64}"] == tb.EINVAL
