@@ -151,13 +151,27 @@ int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int
               [&] { return launch_jsd_stats(ja, dtype, s); });
   }
   if (e != hipSuccess) return fail_hip(e, "launch jsd_stats");
-  e = timed(s, FLJSD_KCLASS_JSD_LOSS, 0.0, 2 * row_bytes,
-            [&] { return launch_jsd_loss(ja, dtype, s); });
-  if (e != hipSuccess) return fail_hip(e, "launch jsd_loss");
+  // bf16 with the transposed gradient: pass 3 also sums the loss terms (not
+  // the reverse KL, whose row loss is its G), so pass 2 computes only G, and
+  // the forward KL, which needs no G, has no pass 2.
+  const bool loss_in_pass3 = write_grad && dzt && ja.mode != kModeReverseKL;
+  if (!(loss_in_pass3 && ja.mode == kModeForwardKL)) {
+    e = timed(s, FLJSD_KCLASS_JSD_LOSS, 0.0, 2 * row_bytes, [&] {
+      return loss_in_pass3 ? launch_jsd_gsum(ja, s) : launch_jsd_loss(ja, dtype, s);
+    });
+    if (e != hipSuccess) return fail_hip(e, "launch jsd_loss");
+  }
   if (write_grad && dzt) {
     e = timed(s, FLJSD_KCLASS_JSD_GRAD, 0.0, 4 * row_bytes,
-              [&] { return launch_jsd_grad_transposed(ja, dzt, ldt, s); });
+              [&] { return launch_jsd_grad_transposed(ja, dzt, ldt, loss_in_pass3, s); });
     if (e != hipSuccess) return fail_hip(e, "launch jsd_grad");
+    if (loss_in_pass3) {
+      int64_t span = 0, nblk = 0;
+      grad_t_geometry(ja.rows, V, &span, &nblk);
+      e = timed(s, FLJSD_KCLASS_LOSS_REDUCE, 0.0, 4.0 * ja.rows * (nblk + 1),
+                [&] { return launch_jsd_row_loss_merge(ja, s); });
+      if (e != hipSuccess) return fail_hip(e, "launch row loss merge");
+    }
   } else if (write_grad) {
     e = timed(s, FLJSD_KCLASS_JSD_GRAD, 0.0, 3 * row_bytes,
               [&] { return launch_jsd_grad(ja, dtype, s); });
@@ -388,6 +402,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
   ja.lg = reinterpret_cast<float2*>(ws + plan.off_lg);
   ja.peak = reinterpret_cast<float4*>(ws + plan.off_peak);
   ja.ref = reinterpret_cast<float*>(ws + plan.off_ref);
+  ja.lpart = reinterpret_cast<float*>(ws + plan.off_lpart);
 
   const char* Xs = static_cast<const char*>(X_s);
   const char* Xt = static_cast<const char*>(X_t);

@@ -43,6 +43,7 @@
 // as their argument goes to 0.
 #include "elem_math.h"
 #include "kernels.h"
+#include "plan.h"
 
 #include <hip/hip_runtime.h>
 
@@ -71,14 +72,14 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
   Q = hw_exp2(as);
   P = hw_exp2(at);
   if constexpr (DIRECT && MODE == kModeGeneralized) {
-    // A tie (P == Q, including masked columns, where both are 0 and D is NaN)
-    // selects zeros over whatever the terms evaluated to. (Evaluating a tie at
-    // D = 0 instead, with no branch, measured 7% slower.)
+    // A tie (equal log-probabilities, so P == Q; masked columns, both -inf,
+    // included) selects zeros over whatever the terms evaluated to.
+    // (Evaluating a tie at D = 0 instead, with no branch, measured 7% slower.)
     const float t = at - as;
     const float D = t * kLn2;
     float r, dmr;
     jsd_r_direct(D, t, beta, r, dmr);
-    const bool tie = P == Q;
+    const bool tie = as == at;
     l = tie ? 0.f : beta * P * dmr - (1.f - beta) * Q * r;
     g = tie ? 0.f : -(1.f - beta) * Q * r;
     gacc = g;
@@ -110,6 +111,20 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
     g = -(1.f - beta) * Q * r;
     gacc = g;
   }
+}
+
+// The bf16 generalized term of G (both pass-2 kernels, so that G does not
+// depend on which outputs were asked for): gsum += g with
+// g = -(1 - beta) Q ln(beta 2^t + 1 - beta), t = a_t - a_s clamped at 64
+// (beyond it Q < 2^-64 P and the term is below any G); a tie (equal
+// log-probabilities, or a masked column) adds 0. One exponential and one log
+// from r's definition: G only enters dA = g - Q G, where an absolute error of
+// a few 1e-7 in r is far below what the bf16 logits' own rounding (2^-9 of
+// each logit, over T) does, and these passes are VALU-bound. The explicit
+// fmaf keeps the compiler from contracting differently in the two kernels.
+__device__ inline float gsum_plain(float gsum, float as, float at, float Q, float beta, float cg) {
+  const float u = fmaf(beta, hw_exp2(fminf(at - as, 64.f)), 1.f - beta);
+  return fmaf(as == at ? 0.f : Q, hw_log2(u) * cg, gsum);
 }
 
 // Row statistics from the S pass-1 partials, merged in slice order by one
@@ -293,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   }
   const float k = a.k2;
   const BetaWeights bw = beta_weights(a.beta);
+  const float cg = -(1.f - a.beta) * kLn2;
   // fp32 forward KL also sums Q and P over the elements below the student's
   // maximum and counts the elements at it, for pass 3's peak rewrite.
   constexpr bool kPeak = sizeof(T) == 4 && MODE == kModeForwardKL;
@@ -311,7 +327,10 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
       jsd_terms<MODE, sizeof(T) == 2>(as, at, a.beta, Q, P, l, g, gacc, &bw);
       if constexpr (kShift) gacc = shifted_g<MODE>(rs, ys[i], yt[i], at - as, Q, P, k, a.beta);
       lsum += l;
-      gsum += gacc;
+      if constexpr (sizeof(T) == 2 && MODE == kModeGeneralized)
+        gsum = gsum_plain(gsum, as, at, Q, a.beta, cg);
+      else
+        gsum += gacc;
       if constexpr (kPeak) {
         const bool rest = ys[i] < L.x;
         qrest += rest ? Q : 0.f;
@@ -528,23 +547,73 @@ hipError_t launch_loss_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
+// bf16 terms of the fused pass with the loss moved into pass 3: a tie is
+// equality of the two log2-probabilities (then P == Q, and masked columns,
+// where both are -inf, count as ties too). Returns g, the term of
+// dA = g - Q G (generalized), and Q, r and D - r for the loss.
+__device__ inline float g_direct(float as, float at, float beta, float& Q, float& r, float& dmr) {
+  Q = hw_exp2(as);
+  const float t = at - as;
+  jsd_r_direct(t * kLn2, t, beta, r, dmr);
+  return as == at ? 0.f : -(1.f - beta) * Q * r;
+}
+
+// Pass 2 when pass 3 computes the loss (bf16, generalized branch): only the
+// cross-column sum G = sum_v g per (row, slice), into lg[.].y (lg[.].x = 0);
+// the loss, which needs the accurate small-t form of r, is summed in pass 3.
+__global__ __launch_bounds__(kThreads) void jsd_gsum_kernel(JsdArgs a) {
+  const int64_t row = blockIdx.x;
+  const int s = blockIdx.y;
+  const int64_t v0 = static_cast<int64_t>(s) * a.slice_w;
+  const int64_t v1 = min(a.V, v0 + a.slice_w);
+  const uint16_t* zs = static_cast<const uint16_t*>(a.zs) + row * a.ld;
+  const uint16_t* zt = static_cast<const uint16_t*>(a.zt) + row * a.ld;
+  const float4 L = row_log_norms(a, row);
+  const float k = a.k2;
+  const float cg = -(1.f - a.beta) * kLn2;
+  float gsum = 0.f;
+  for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
+    const int n = static_cast<int>(min<int64_t>(8, v1 - v));
+    float ys[8], yt[8];
+    load8(zs, v, n, a.vec_ok, ys);
+    load8(zt, v, n, a.vec_ok, yt);
+    // Columns past the row end load as -inf in both rows: a tie, adding 0.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
+      gsum = gsum_plain(gsum, as, at, hw_exp2(as), a.beta, cg);
+    }
+  }
+  gsum = wave_sum(gsum);
+  __shared__ float sh[kWaves];
+  const int wave = threadIdx.x / 64;
+  if ((threadIdx.x & 63) == 0) sh[wave] = gsum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float acc = sh[0];
+    for (int w = 1; w < kWaves; ++w) acc += sh[w];
+    a.lg[row * a.S + s] = make_float2(0.f, acc);
+  }
+}
+
 // Pass 3 over 64-row x 64-column tiles, bf16: dZ written in place as by
 // jsd_grad_kernel, and the same tile, transposed through LDS, to
 // dzt [V, ldt] for the weight-gradient product. A workgroup covers 64 rows and
-// `span` columns (a multiple of 64, smaller when there are few rows so the
-// launch still fills the chip); threads 0..63 first merge their row's
+// `span` columns (grad_t_span); threads 0..63 first merge their row's
 // statistics and pass-2 partials. In the LDS tile, 16-byte chunk c of row r
 // sits at c ^ ((r / 8) % 8), so both the row-wise writes and the column-wise
-// reads are free of bank conflicts.
-constexpr int64_t kTileColsMax = 1024;
-constexpr int64_t kGradTargetBlocks = 2048;
-
-template <int MODE>
+// reads are free of bank conflicts; two tile buffers alternate, so one
+// barrier per tile suffices (a buffer is rewritten only after every thread
+// has passed the barrier that follows its last read).
+// LOSS (generalized and forward KL): the per-element loss terms are summed
+// here instead of in pass 2, per row over the workgroup's columns, into
+// lpart [column block][rows]; jsd_row_loss_merge_kernel adds them up.
+template <int MODE, bool LOSS>
 __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_t* dzt,
                                                              int64_t ldt, int64_t span) {
   __shared__ float4 sh_L[64];
   __shared__ float sh_G[64];
-  __shared__ uint4 tile[64][8];
+  __shared__ uint4 tile[2][64][8];
   const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64;
   const int64_t c_begin = static_cast<int64_t>(blockIdx.x) * span;
   const int64_t c_end = min(a.V, c_begin + span);
@@ -561,14 +630,16 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         md_merge(acc.z, acc.w, st[s].z, st[s].w, a.k2);
       }
       L = make_float4(acc.x, hw_log2(acc.y), acc.z, hw_log2(acc.w));
-      const float2* lg = a.lg + row * a.S;
-      float2 sum = lg[0];
-      for (int j = 1; j < a.S; ++j) {
-        sum.x += lg[j].x;
-        sum.y += lg[j].y;
+      if (MODE != kModeForwardKL) {
+        const float2* lg = a.lg + row * a.S;
+        float2 sum = lg[0];
+        for (int j = 1; j < a.S; ++j) {
+          sum.x += lg[j].x;
+          sum.y += lg[j].y;
+        }
+        G = sum.y;
+        if (!LOSS && blockIdx.x == 0) a.row_loss[row] = sum.x * a.row_scale;
       }
-      G = sum.y;
-      if (blockIdx.x == 0) a.row_loss[row] = sum.x * a.row_scale;
     }
     sh_L[t] = L;
     sh_G[t] = G;
@@ -578,6 +649,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
   const uint16_t* zt = static_cast<const uint16_t*>(a.zt);
   uint16_t* gr = static_cast<uint16_t*>(a.grad);
   const float k = a.k2;
+  const float beta = a.beta;
   // Row-major: thread -> (row, 8-column chunk) for rows t/8 and t/8 + 32.
   // Whole 16-byte groups of both rows (and of the next 64-column tile) are
   // loaded before any of this tile is computed: dZ goes over the student
@@ -597,9 +669,89 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
       }
     }
   };
+  float lsum[2] = {0.f, 0.f};
+  // The dZ of 8 logits of one row, and its loss terms into *ls.
+  auto elem8 = [&](const uint4& qs, const uint4& qt, const float4& L, float G, float& ls) {
+    const uint32_t ws[4] = {qs.x, qs.y, qs.z, qs.w};
+    const uint32_t wt[4] = {qt.x, qt.y, qt.z, qt.w};
+    float out[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float zsv = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
+      const float ztv = (i & 1) ? bf16_hi(wt[i >> 1]) : bf16_lo(wt[i >> 1]);
+      const float as = (zsv - L.x) * k - L.y, at = (ztv - L.z) * k - L.w;
+      float dA, l = 0.f;
+      if constexpr (LOSS && MODE == kModeGeneralized) {
+        float Q, r, dmr;
+        const float g = g_direct(as, at, beta, Q, r, dmr);
+        dA = g - Q * G;
+        l = as == at ? 0.f : beta * hw_exp2(at) * dmr - (1.f - beta) * Q * r;
+      } else {
+        float Q, P, g, gacc;
+        jsd_terms<MODE, true>(as, at, beta, Q, P, l, g, gacc);
+        dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+      }
+      out[i] = dA * a.grad_scale;
+      if constexpr (LOSS) ls += l;
+    }
+    return make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
+                      pack_bf16x2(out[4], out[5]), pack_bf16x2(out[6], out[7]));
+  };
+  // Interior workgroups (64 whole rows, every column tile whole, 16-byte
+  // rows): a loop with no bounds checks over pointers advanced per tile.
+  const bool interior = a.vec_ok && r0 + 64 <= a.rows && c_end - c_begin == span;
+  if (interior) {
+    const int rl0 = t / 8;
+    const int64_t off0 = (r0 + rl0) * a.ld + c_begin + chunk * 8;
+    const int64_t off1 = off0 + 32 * a.ld;
+    const float4 L0 = sh_L[rl0], L1 = sh_L[rl0 + 32];
+    const float G0 = sh_G[rl0], G1 = sh_G[rl0 + 32];
+    const int j = t % 8;
+    uint16_t* d0 = dzt + (c_begin + rl0) * ldt + r0 + 8 * j;   // column c_begin + t/8
+    uint16_t* d1 = d0 + 32 * ldt;                              // column c_begin + t/8 + 32
+    const int ntile = static_cast<int>(span / 64);
+    uint4 s0 = *reinterpret_cast<const uint4*>(zs + off0), s1 = *reinterpret_cast<const uint4*>(zs + off1);
+    uint4 u0 = *reinterpret_cast<const uint4*>(zt + off0), u1 = *reinterpret_cast<const uint4*>(zt + off1);
+    for (int it = 0; it < ntile; ++it) {
+      const int64_t c = static_cast<int64_t>(it) * 64;
+      uint4 ns0 = s0, ns1 = s1, nu0 = u0, nu1 = u1;
+      if (it + 1 < ntile) {
+        ns0 = *reinterpret_cast<const uint4*>(zs + off0 + c + 64);
+        ns1 = *reinterpret_cast<const uint4*>(zs + off1 + c + 64);
+        nu0 = *reinterpret_cast<const uint4*>(zt + off0 + c + 64);
+        nu1 = *reinterpret_cast<const uint4*>(zt + off1 + c + 64);
+      }
+      const uint4 p0 = elem8(s0, u0, L0, G0, lsum[0]);
+      const uint4 p1 = elem8(s1, u1, L1, G1, lsum[1]);
+      *reinterpret_cast<uint4*>(gr + off0 + c) = p0;
+      *reinterpret_cast<uint4*>(gr + off1 + c) = p1;
+      tile[it & 1][rl0][chunk ^ ((rl0 >> 3) & 7)] = p0;
+      tile[it & 1][rl0 + 32][chunk ^ (((rl0 + 32) >> 3) & 7)] = p1;
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[it & 1][0][0]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int cl = rl0 + 32 * h;
+        uint16_t e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int rl = 8 * j + i;
+          e[i] = t16[rl * 64 + ((cl >> 3) ^ ((rl >> 3) & 7)) * 8 + (cl & 7)];
+        }
+        *reinterpret_cast<uint4*>((h ? d1 : d0) + c * ldt) =
+            make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                       e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+      }
+      s0 = ns0;
+      s1 = ns1;
+      u0 = nu0;
+      u1 = nu1;
+    }
+  }
   uint4 cs[2], ct[2], ns[2], nt[2];
-  fetch(c_begin, cs, ct);
-  for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
+  if (!interior) fetch(c_begin, cs, ct);
+  int buf = 0;
+  for (int64_t c0 = interior ? c_end : c_begin; c0 < c_end; c0 += 64) {
     if (c0 + 64 < c_end) fetch(c0 + 64, ns, nt);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -628,21 +780,32 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          float Q, P, l, g, gacc;
-          jsd_terms<MODE, true>((ys[i] - L.x) * k - L.y, (yt[i] - L.z) * k - L.w, a.beta, Q, P, l, g,
-                          gacc);
-          const float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+          const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
+          float dA, l = 0.f;
+          if constexpr (LOSS && MODE == kModeGeneralized) {
+            float Q, r, dmr;
+            const float g = g_direct(as, at, beta, Q, r, dmr);
+            dA = g - Q * G;
+            const float P = hw_exp2(at);
+            l = as == at ? 0.f : beta * P * dmr - (1.f - beta) * Q * r;
+          } else {
+            float Q, P, g, gacc;
+            jsd_terms<MODE, true>(as, at, beta, Q, P, l, g, gacc);
+            dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+          }
           out[i] = dA * a.grad_scale;
+          // Columns past the row end load as -inf: no loss term.
+          if constexpr (LOSS) lsum[h] += i < n ? l : 0.f;
         }
         packed = pack8_bf16(out, n);
         store8_packed(gr + row * a.ld, v, n, a.vec_ok, packed);
       }
-      tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
+      tile[buf][rl][chunk ^ ((rl >> 3) & 7)] = packed;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // Transposed: thread -> (column, eight consecutive rows); a wave writes
     // 8 rows of dzt, 128 contiguous bytes each.
-    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[0][0]);
+    const uint16_t* t16 = reinterpret_cast<const uint16_t*>(&tile[buf][0][0]);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int cl = t / 8 + 32 * h;
@@ -667,13 +830,41 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    buf ^= 1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       cs[h] = ns[h];
       ct[h] = nt[h];
     }
   }
+  if constexpr (LOSS) {
+    // The 8 threads of a row are 8 consecutive lanes: sum them, fixed order
+    // per lane pattern, and write this workgroup's partial of each row.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float x = lsum[h];
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      const int64_t row = r0 + t / 8 + 32 * h;
+      if (chunk == 0 && row < a.rows) a.lpart[static_cast<int64_t>(blockIdx.x) * a.rows + row] = x;
+    }
+  }
+}
+
+// Row losses from pass 3's per-workgroup partials: one wave per row, lane l
+// adding blocks l, l + 64, ... in order, then a fixed butterfly over the
+// lanes (the same order every run).
+__global__ __launch_bounds__(256) void jsd_row_loss_merge_kernel(const float* lpart, int64_t rows,
+                                                                 int nblk, float row_scale,
+                                                                 float* row_loss) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  float acc = 0.f;
+  for (int b = lane; b < nblk; b += 64) acc += lpart[static_cast<int64_t>(b) * rows + row];
+  acc = wave_sum(acc);
+  if (lane == 0) row_loss[row] = acc * row_scale;
 }
 
 template <typename T>
@@ -709,22 +900,39 @@ hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s) {
   return dtype == 1 ? launch_grad_t<uint16_t>(a, s, grid) : launch_grad_t<float>(a, s, grid);
 }
 
-hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, hipStream_t s) {
+hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, bool loss_in_pass3,
+                                      hipStream_t s) {
+  int64_t span = 0, nblk = 0;
+  grad_t_geometry(a.rows, a.V, &span, &nblk);
   const int64_t row_blocks = (a.rows + 63) / 64;
-  const int64_t tiles = (a.V + 63) / 64;   // 64-column tiles per row block
-  // Columns per workgroup: as many 64-column tiles as keep kGradTargetBlocks
-  // workgroups in the launch, at most kTileColsMax.
-  int64_t per = (tiles * row_blocks + kGradTargetBlocks - 1) / kGradTargetBlocks;
-  per = std::max<int64_t>(1, std::min<int64_t>(per, kTileColsMax / 64));
-  const int64_t span = per * 64;
-  const dim3 grid(static_cast<unsigned>((a.V + span - 1) / span), static_cast<unsigned>(row_blocks));
+  const dim3 grid(static_cast<unsigned>(nblk), static_cast<unsigned>(row_blocks));
   uint16_t* d = static_cast<uint16_t*>(dzt);
-  if (a.mode == kModeForwardKL)
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeForwardKL>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
+  const dim3 block(kThreads);
+  if (loss_in_pass3 && a.mode == kModeForwardKL)
+    hipLaunchKernelGGL((jsd_grad_t_kernel<kModeForwardKL, true>), grid, block, 0, s, a, d, ldt, span);
+  else if (loss_in_pass3 && a.mode == kModeGeneralized)
+    hipLaunchKernelGGL((jsd_grad_t_kernel<kModeGeneralized, true>), grid, block, 0, s, a, d, ldt, span);
+  else if (a.mode == kModeForwardKL)
+    hipLaunchKernelGGL((jsd_grad_t_kernel<kModeForwardKL, false>), grid, block, 0, s, a, d, ldt, span);
   else if (a.mode == kModeReverseKL)
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeReverseKL>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
+    hipLaunchKernelGGL((jsd_grad_t_kernel<kModeReverseKL, false>), grid, block, 0, s, a, d, ldt, span);
   else
-    hipLaunchKernelGGL(jsd_grad_t_kernel<kModeGeneralized>, grid, dim3(kThreads), 0, s, a, d, ldt, span);
+    hipLaunchKernelGGL((jsd_grad_t_kernel<kModeGeneralized, false>), grid, block, 0, s, a, d, ldt, span);
+  return hipGetLastError();
+}
+
+hipError_t launch_jsd_gsum(const JsdArgs& a, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(a.rows), static_cast<unsigned>(a.S));
+  hipLaunchKernelGGL(jsd_gsum_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_jsd_row_loss_merge(const JsdArgs& a, hipStream_t s) {
+  int64_t span = 0, nblk = 0;
+  grad_t_geometry(a.rows, a.V, &span, &nblk);
+  const dim3 grid(static_cast<unsigned>((a.rows + 3) / 4));
+  hipLaunchKernelGGL(jsd_row_loss_merge_kernel, grid, dim3(256), 0, s, a.lpart, a.rows,
+                     static_cast<int>(nblk), a.row_scale, a.row_loss);
   return hipGetLastError();
 }
 

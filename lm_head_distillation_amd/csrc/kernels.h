@@ -34,6 +34,7 @@ struct JsdArgs {
   // maximum logit (the largest, if the maximum is tied), the reference element
   // of the gradient terms (see jsd_loss_kernel)
   float* ref = nullptr;
+  float* lpart = nullptr;       // [column blocks][rows] bf16 pass 3's loss partials
   float* row_loss = nullptr;    // [rows] per-row loss out
   float row_scale = 1.f;        // multiplies the per-row losses (T^2 when asked)
 };
@@ -92,7 +93,13 @@ hipError_t launch_jsd_stats(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_loss(const JsdArgs& a, int dtype, hipStream_t s);
 hipError_t launch_jsd_grad(const JsdArgs& a, int dtype, hipStream_t s);
 // Pass 3 for bf16 that also writes dZ^T [V, ldt] (the weight-gradient operand).
-hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, hipStream_t s);
+// loss_in_pass3 (generalized and forward KL): pass 3 also sums the loss terms
+// into a.lpart (after launch_jsd_gsum, or no pass 2 at all for the forward
+// KL); launch_jsd_row_loss_merge then writes the row losses.
+hipError_t launch_jsd_grad_transposed(const JsdArgs& a, void* dzt, int64_t ldt, bool loss_in_pass3,
+                                      hipStream_t s);
+hipError_t launch_jsd_gsum(const JsdArgs& a, hipStream_t s);
+hipError_t launch_jsd_row_loss_merge(const JsdArgs& a, hipStream_t s);
 // Pass 1 from the logits GEMMs' row-statistic partials [rows, tiles] (student,
 // teacher): writes the row statistics the loss passes read.
 hipError_t launch_jsd_stats_merge(const JsdArgs& a, const float2* part_s, const float2* part_t,

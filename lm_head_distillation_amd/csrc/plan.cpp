@@ -75,6 +75,18 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   p.off_lg = L.take(rs, 1, 8);
   p.off_peak = L.take(rs, 1, 16);
   p.off_ref = L.take(rs, 1, 4);
+  {
+    // bf16 with a weight gradient: pass 3's per-row loss partials, sized for
+    // both chunk lengths the plan runs (C, and the last chunk's).
+    int64_t span = 0, nblk = 0, nblk_last = 0;
+    const int64_t last = BT - (p.n_chunks - 1) * p.C;
+    grad_t_geometry(p.C, V, &span, &nblk);
+    grad_t_geometry(last, V, &span, &nblk_last);
+    int64_t n = 0, n_last = 0;
+    if (__builtin_mul_overflow(nblk, p.C, &n)) n = INT64_MAX;
+    if (__builtin_mul_overflow(nblk_last, last, &n_last)) n_last = INT64_MAX;
+    p.off_lpart = L.take(dtype == 1 ? std::max(n, n_last) : 0, 1, 4);
+  }
   p.off_partial = L.take(p.splitk > 1 ? p.splitk * p.C : 0, H_s, 4);
   p.off_xt = L.take(p.transposed_grad_w ? H_s : 0, p.ldt, es);
   p.off_dzt = L.take(p.transposed_grad_w ? V : 0, p.ldt, es);

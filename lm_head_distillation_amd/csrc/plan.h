@@ -59,6 +59,22 @@ inline int dtype_size(int dtype) { return dtype == 0 ? 4 : 2; }
 // Elements per 16-byte vector for the dtype.
 inline int dtype_vec(int dtype) { return dtype == 0 ? 4 : 8; }
 
+// Column span of one workgroup of the bf16 gradient pass (64-row x 64-column
+// tiles): as many 64-column tiles as keep about kGradTargetBlocks workgroups in
+// the launch, at most kGradTileColsMax columns; nblk column blocks per row.
+constexpr int64_t kGradTileColsMax = 1024;
+constexpr int64_t kGradTargetBlocks = 2048;
+inline void grad_t_geometry(int64_t rows, int64_t V, int64_t* span, int64_t* nblk) {
+  const int64_t row_blocks = cdiv(rows, 64);
+  const int64_t tiles = cdiv(V, 64);
+  int64_t work = 0;
+  if (__builtin_mul_overflow(tiles, row_blocks, &work)) work = INT64_MAX;
+  int64_t per = cdiv(work, kGradTargetBlocks);
+  per = per < 1 ? 1 : (per > kGradTileColsMax / 64 ? kGradTileColsMax / 64 : per);
+  *span = per * 64;
+  *nblk = cdiv(V, *span);
+}
+
 struct SlicePlan {
   int S = 1;             // slices per row
   int64_t slice_w = 0;   // elements per slice, a multiple of kJsdVec
@@ -89,7 +105,7 @@ struct ChunkPlan {
   int64_t k_per_split = 0;
   // Workspace layout, byte offsets from the workspace base.
   size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0, off_peak = 0,
-         off_ref = 0, off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0, total = 0;
+         off_ref = 0, off_lpart = 0, off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0, total = 0;
 };
 
 // Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).

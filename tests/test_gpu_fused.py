@@ -277,8 +277,14 @@ def test_optional_gradients_and_determinism(fl, dtype):
     neither = _run(fl, dev, 0.3, 1.0, "batchmean", 2, grad_input=False, grad_weight=False)
     assert only_x[2] is None and only_w[1] is None
     assert torch.equal(only_x[1], full[1]) and torch.equal(only_w[2], full[2])
-    for r in (only_x, only_w, neither):
-        assert torch.equal(r[0], full[0])
+    assert torch.equal(only_w[0], full[0])
+    # Without a weight gradient (or any gradient) the loss terms are summed in
+    # pass 2 instead of pass 3 (bf16): the same terms in another order.
+    for r in (only_x, neither):
+        if dtype == "f32":
+            assert torch.equal(r[0], full[0])
+        else:
+            assert abs(float(r[0]) - float(full[0])) <= 1e-6 * abs(float(full[0]))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
