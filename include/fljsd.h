@@ -285,6 +285,27 @@ int fljsd_flce_forward_backward(const void* X, const void* W, const int64_t* lab
                                 void* grad_X, void* grad_W,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fljsd_flce_forward_backward_ex - fljsd_flce_forward_backward with the
+ * weight-gradient options of fljsd_forward_backward_ex (PR #1429, Details:
+ * the accum_dtype=float32 path, where the per-chunk products of grad_weight
+ * add up in fp32):
+ *   grad_w_dtype  `dtype`, or FLJSD_F32 with FLJSD_BF16 inputs (grad_W [V, H]
+ *                 in fp32: the bf16 products stored and summed over chunks in
+ *                 fp32, no rounding in between); anything else FLJSD_EDTYPE.
+ *   flags         0 or FLJSD_ACCUMULATE_GRAD_W (the first chunk adds to the
+ *                 grad_W the caller passes); other bits FLJSD_EINVAL.
+ * fljsd_flce_forward_backward(...) is this call with (dtype, 0). The
+ * workspace size does not depend on either argument.
+ */
+int fljsd_flce_forward_backward_ex(const void* X, const void* W, const int64_t* labels,
+                                   int64_t BT, int64_t H, int64_t V, int dtype,
+                                   int64_t ignore_index, float label_smoothing,
+                                   int reduction, int num_chunks, float* loss,
+                                   void* grad_X, void* grad_W, int grad_w_dtype,
+                                   unsigned flags, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* Workspace bytes of fljsd_flce_forward_backward (0 for invalid arguments),
  * and the smallest chunk count whose workspace fits `budget_bytes` (or a
  * negative status code). Host-only. */

@@ -665,11 +665,26 @@ FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const
                                              int reduction, int num_chunks, float* loss,
                                              void* grad_X, void* grad_W, void* workspace,
                                              size_t workspace_bytes, void* stream) {
+  return fljsd_flce_forward_backward_ex(X, W, labels, BT, H, V, dtype, ignore_index,
+                                        label_smoothing, reduction, num_chunks, loss, grad_X,
+                                        grad_W, dtype, 0u, workspace, workspace_bytes, stream);
+}
+
+FLJSD_EXPORT int fljsd_flce_forward_backward_ex(const void* X, const void* W,
+                                                const int64_t* labels, int64_t BT, int64_t H,
+                                                int64_t V, int dtype, int64_t ignore_index,
+                                                float label_smoothing, int reduction,
+                                                int num_chunks, float* loss, void* grad_X,
+                                                void* grad_W, int grad_w_dtype, unsigned flags,
+                                                void* workspace, size_t workspace_bytes,
+                                                void* stream) {
   clear_last_error();
   CePlan plan;
   int rc = check_flce(X, W, labels, BT, H, V, dtype, label_smoothing, reduction, num_chunks, loss,
-                      grad_X, grad_W, workspace, workspace_bytes, &plan);
+                      grad_X, grad_W, grad_w_dtype, flags, workspace, workspace_bytes, &plan);
   if (rc != FLJSD_OK) return rc;
+  const bool gw_f32_acc = dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32;
+  const bool gw_add_existing = (flags & FLJSD_ACCUMULATE_GRAD_W) != 0;
   rc = check_device();
   if (rc != FLJSD_OK) return rc;
 
@@ -721,9 +736,14 @@ FLJSD_EXPORT int fljsd_flce_forward_backward(const void* X, const void* W, const
       if (rc != FLJSD_OK) return rc;
     }
     if (grad_W) {
+      // As in the JSD pass: chunk 0 overwrites unless asked to add; an fp32
+      // grad_W takes the bf16 products unrounded (PR #1429, Details).
+      const bool add = ci > 0 || gw_add_existing;
+      const int epi = gw_f32_acc ? (add ? kEpiAccumulateF32 : kEpiPartialF32)
+                                 : (add ? kEpiAccumulate : kEpiStore);
       rc = run_grad_weight(dtype, Z, plan.ldz, Xc + r0 * H * es, rows, H, V, grad_W,
                            plan.transposed_grad_w, ws + plan.off_zt, ws + plan.off_xt, plan.ldt,
-                           ci == 0 ? kEpiStore : kEpiAccumulate, s, /*dz_transposed=*/true);
+                           epi, s, /*dz_transposed=*/true);
       if (rc != FLJSD_OK) return rc;
     }
   }

@@ -137,8 +137,8 @@ int check_elem_loss(const void* a, const void* b, int64_t BT, int64_t V, int64_t
 
 int check_flce(const void* X, const void* W, const int64_t* labels, int64_t BT, int64_t H,
                int64_t V, int dtype, float label_smoothing, int reduction, int num_chunks,
-               const float* loss, const void* grad_X, const void* grad_W, const void* workspace,
-               size_t workspace_bytes, CePlan* plan) {
+               const float* loss, const void* grad_X, const void* grad_W, int grad_w_dtype,
+               unsigned flags, const void* workspace, size_t workspace_bytes, CePlan* plan) {
   if (!X || !W || !labels || !loss) return fail(FLJSD_EINVAL, "X, W, labels and loss must not be NULL");
   if (BT <= 0 || H <= 0 || V <= 0) return fail(FLJSD_EINVAL, "BT, H and V must be > 0");
   if (BT > INT32_MAX || V > INT32_MAX) return fail(FLJSD_EINVAL, "BT and V must fit in int32");
@@ -148,6 +148,10 @@ int check_flce(const void* X, const void* W, const int64_t* labels, int64_t BT, 
   if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f))
     return fail(FLJSD_EINVAL, "label_smoothing must be in [0, 1]");
   if (num_chunks < 0) return fail(FLJSD_EINVAL, "num_chunks must be >= 0");
+  if (grad_w_dtype != dtype && !(dtype == FLJSD_BF16 && grad_w_dtype == FLJSD_F32))
+    return fail(FLJSD_EDTYPE, "grad_w_dtype must equal dtype, or be F32 with BF16 inputs");
+  if (flags & ~static_cast<unsigned>(FLJSD_ACCUMULATE_GRAD_W))
+    return fail(FLJSD_EINVAL, "unknown flag bits");
   int rc = check_aligned({X, W, loss, grad_X, grad_W, workspace});
   if (rc != FLJSD_OK) return rc;
   if ((reinterpret_cast<uintptr_t>(labels) & 7u) != 0)

@@ -54,7 +54,7 @@ int check_elem_loss(const void* a, const void* b, int64_t BT, int64_t V, int64_t
 // fljsd_flce_forward_backward.
 int check_flce(const void* X, const void* W, const int64_t* labels, int64_t BT, int64_t H,
                int64_t V, int dtype, float label_smoothing, int reduction, int num_chunks,
-               const float* loss, const void* grad_X, const void* grad_W, const void* workspace,
-               size_t workspace_bytes, CePlan* plan);
+               const float* loss, const void* grad_X, const void* grad_W, int grad_w_dtype,
+               unsigned flags, const void* workspace, size_t workspace_bytes, CePlan* plan);
 
 }  // namespace fljsd

@@ -69,6 +69,9 @@ def load_library() -> ctypes.CDLL:
     lib.fljsd_flce_forward_backward.argtypes = [vp, vp, vp, i64, i64, i64, cint, i64, f32, cint, cint,
                                                 vp, vp, vp, vp, sz, vp]
     lib.fljsd_flce_forward_backward.restype = cint
+    lib.fljsd_flce_forward_backward_ex.argtypes = [vp, vp, vp, i64, i64, i64, cint, i64, f32, cint,
+                                                   cint, vp, vp, vp, cint, ctypes.c_uint, vp, sz, vp]
+    lib.fljsd_flce_forward_backward_ex.restype = cint
     lib.fljsd_flce_workspace_size.argtypes = [i64, i64, i64, cint, cint]
     lib.fljsd_flce_workspace_size.restype = sz
     lib.fljsd_flce_plan_num_chunks.argtypes = [i64, i64, i64, cint, sz]
@@ -423,6 +426,23 @@ def fljsd_flce_forward_backward(X: torch.Tensor, W: torch.Tensor, labels: torch.
                                 workspace: Optional[torch.Tensor] = None, stream=None):
     """Fused-linear cross-entropy forward + backward with hard labels.
     Returns (loss, grad_X or None, grad_W or None)."""
+    return fljsd_flce_forward_backward_ex(X, W, labels, ignore_index, label_smoothing, reduction,
+                                          num_chunks, grad_input=grad_input,
+                                          grad_weight=grad_weight, workspace=workspace,
+                                          stream=stream, _entry="plain")
+
+
+def fljsd_flce_forward_backward_ex(X: torch.Tensor, W: torch.Tensor, labels: torch.Tensor,
+                                   ignore_index: int = -100, label_smoothing: float = 0.0,
+                                   reduction: str = "mean", num_chunks: int = 0, *,
+                                   grad_w_dtype: Optional[torch.dtype] = None, flags: int = 0,
+                                   grad_input: bool = True, grad_weight: bool = True,
+                                   workspace: Optional[torch.Tensor] = None,
+                                   out: Optional[Tuple[torch.Tensor, Optional[torch.Tensor], Optional[torch.Tensor]]] = None,
+                                   stream=None, _entry: str = "ex"):
+    """fljsd_flce_forward_backward with a weight-gradient dtype (None: the input
+    dtype; torch.float32 with bf16 inputs: per-chunk products summed in fp32)
+    and flags (FLJSD_ACCUMULATE_GRAD_W adds to the grad_W given in ``out``)."""
     lib = load_library()
     _require_device(X, W)
     dt = _dtype_code(X)
@@ -434,7 +454,13 @@ def fljsd_flce_forward_backward(X: torch.Tensor, W: torch.Tensor, labels: torch.
         raise ValueError("shape mismatch: X [BT,H], W [V,H]")
     if labels.dtype != torch.int64 or labels.shape != (BT,) or not labels.is_cuda or not labels.is_contiguous():
         raise ValueError("labels must be a contiguous int64 GPU tensor of shape [BT]")
+    if labels.device != X.device:
+        raise ValueError("labels must live on the inputs' device")
     red = _reduction_code(reduction)
+    gw_torch = X.dtype if grad_w_dtype is None else grad_w_dtype
+    gw_code = {torch.float32: 0, torch.bfloat16: 1}.get(gw_torch, -1)
+    if (flags & FLJSD_ACCUMULATE_GRAD_W) and (out is None or out[2] is None):
+        raise ValueError("FLJSD_ACCUMULATE_GRAD_W needs the grad_W to add to, passed in `out`")
     nc = int(num_chunks)
     if nc == 0:
         budget = workspace.numel() * workspace.element_size() if workspace is not None else default_budget_bytes()
@@ -443,13 +469,24 @@ def fljsd_flce_forward_backward(X: torch.Tensor, W: torch.Tensor, labels: torch.
         workspace = torch.empty(fljsd_flce_workspace_size(BT, H, V, dt, nc), dtype=torch.uint8,
                                 device=X.device)
     _check_workspace(workspace, X.device)
-    loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X.device)
-    gX = torch.empty_like(X) if grad_input else None
-    gW = torch.empty_like(W) if grad_weight else None
-    rc = lib.fljsd_flce_forward_backward(
-        X.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt, int(ignore_index),
-        float(label_smoothing), red, nc, loss.data_ptr(), _ptr(gX), _ptr(gW), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _stream(stream))
+    if out is not None:
+        loss, gX, gW = out
+        _check_out(loss, torch.float32, BT if red == 3 else 1, X.device, "loss")
+        if gX is not None:
+            _check_out(gX, X.dtype, BT * H, X.device, "grad_X")
+        if gW is not None:
+            _check_out(gW, gw_torch, V * H, X.device, "grad_W")
+    else:
+        loss = torch.empty(BT if red == 3 else 1, dtype=torch.float32, device=X.device)
+        gX = torch.empty_like(X) if grad_input else None
+        gW = torch.empty(V, H, dtype=gw_torch, device=X.device) if grad_weight else None
+    args = (X.data_ptr(), W.data_ptr(), labels.data_ptr(), BT, H, V, dt, int(ignore_index),
+            float(label_smoothing), red, nc, loss.data_ptr(), _ptr(gX), _ptr(gW))
+    tail = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(stream))
+    if _entry == "plain":
+        rc = lib.fljsd_flce_forward_backward(*args, *tail)
+    else:
+        rc = lib.fljsd_flce_forward_backward_ex(*args, gw_code, int(flags), *tail)
     _check(rc)
     return (loss if red == 3 else loss[0]), gX, gW
 

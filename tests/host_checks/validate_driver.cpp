@@ -7,7 +7,7 @@
 //   jsd   zs zt BT V ld dtype beta T reduction loss grad ws ws_bytes
 //   noalloc zs zt BT V ld dtype beta T reduction loss grad
 //   elem  kind(0 = log-probability JSD, 1 = TVD) a b BT V ld dtype beta reduction loss grad ws ws_bytes
-//   flce  X W labels BT H V dtype ls reduction nc loss gX gW ws ws_bytes
+//   flce  X W labels BT H V dtype ls reduction nc loss gX gW gw_dtype flags ws ws_bytes
 //   ws    BT H_s H_t V dtype nc          (fljsd_workspace_size)
 //   gws   BT V dtype                     (fljsd_generalized_jsd_workspace_size)
 //   plan  BT H_s H_t V dtype budget      (fljsd_plan_num_chunks)
@@ -106,10 +106,14 @@ int main() {
       const float ls = r.f32();
       const int red = r.i32(), nc = r.i32();
       const float* loss = static_cast<const float*>(r.ptr());
-      const void *gX = r.ptr(), *gW = r.ptr(), *ws = r.ptr();
+      const void *gX = r.ptr(), *gW = r.ptr();
+      const int gwd = r.i32();
+      const unsigned flags = static_cast<unsigned>(r.u64());
+      const void* ws = r.ptr();
       const size_t wsb = r.u64();
       CePlan plan;
-      out = check_flce(X, W, labels, BT, H, V, dtype, ls, red, nc, loss, gX, gW, ws, wsb, &plan);
+      out = check_flce(X, W, labels, BT, H, V, dtype, ls, red, nc, loss, gX, gW, gwd, flags, ws, wsb,
+                       &plan);
     } else if (op == "ws") {
       const int64_t BT = r.i64(), Hs = r.i64(), Ht = r.i64(), V = r.i64();
       const int dtype = r.i32(), nc = r.i32();

@@ -44,7 +44,7 @@ def test_header_declares_the_entry_points():
               "fljsd_flce_workspace_size", "fljsd_flce_plan_num_chunks", "fljsd_workspace_size",
               "fljsd_generalized_jsd_workspace_size", "fljsd_plan_num_chunks", "fljsd_strerror",
               "fljsd_last_error", "fljsd_profile_enable", "fljsd_profile_read",
-              "fljsd_generalized_jsd_noalloc"):
+              "fljsd_generalized_jsd_noalloc", "fljsd_flce_forward_backward_ex"):
         assert n in names
 
 
@@ -321,6 +321,29 @@ def flce(lib, **over):
 @pytest.mark.parametrize("over,code", FLCE_CASES)
 def test_flce_rejects(lib, over, code):
     assert flce(lib, **over) == code
+    assert lib.fljsd_last_error()
+
+
+FLCEX_ARGS = dict(FLCE_ARGS, gw_dtype=BF16, flags=0)
+FLCEX_CASES = [
+    (dict(gw_dtype=2), EDTYPE), (dict(dtype=F32, gw_dtype=BF16), EDTYPE), (dict(flags=2), EINVAL),
+    (dict(flags=0x80000001), EINVAL), (dict(gw_dtype=F32, X=None), EINVAL),
+    (dict(gw_dtype=F32, flags=1, ws_bytes=64), EWORKSPACE), (dict(gw_dtype=F32, gW=FAKE + 8), EALIGN),
+]
+
+
+def flcex(lib, **over):
+    a = dict(FLCEX_ARGS)
+    a.update(over)
+    return lib.fljsd_flce_forward_backward_ex(a["X"], a["W"], a["labels"], a["BT"], a["H"], a["V"],
+                                              a["dtype"], a["ignore"], a["eps"], a["reduction"],
+                                              a["nc"], a["loss"], a["gX"], a["gW"], a["gw_dtype"],
+                                              a["flags"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", FLCE_CASES + FLCEX_CASES)
+def test_flce_ex_rejects(lib, over, code):
+    assert flcex(lib, **over) == code
     assert lib.fljsd_last_error()
 
 

@@ -9,8 +9,8 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_util import TOL, assert_loss_close, assert_tensor_close, from_device, to_device, \
-    to_f64
+from tests.gpu_util import TOL, assert_loss_close, assert_tensor_close, from_device, normwise, \
+    to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -144,3 +144,99 @@ def test_beyond_2g_logit_elements(fl):
     lhs = float((gW.double() * Wd.double()).sum())
     rhs = float((gX.double() * Xd.double()).sum())
     assert abs(lhs - rhs) <= 2e-2 * max(abs(lhs), abs(rhs)), f"{lhs} vs {rhs}"
+
+
+# ---- fp32 weight gradient (Liger-Kernel PR #1429, Details) and adding to an existing one --
+
+def _ex(fl, X, W, y, nc, **kw):
+    out = fl.fljsd_flce_forward_backward_ex(to_device(X, "bf16"), to_device(W, "bf16"),
+                                            torch.from_numpy(y).cuda(), -100, 0.05, "mean", nc, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.fixture(scope="module")
+def flce_bf16_case():
+    # Several 256-wide vocabulary tiles with a ragged last one, a ragged
+    # hidden tile, and chunks down to 4 rows.
+    X, W, y = _case(611, 64, 264, 5003, "bf16")
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, "bf16"), to_f64(W, "bf16"), y, -100, 0.05, "mean")
+    return X, W, y, ref
+
+
+@pytest.mark.parametrize("nc", [1, 4, 16])
+def test_flce_fp32_grad_w_matches_oracle(fl, flce_bf16_case, nc):
+    X, W, y, ref = flce_bf16_case
+    loss, gX, gW = _ex(fl, X, W, y, nc, grad_w_dtype=torch.float32)
+    assert gW.dtype == torch.float32 and gX.dtype == torch.bfloat16
+    _check("bf16", (loss, gX, gW), ref, f"fp32 grad_W nc={nc}")
+
+
+def test_flce_fp32_grad_w_does_not_depend_on_chunks(fl, flce_bf16_case):
+    """dZ rows do not depend on the chunking, so the fp32 sums over 1, 4 and 16
+    chunks differ only by fp32 rounding; the bf16 result carries one bf16
+    rounding per chunk."""
+    X, W, y, _ = flce_bf16_case
+    f32 = {nc: from_device(_ex(fl, X, W, y, nc, grad_w_dtype=torch.float32)[2]) for nc in (1, 4, 16)}
+    b16 = {nc: from_device(_ex(fl, X, W, y, nc)[2]) for nc in (1, 16)}
+    for nc in (4, 16):
+        e = normwise(f32[nc], f32[1])
+        assert e <= 1e-5, f"fp32 grad_W nc={nc} vs nc=1: {e:.3e}"
+    print(f"fp32 nc=16 vs 1: {normwise(f32[16], f32[1]):.2e}; "
+          f"bf16 nc=16 vs 1: {normwise(b16[16], b16[1]):.2e}", flush=True)
+
+
+def test_flce_fp32_one_chunk_rounds_to_the_bf16_mode(fl, flce_bf16_case):
+    """With one chunk the fp32 grad_W is the unrounded product; rounding it to
+    bf16 gives the bf16 mode's bits."""
+    X, W, y, _ = flce_bf16_case
+    f32 = _ex(fl, X, W, y, 1, grad_w_dtype=torch.float32)[2]
+    b16 = _ex(fl, X, W, y, 1)[2]
+    assert torch.equal(f32.to(torch.bfloat16).view(torch.int16), b16.view(torch.int16))
+
+
+@pytest.mark.parametrize("gw_dtype", [torch.bfloat16, torch.float32])
+def test_flce_accumulate_into_existing_grad_w(fl, flce_bf16_case, gw_dtype):
+    """FLJSD_ACCUMULATE_GRAD_W: the call adds its gradient to the grad_W it is
+    given (micro-batch sums), in every chunk, the first included."""
+    X, W, y, ref = flce_bf16_case
+    rng = np.random.default_rng(612)
+    base = (rng.standard_normal((W.shape[0], W.shape[1])) * float(np.std(ref[2]))).astype(np.float32)
+    gW = torch.from_numpy(base).cuda().to(gw_dtype)
+    start = from_device(gW)
+    loss = torch.empty(1, dtype=torch.float32, device="cuda")
+    gX = torch.empty(X.shape, dtype=torch.bfloat16, device="cuda")
+    _ex(fl, X, W, y, 3, grad_w_dtype=gw_dtype, flags=fl.FLJSD_ACCUMULATE_GRAD_W, out=(loss, gX, gW))
+    assert_tensor_close(from_device(gW), start + ref[2], TOL["bf16"], "grad_W added")
+
+
+def test_flce_accumulate_fp32_inputs(fl):
+    X, W, y = _case(613, 24, 64, 700, "f32")
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, "f32"), to_f64(W, "f32"), y, -100, 0.05, "mean")
+    g0 = workloads.draw(9003, W.shape, float(np.std(ref[2])), "f32")
+    out = (torch.empty(1, dtype=torch.float32, device="cuda"),
+           torch.empty(X.shape, dtype=torch.float32, device="cuda"), to_device(g0, "f32"))
+    fl.fljsd_flce_forward_backward_ex(to_device(X, "f32"), to_device(W, "f32"), torch.from_numpy(y).cuda(),
+                                      -100, 0.05, "mean", 5, flags=fl.FLJSD_ACCUMULATE_GRAD_W, out=out)
+    torch.cuda.synchronize()
+    tol = TOL["f32"]
+    assert_loss_close(from_device(out[0]), ref[0], tol)
+    assert_tensor_close(from_device(out[1]), ref[1], tol, "grad_input")
+    assert_tensor_close(from_device(out[2]), to_f64(g0, "f32") + ref[2], tol, "grad_weight + existing")
+
+
+def test_flce_plain_entry_point_is_the_ex_default(fl, flce_bf16_case):
+    X, W, y, _ = flce_bf16_case
+    a = _run(fl, X, W, y, "bf16", -100, 0.05, "mean", 4)
+    b = _ex(fl, X, W, y, 4)
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+def test_flce_ex_rejects_on_device(fl, flce_bf16_case):
+    X, W, y, _ = flce_bf16_case
+    with pytest.raises(fl.FljsdError):
+        _ex(fl, X, W, y, 2, grad_w_dtype=torch.float16)
+    with pytest.raises(ValueError):
+        _ex(fl, X, W, y, 2, flags=fl.FLJSD_ACCUMULATE_GRAD_W)

@@ -90,6 +90,7 @@ def flce_line(a):
     return " ".join(["flce", str(_p(a["X"])), str(_p(a["W"])), str(_p(a["labels"])), str(a["BT"]),
                      str(a["H"]), str(a["V"]), str(a["dtype"]), _f(a["eps"]), str(a["reduction"]),
                      str(a["nc"]), str(_p(a["loss"])), str(_p(a["gX"])), str(_p(a["gW"])),
+                     str(a.get("gw_dtype", a["dtype"])), str(a.get("flags", 0)),
                      str(_p(a["ws"])), str(a["ws_bytes"])])
 
 
@@ -126,6 +127,10 @@ def test_boundary_cases_match_the_library(driver):
         lines.append(flce_line(dict(tb.FLCE_ARGS, **over)))
         expect.append(code)
         assert tb.flce(lib, **over) == code
+    for over, code in tb.FLCEX_CASES:
+        lines.append(flce_line(dict(tb.FLCEX_ARGS, **over)))
+        expect.append(code)
+        assert tb.flcex(lib, **over) == code
     # And the valid calls themselves pass every check.
     lines += [fb_line(tb.FB_ARGS, False), jsd_line(tb.JSD_ARGS), jsd_line(tb.NOALLOC_ARGS, "noalloc"),
               elem_line(tb.ELEM_ARGS, "tvd"), flce_line(tb.FLCE_ARGS)]
