@@ -355,12 +355,12 @@ const char* fljsd_last_error(void);
  */
 #define FLJSD_KCLASS_GEMM_LOGITS 0      /* Z = X W^T (student and teacher) */
 #define FLJSD_KCLASS_JSD_STATS 1        /* pass 1: row max / denominator */
-#define FLJSD_KCLASS_JSD_LOSS 2         /* pass 2: loss and dX_sum partials */
-#define FLJSD_KCLASS_JSD_GRAD 3         /* pass 3: dZ in place, row loss */
+#define FLJSD_KCLASS_JSD_LOSS 2         /* pass 2: loss and G (bf16 with grad_W: G alone) */
+#define FLJSD_KCLASS_JSD_GRAD 3         /* pass 3: dZ in place (and dZ^T, loss partials) */
 #define FLJSD_KCLASS_GEMM_GRAD_INPUT 4  /* grad_X = dZ W_s */
 #define FLJSD_KCLASS_SPLITK_REDUCE 5    /* split-K partial sums -> grad_X */
 #define FLJSD_KCLASS_GEMM_GRAD_WEIGHT 6 /* grad_W (=|+=) dZ^T X_s */
-#define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss */
+#define FLJSD_KCLASS_LOSS_REDUCE 7      /* scalar loss; row losses from pass 3's partials */
 #define FLJSD_KCLASS_TRANSPOSE 8        /* dZ^T and X_s^T for the grad_W product */
 #define FLJSD_KCLASS_ELEM_LOSS 9        /* fljsd_jsd_logprob / fljsd_tvd element pass */
 #define FLJSD_KCLASS_CE_STATS 10        /* cross-entropy pass 1: row max / denominator */
