@@ -80,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void ce_stats_kernel(CeArgs a) {
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float x[8];
-    load8(z, v, n, a.vec_ok, x);
+    load8<false>(z, v, n, a.vec_ok, x);
     md_update8(m, d, x, kLog2e);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -138,14 +138,14 @@ __global__ __launch_bounds__(kThreads) void ce_grad_kernel(CeArgs a, bool write_
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
     float x[8], out[8];
-    load8(z, v, n, a.vec_ok, x);
+    load8<false>(z, v, n, a.vec_ok, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const float q = hw_exp2((x[i] - m) * kLog2e - l2d);
       const float dz = q - off - (v + i == y ? hit : 0.f);
       out[i] = ok ? dz * gs : 0.f;
     }
-    store8(gr, v, n, a.vec_ok, out);
+    store8<false>(gr, v, n, a.vec_ok, out);
   }
 }
 
@@ -212,14 +212,14 @@ __global__ __launch_bounds__(kThreads) void ce_grad_t_kernel(CeArgs a, uint16_t*
         const float gs = sh_gs[rl];
         const int64_t y = sh_y[rl];
         float x[8], out[8];
-        load8(z + row * a.ld, v, n, a.vec_ok, x);
+        load8<false>(z + row * a.ld, v, n, a.vec_ok, x);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float q = hw_exp2((x[i] - ml.x) * kLog2e - ml.y);
           out[i] = (q - off - (v + i == y ? hit : 0.f)) * gs;
         }
         packed = pack8_bf16(out, n);
-        store8_packed(gr + row * a.ld, v, n, a.vec_ok, packed);
+        store8_packed<false>(gr + row * a.ld, v, n, a.vec_ok, packed);
       }
       tile[rl][chunk ^ ((rl >> 3) & 7)] = packed;
     }

@@ -33,6 +33,23 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ inline uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Non-temporal 16-byte load and store for data a pass touches once (the
+// logits streamed by the loss passes, the gradients they write): on MI355X a
+// plain copy moves 5.3 TB/s, one with non-temporal loads and stores 5.7. The
+// 8-element helpers below stream by default; the cross-entropy passes, whose
+// second pass re-reads what the first read (partly still in the Infinity
+// Cache at small chunks), measured faster with plain accesses.
+__device__ inline uint4 ld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(static_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline void st_stream(void* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<u32x4_t*>(p));
+}
+
 // Eight values as packed bf16; entries at or past n are zero.
 __device__ inline uint4 pack8_bf16(const float* x, int n) {
   float y[8];
@@ -46,23 +63,27 @@ __device__ inline uint4 pack8_bf16(const float* x, int n) {
 // read as `fill` (-inf for logits: a masked column carries no probability
 // mass). A full group uses 16-byte loads when `vec` says the rows are 16-byte
 // aligned.
+template <bool STREAM = true>
 __device__ inline void load8(const float* p, int64_t v, int n, bool vec, float* x,
                              float fill = -INFINITY) {
   if (n == 8 && vec) {
-    const float4 a = *reinterpret_cast<const float4*>(p + v);
-    const float4 b = *reinterpret_cast<const float4*>(p + v + 4);
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    const uint4 a = STREAM ? ld_stream(p + v) : *reinterpret_cast<const uint4*>(p + v);
+    const uint4 b = STREAM ? ld_stream(p + v + 4) : *reinterpret_cast<const uint4*>(p + v + 4);
+    x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y);
+    x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+    x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y);
+    x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = i < n ? p[v + i] : fill;
   }
 }
 
+template <bool STREAM = true>
 __device__ inline void load8(const uint16_t* p, int64_t v, int n, bool vec, float* x,
                              float fill = -INFINITY) {
   if (n == 8 && vec) {
-    const uint4 q = *reinterpret_cast<const uint4*>(p + v);
+    const uint4 q = STREAM ? ld_stream(p + v) : *reinterpret_cast<const uint4*>(p + v);
     x[0] = bf16_lo(q.x); x[1] = bf16_hi(q.x);
     x[2] = bf16_lo(q.y); x[3] = bf16_hi(q.y);
     x[4] = bf16_lo(q.z); x[5] = bf16_hi(q.z);
@@ -73,27 +94,40 @@ __device__ inline void load8(const uint16_t* p, int64_t v, int n, bool vec, floa
   }
 }
 
+template <bool STREAM = true>
+__device__ inline void store16(void* p, uint4 v) {
+  if (STREAM)
+    st_stream(p, v);
+  else
+    *static_cast<uint4*>(p) = v;
+}
+
+template <bool STREAM = true>
 __device__ inline void store8(float* p, int64_t v, int n, bool vec, const float* x) {
   if (n == 8 && vec) {
-    *reinterpret_cast<float4*>(p + v) = make_float4(x[0], x[1], x[2], x[3]);
-    *reinterpret_cast<float4*>(p + v + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    store16<STREAM>(p + v, make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]),
+                                      __float_as_uint(x[2]), __float_as_uint(x[3])));
+    store16<STREAM>(p + v + 4, make_uint4(__float_as_uint(x[4]), __float_as_uint(x[5]),
+                                          __float_as_uint(x[6]), __float_as_uint(x[7])));
   } else {
     for (int i = 0; i < n; ++i) p[v + i] = x[i];
   }
 }
 
 // Up to 8 packed bf16 values (pack8_bf16) to columns v .. v + n - 1.
+template <bool STREAM = true>
 __device__ inline void store8_packed(uint16_t* p, int64_t v, int n, bool vec, uint4 q) {
   if (n == 8 && vec) {
-    *reinterpret_cast<uint4*>(p + v) = q;
+    store16<STREAM>(p + v, q);
   } else {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     for (int i = 0; i < n; ++i) p[v + i] = static_cast<uint16_t>(w[i >> 1] >> (16 * (i & 1)));
   }
 }
 
+template <bool STREAM = true>
 __device__ inline void store8(uint16_t* p, int64_t v, int n, bool vec, const float* x) {
-  store8_packed(p, v, n, vec, pack8_bf16(x, n));
+  store8_packed<STREAM>(p, v, n, vec, pack8_bf16(x, n));
 }
 
 __device__ inline float wave_sum(float x) {

@@ -664,8 +664,8 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
       const int64_t row = r0 + t / 8 + 32 * h;
       const int64_t v = c0 + chunk * 8;
       if (full(row, v)) {
-        qs[h] = *reinterpret_cast<const uint4*>(zs + row * a.ld + v);
-        qt[h] = *reinterpret_cast<const uint4*>(zt + row * a.ld + v);
+        qs[h] = ld_stream(zs + row * a.ld + v);
+        qt[h] = ld_stream(zt + row * a.ld + v);
       }
     }
   };
@@ -710,21 +710,21 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
     uint16_t* d0 = dzt + (c_begin + rl0) * ldt + r0 + 8 * j;   // column c_begin + t/8
     uint16_t* d1 = d0 + 32 * ldt;                              // column c_begin + t/8 + 32
     const int ntile = static_cast<int>(span / 64);
-    uint4 s0 = *reinterpret_cast<const uint4*>(zs + off0), s1 = *reinterpret_cast<const uint4*>(zs + off1);
-    uint4 u0 = *reinterpret_cast<const uint4*>(zt + off0), u1 = *reinterpret_cast<const uint4*>(zt + off1);
+    uint4 s0 = ld_stream(zs + off0), s1 = ld_stream(zs + off1);
+    uint4 u0 = ld_stream(zt + off0), u1 = ld_stream(zt + off1);
     for (int it = 0; it < ntile; ++it) {
       const int64_t c = static_cast<int64_t>(it) * 64;
       uint4 ns0 = s0, ns1 = s1, nu0 = u0, nu1 = u1;
       if (it + 1 < ntile) {
-        ns0 = *reinterpret_cast<const uint4*>(zs + off0 + c + 64);
-        ns1 = *reinterpret_cast<const uint4*>(zs + off1 + c + 64);
-        nu0 = *reinterpret_cast<const uint4*>(zt + off0 + c + 64);
-        nu1 = *reinterpret_cast<const uint4*>(zt + off1 + c + 64);
+        ns0 = ld_stream(zs + off0 + c + 64);
+        ns1 = ld_stream(zs + off1 + c + 64);
+        nu0 = ld_stream(zt + off0 + c + 64);
+        nu1 = ld_stream(zt + off1 + c + 64);
       }
       const uint4 p0 = elem8(s0, u0, L0, G0, lsum[0]);
       const uint4 p1 = elem8(s1, u1, L1, G1, lsum[1]);
-      *reinterpret_cast<uint4*>(gr + off0 + c) = p0;
-      *reinterpret_cast<uint4*>(gr + off1 + c) = p1;
+      st_stream(gr + off0 + c, p0);
+      st_stream(gr + off1 + c, p1);
       tile[it & 1][rl0][chunk ^ ((rl0 >> 3) & 7)] = p0;
       tile[it & 1][rl0 + 32][chunk ^ (((rl0 + 32) >> 3) & 7)] = p1;
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -738,9 +738,9 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
           const int rl = 8 * j + i;
           e[i] = t16[rl * 64 + ((cl >> 3) ^ ((rl >> 3) & 7)) * 8 + (cl & 7)];
         }
-        *reinterpret_cast<uint4*>((h ? d1 : d0) + c * ldt) =
-            make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                       e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+        st_stream((h ? d1 : d0) + c * ldt,
+                  make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                             e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)));
       }
       s0 = ns0;
       s1 = ns1;
@@ -821,9 +821,8 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
         }
         uint16_t* q = dzt + v * ldt + r;
         if (r + 8 <= a.rows) {
-          *reinterpret_cast<uint4*>(q) =
-              make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
-                         e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16));
+          st_stream(q, make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
+                                  e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)));
         } else {
           for (int i = 0; i < 8; ++i)
             if (r + i < a.rows) q[i] = e[i];
