@@ -15,6 +15,11 @@ Fields beyond the throughput:
                 events the library records around each launch during the
                 timed steps, against MI355X's published peak.
   kernels       the same tally for every kernel class.
+  jsd_*         the loss passes (statistics merge, pass 2, pass 3): algorithmic
+                GB/s, the pages' three-pass byte count (7·V·s per row) over
+                their time, the compulsory bytes (3·V·s) at 8 TB/s over their
+                time, and HBM GB/s from the counter summary
+                (profiles/traffic.json, current sources only).
   mfma_util_counter / mfma_counters
                 matrix-core utilisation of the three products from rocprofv3
                 counters (profiles/mfma.json, used only when it was taken with
@@ -528,6 +533,17 @@ def main():
                         "unit": r["unit"], "frac": round(r["achieved"] / r["peak"], 4)}
                     for c, r in per_class.items()},
     }
+    # The loss passes against the method's own byte counts: the three-pass
+    # figure (7·V·s per row) and the compulsory one (3·V·s: each logit read
+    # once, dX written once) at 8 TB/s; and, from the committed counter
+    # summary, the HBM bytes the passes moved over their time.
+    jsd_s = jsd_ms / args.steps / 1e3
+    result["jsd_effective_gbps_7vs"] = round(7.0 * V * 2 * BT / jsd_s / 1e9, 1)
+    result["jsd_compulsory_frac"] = round(3.0 * V * 2 * BT / (PEAK_HBM_GBPS * 1e9) / jsd_s, 4)
+    jsd_traffic = [traffic_for(c) for c in jsd_cls]
+    if all(t is not None for t in jsd_traffic):
+        moved = sum(t * kernels[c]["launches"] / args.steps for t, c in zip(jsd_traffic, jsd_cls))
+        result["jsd_hbm_gbps_counter"] = round(moved / jsd_s / 1e9, 1)
     mfma = mfma_counters()
     result["mfma_util_counter"] = mfma.get("gemms")
     if mfma:
