@@ -4,7 +4,8 @@ teacher and student hidden sizes apart, every chunk count from the policy's
 up to more chunks than rows), every β branch, temperatures around 1, every
 reduction, and the entry points' options (fp32 weight gradient, adding to an
 existing one, the standalone loss step in place or with a padded row stride,
-the fused-linear cross-entropy with ignored labels and label smoothing).
+the fused-linear cross-entropy with ignored labels and label smoothing, the
+log-space JSD and the TVD).
 
 The configurations are drawn once from a fixed seed, so every run checks the
 same cases; each case prints its parameters before any device work.
@@ -186,3 +187,59 @@ def test_flce_random(fl, case):
         assert_loss_close(from_device(loss), rl, tol, "loss")
     assert_tensor_close(from_device(gX), ref[1], tol, "grad_input")
     assert_tensor_close(from_device(gW), ref[2], gw_tol(dtype, tol, BT, nc), "grad_weight")
+
+
+def _elem_cases(n=10, seed=1204):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = "f32" if i % 2 == 0 else "bf16"
+        R = int(rng.integers(1, 400))
+        V = int(rng.integers(1, 30000))
+        red = REDUCTIONS[int(rng.integers(0, 4))]
+        in_place = bool(rng.random() < 0.5)
+        cases.append((i, dtype, R, V, _beta(rng), red, in_place))
+    return cases
+
+
+def _dist(seed, R, V, dtype, log):
+    """Seeded rows as log-probabilities or probabilities, rounded to dtype."""
+    z = workloads.draw(seed, (R, V), 2.0, "f32").astype(np.float64)
+    z = z - z.max(axis=1, keepdims=True)
+    lse = np.log(np.exp(z).sum(axis=1, keepdims=True))
+    x = (z - lse) if log else np.exp(z - lse)
+    f = np.asarray(x, dtype=np.float32)
+    return f if dtype == "f32" else workloads.f32_to_bf16_bits(f)
+
+
+@pytest.mark.parametrize("case", _elem_cases(), ids=lambda c: f"case{c[0]}")
+def test_logprob_jsd_random(fl, case):
+    i, dtype, R, V, beta, red, in_place = case
+    print(f"case {i}: {dtype} R={R} V={V} beta={beta} {red} in_place={in_place}", flush=True)
+    x = _dist(8500 + 2 * i, R, V, dtype, True)
+    y = _dist(8501 + 2 * i, R, V, dtype, True)
+    rl, rg = oracle.jsd_logprob(to_f64(x, dtype), to_f64(y, dtype), beta, red)
+    loss, grad = fl.fljsd_jsd_logprob(to_device(x, dtype), to_device(y, dtype), beta, red,
+                                      in_place=in_place)
+    torch.cuda.synchronize()
+    assert_loss_close(from_device(loss), rl, TOL[dtype], "loss")
+    assert_tensor_close(from_device(grad), rg, TOL[dtype], "grad_logq")
+
+
+@pytest.mark.parametrize("case", _elem_cases(seed=1205), ids=lambda c: f"case{c[0]}")
+def test_tvd_random(fl, case):
+    i, dtype, R, V, _, red, in_place = case
+    print(f"case {i}: {dtype} R={R} V={V} {red} in_place={in_place}", flush=True)
+    p = _dist(8600 + 2 * i, R, V, dtype, False)
+    q = _dist(8601 + 2 * i, R, V, dtype, False)
+    q[: R // 4] = p[: R // 4]                       # tied rows
+    rl, rg = oracle.tvd(to_f64(p, dtype), to_f64(q, dtype), red)
+    loss, grad = fl.fljsd_tvd(to_device(p, dtype), to_device(q, dtype), red, in_place=in_place)
+    torch.cuda.synchronize()
+    if red == "none":
+        assert_tensor_close(from_device(loss), rl, TOL["f32"], "elementwise tvd")
+    else:
+        assert_loss_close(from_device(loss), rl, TOL[dtype], "loss")
+    g = from_device(grad)
+    assert np.all(g[: R // 4] == 0.0)
+    assert_tensor_close(g, rg, TOL[dtype], "grad_p")
