@@ -496,12 +496,14 @@ def main():
                 "unit": d["unit"], "frac": round(d["achieved"] / d["peak"], 4), "traffic": traffic,
                 "kernel": dominant, "avg_launch_ms": round(d["avg_launch_ms"], 4),
                 "per_launch": d["per_launch"]}
-    clock = clock_for(dominant)
-    if clock and d["bound"] == "mfma":
-        # The published peak assumes 2.4 GHz; the fraction at the clock the
-        # kernel held (from the committed counter summary) is reported beside it.
-        roofline["clock_mhz"] = round(clock)
-        roofline["frac_at_clock"] = round(d["achieved"] / (d["peak"] * clock / 2400.0), 4)
+    mentry = _profile_entry(MFMA_FILE, dominant)
+    if mentry and d["bound"] == "mfma":
+        # The published peak assumes 2.4 GHz. Beside it, from the committed
+        # counter run (one box, one run): the clock the kernel held there and
+        # its counted matrix flops over its own traced time against the peak
+        # at that clock.
+        roofline["clock_mhz"] = round(mentry["clock_mhz"])
+        roofline["frac_at_clock"] = round(mentry["frac_nominal"] * 2400.0 / mentry["clock_mhz"], 4)
     gemm_ms = sum(kernels[c]["ms"] for c in GEMM_CLASSES)
     gemm_flops = sum(kernels[c]["flops"] for c in GEMM_CLASSES)
     jsd_cls = ("jsd_stats", "jsd_loss", "jsd_grad")
