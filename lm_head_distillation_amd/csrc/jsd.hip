@@ -6,6 +6,10 @@
 //   pass 2  the per-row loss and the cross-column term dX_sum;
 //   pass 3  dX, written over the student logits when the caller asks for it
 //           in place.
+// With bf16 logits and a weight gradient, pass 3 also writes dX transposed
+// for the weight-gradient product and sums the loss terms itself (per row
+// over its column block, merged in a fixed order afterwards), so pass 2
+// computes dX_sum alone (and the forward KL, which needs none, skips it).
 // Everything from the loaded logit onward is fp32 (PR #1352 Details: the cast
 // happens at load). Exponentials are base 2 (PR #1352 Details, last bullet):
 // with k = log2(e)/T, a row's statistics are m = max z (in logit units, so
@@ -28,8 +32,9 @@
 //                terms
 //   forward KL:  l = P D - P + Q,  dA = Q - P          (sum_v P = 1 exactly)
 //   reverse KL:  l = P - Q - Q D,  G = sum_v l,  dA = -Q D - Q G
-// and an exact tie P == Q gives l = g = 0 (PR #1374 "Fix TVD gradient at
-// p == q": one predicate and one select per element).
+// and an exact tie gives l = g = 0 (PR #1374 "Fix TVD gradient at p == q":
+// one predicate and one select per element): P == Q for fp32 logits, equal
+// log2 probabilities a_s == a_t for bf16 logits (then P == Q too).
 // The KL terms carry "- P + Q" (which sums to zero over a row) so that each
 // term is O(D^2) and non-negative: the plain P D terms are O(D) and cancel
 // across the row, which turns the fp32 rounding of the row normalizers into a
@@ -62,7 +67,7 @@ constexpr int kWaves = kThreads / 64;
 // gradient term g (dA = g - Q G) and gacc, the term summed into G.
 //
 // DIRECT (bf16 logits): the generalized branch takes r from jsd_r_direct
-// (one hardware exponential and one log2, or a degree-5 polynomial near
+// (one hardware exponential and one log2, or a degree-4 polynomial near
 // D = 0) instead of the expm1 and log1p series, whose extra accuracy (a few
 // ulp of r against ~1e-7 relative) is kept for fp32 logits: a bf16 logit's
 // own rounding moves D by up to 2^-9 |z| / T.
