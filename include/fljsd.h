@@ -105,7 +105,13 @@ typedef enum fljsd_reduction {
  *   place, PR #1352 Details), per-row loss, row statistics (for bf16, per-tile
  *   partials written by the logits products), split-K partial sums, and for
  *   bf16 the transposed dZ and X_s chunk the weight-gradient product reads.
- *   Its contents on entry do not matter.
+ *   For bf16 with V a multiple of 256, H_s a multiple of 64 and chunks of at
+ *   least 256 rows, the size also counts W_s^T (V * H_s * 2 bytes), which the
+ *   first chunk's student logits product writes so that grad_input reads both
+ *   of its operands along the reduction index. A workspace that is short of
+ *   exactly that region still runs, with grad_input reading W_s as given
+ *   (same results, a slower product); the region is also unused when
+ *   grad_X_s is NULL. Its contents on entry do not matter.
  * Errors: FLJSD_EINVAL, FLJSD_EDTYPE, FLJSD_EALIGN, FLJSD_EWORKSPACE (all
  *   before any work is enqueued), FLJSD_EDEVICE, FLJSD_EHIP.
  */
@@ -318,7 +324,8 @@ int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
  * Details, memory table: a chunk of C rows holds both logits tensors, and only
  * the per-row loss grows with BT): for bf16 about 3 * C * V * 2 bytes (student
  * logits / dZ, teacher logits, dZ^T) plus C * H_s * 2 (X_s^T) and small
- * per-row arrays; for fp32 2 * C * V * 4 plus the per-row arrays. Pure host
+ * per-row arrays (and W_s^T, V * H_s * 2, for the shapes named under
+ * fljsd_forward_backward); for fp32 2 * C * V * 4 plus the per-row arrays. Pure host
  * arithmetic; no device is touched. Returns 0 for invalid arguments (sizes
  * <= 0, num_chunks < 1, bad dtype). */
 size_t fljsd_workspace_size(int64_t BT, int64_t H_s, int64_t H_t, int64_t V,
@@ -329,7 +336,9 @@ size_t fljsd_generalized_jsd_workspace_size(int64_t BT, int64_t V, int dtype);
 
 /* Chunk policy (a replacement for the cdiv(V, H) heuristic that PR #1352,
  * Open question 4, calls mis-tuned for JSD): the smallest num_chunks >= 1
- * whose workspace fits in budget_bytes. Larger chunks keep the GEMMs
+ * whose workspace, less the optional W_s^T region, fits in budget_bytes (that
+ * region never costs a chunk; it is used when the budget also holds it).
+ * Larger chunks keep the GEMMs
  * compute-bound, and the pages' sweep shows speed rising with chunk size.
  * Pure host arithmetic. Returns the count, or FLJSD_EINVAL for invalid sizes,
  * or FLJSD_EWORKSPACE when even one-row chunks do not fit. */

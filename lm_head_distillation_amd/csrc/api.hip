@@ -188,9 +188,12 @@ int run_jsd_passes(const JsdArgs& ja, int dtype, bool write_grad, int64_t V, int
 // Z[rows, ldz] = X[rows, H] W[V, H]^T, rounded once to the dtype. With
 // `stat_part` (bf16), also each row's statistics per N-tile of the rounded
 // logits (max, sum 2^((z - max) stat_k)) into stat_part [rows, stat_tiles].
+// With `wt` (bf16, shapes that tile evenly), the product also writes
+// W^T [H, ldwt] from the W tiles its first M-tile's workgroups hold in LDS.
 int run_logits_gemm(int dtype, const void* X, const void* W, void* Z, int64_t rows, int64_t V,
                     int64_t H, int64_t ldz, hipStream_t s, float2* stat_part = nullptr,
-                    int64_t stat_tiles = 0, float stat_k = 0.f) {
+                    int64_t stat_tiles = 0, float stat_k = 0.f, void* wt = nullptr,
+                    int64_t ldwt = 0) {
   GemmArgs g;
   g.A = X;
   g.B = W;
@@ -210,28 +213,33 @@ int run_logits_gemm(int dtype, const void* X, const void* W, void* Z, int64_t ro
   g.splitk = 1;
   g.k_per_split = H;
   g.group_m = 4;
+  g.bt = wt;
+  g.ldbt = ldwt;
+  const double side_bytes = wt ? static_cast<double>(V) * H * dtype_size(dtype) : 0.0;
   hipError_t e = timed(s, FLJSD_KCLASS_GEMM_LOGITS, 2.0 * rows * V * H,
-                       gemm_bytes(g, dtype_size(dtype)), [&] { return gemm(dtype, g, s); });
+                       gemm_bytes(g, dtype_size(dtype)) + side_bytes,
+                       [&] { return gemm(dtype, g, s); });
   return e == hipSuccess ? FLJSD_OK : fail_hip(e, "launch logits GEMM");
 }
 
 // gx[rows, H] = dZ[rows, ldz] W[V, H]; bf16 splits K when the output has few
-// tiles, summing fp32 partials (in `partial`) in split order.
+// tiles, summing fp32 partials (in `partial`) in split order. With `wt`
+// (W^T [H, ldwt]) both operands are K-contiguous.
 int run_grad_input(int dtype, const void* dZ, int64_t ldz, const void* W, int64_t rows,
                    int64_t H, int64_t V, void* gx, int splitk, int64_t k_per_split,
-                   void* partial, hipStream_t s) {
+                   void* partial, hipStream_t s, const void* wt = nullptr, int64_t ldwt = 0) {
   const int es = dtype_size(dtype);
   GemmArgs g;
   g.A = dZ;
-  g.B = W;
+  g.B = wt ? wt : W;
   g.M = rows;
   g.N = H;
   g.K = V;
   g.lda = ldz;
-  g.ldb = H;
+  g.ldb = wt ? ldwt : H;
   g.ldc = H;
   g.a_kcontig = true;
-  g.b_kcontig = false;
+  g.b_kcontig = wt != nullptr;
   g.group_m = 8;
   const bool split = dtype == FLJSD_BF16 && splitk > 1;
   if (split) {
@@ -412,8 +420,10 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
 
     float2* part_s = plan.gemm_stats ? reinterpret_cast<float2*>(ws + plan.off_spart) : nullptr;
     float2* part_t = plan.gemm_stats ? part_s + plan.C * plan.stat_tiles : nullptr;
+    // W_s^T for grad_input, written once, by the first chunk's product.
+    void* wst = (grad_X_s && plan.w_transposed) ? ws + plan.off_wst : nullptr;
     rc = run_logits_gemm(dtype, Xs + r0 * H_s * es, W_s, Zs, rows, V, H_s, plan.ldz, s, part_s,
-                         plan.stat_tiles, ja.k2);
+                         plan.stat_tiles, ja.k2, ci == 0 ? wst : nullptr, plan.ldz);
     if (rc == FLJSD_OK)
       rc = run_logits_gemm(dtype, Xt + r0 * H_t * es, W_t, Zt, rows, V, H_t, plan.ldz, s, part_t,
                            plan.stat_tiles, ja.k2);
@@ -430,7 +440,7 @@ FLJSD_EXPORT int fljsd_forward_backward_ex(const void* X_s, const void* W_s, con
     if (grad_X_s) {
       rc = run_grad_input(dtype, Zs, plan.ldz, W_s, rows, H_s, V,
                           static_cast<char*>(grad_X_s) + r0 * H_s * es, plan.splitk,
-                          plan.k_per_split, ws + plan.off_partial, s);
+                          plan.k_per_split, ws + plan.off_partial, s, wst, plan.ldz);
       if (rc != FLJSD_OK) return rc;
     }
 

@@ -43,6 +43,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 XCDs, each with its own L2
 
@@ -63,6 +64,14 @@ __device__ inline void tile_of(int bid, int nblk, int tiles_m, int tiles_n, int 
   const int r = logical % in_group;
   tm = first_m + r % gm;
   tn = r / gm;
+}
+
+// The M-tile whose workgroup writes B^T for N-tile tn (GemmArgs::bt): one of
+// the whole M-tiles, rotating with tn. Each XCD runs one range of M-tile
+// groups (tile_of), so a fixed M-tile would put every writer, and all of the
+// B^T stores, on one XCD.
+__device__ inline int side_tile_m(const GemmArgs& g, int tn) {
+  return tn % static_cast<int>(g.M / kGemmBM);
 }
 
 // Physical 16-byte chunk of logical chunk c in LDS row r (eight chunks, 128
@@ -118,7 +127,7 @@ __device__ inline uint4 load_partial_row(const uint16_t* p, int n) {
 __device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
-          int EPI, bool PRE_OLD = false, int EARLY_B = -1>
+          int EPI, bool PRE_OLD = false, int EARLY_B = -1, bool SIDE = false>
 struct GemmKernel {
   static constexpr int NT = WAVES_M * WAVES_N * 64;
   static constexpr int NW = NT / 64;
@@ -376,6 +385,42 @@ struct GemmKernel {
   static constexpr bool kSplitCopies =
       EARLY_B >= 0 && EARLY_B <= 8 && BM == 256 && BN == 256 && NW == 8;
 
+  // B^T side output (GemmArgs::bt, SIDE): the B tile of `stage` (rows n0 ..
+  // n0 + BN - 1 of B, the K-tile at k0) written transposed, bt[k][n] = B(n, k).
+  // gfx950's transposing LDS read (ds_read_b64_tr_b16) hands each lane four
+  // consecutive rows n of one column k: in each 16-lane group, lane 4j + q
+  // names row nb + 4q + j at column kb (8 bytes), and lane i receives rows
+  // nb + 4(i / 4) .. + 3 of column kb + i % 4. One wave instruction covers
+  // 64 rows x 4 columns, so each column's 64 rows leave as one 128-byte run.
+  static constexpr bool kSideOut = SIDE;
+  static_assert(!SIDE || (A_K && B_K && NW == 8 && BM == 256 && BN == 256 &&
+                          (EPI == kEpiStore || EPI == kEpiStoreStats)),
+                "B^T is written by the 256 x 256 tiles' direct-copy loop");
+  template <int SW = NW>
+  static __device__ inline void side_out(const uint4* stage, const GemmArgs& g, int64_t n0,
+                                         int64_t k0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = (threadIdx.x >> 6) % SW;
+    const int grp = lane >> 4;
+    const int li = lane & 15;
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const __attribute__((address_space(3))) char* base =
+        (const __attribute__((address_space(3))) char*)(stage);
+    uint16_t* bt = static_cast<uint16_t*>(g.bt);
+    constexpr int kInst = BN * BK / (64 * 4) / SW;
+#pragma unroll
+    for (int u = 0; u < kInst; ++u) {
+      const int idx = wave * kInst + u;
+      const int nb = 64 * (idx % (BN / 64)) + 16 * grp;
+      const int kb = 4 * (idx / (BN / 64));
+      const int n = nb + 4 * (li & 3) + (li >> 2);
+      const int off = ((BM + n) * CPR + swz<CPR>(n, kb >> 3)) * 16 + (kb & 7) * 2;
+      const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + off));
+      uint16_t* dst = bt + (k0 + kb + (li & 3)) * g.ldbt + n0 + nb + 4 * (li >> 2);
+      *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);
+    }
+  }
+
   template <int STEP>
   static __device__ inline void loop_dma2(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
                                           int64_t n0, int64_t kb, int nkf,
@@ -410,17 +455,55 @@ struct GemmKernel {
     }
   }
 
+  // The workgroup that writes B^T: the early waves copy both operands, the
+  // late waves write each stage's B tile transposed. Only the copying waves
+  // wait for their own vector-memory operations before the hand-off barrier
+  // (the writers have no copies in flight after the first tile), so the
+  // writers' stores stay in flight across K-tiles.
+  template <bool WRITER>
+  static __device__ inline void loop_side(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
+                                          int64_t n0, int64_t kb, int nkf,
+                                          floatx16 (&acc)[TM][TN]) {
+    const uint16_t* A = static_cast<const uint16_t*>(g.A);
+    const uint16_t* B = static_cast<const uint16_t*>(g.B);
+    const int wg = (threadIdx.x >> 6) % (NW / 2);
+    for (int t = 0; t < nkf; ++t) {
+      if (!WRITER || t == 0) wait_vmem_all();
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const bool more = t + 1 < nkf;
+      if constexpr (WRITER) {
+        side_out<NW / 2>(lds[t & 1], g, n0, kb + static_cast<int64_t>(t) * BK);
+      } else if (more) {
+        uint4* st = lds[(t + 1) & 1];
+        const int64_t k0 = kb + static_cast<int64_t>(t + 1) * BK;
+        dma_rows<BM / 32>(A, g.lda, m0, k0, st, 0, wg);
+        dma_rows<BN / 32>(B, g.ldb, n0, k0, st + BM * CPR, 0, wg);
+      }
+      compute_stage(lds[t & 1], acc);
+    }
+  }
+
   // Both operands K-contiguous, interior block, whole K-tiles: every tile is
   // copied straight into LDS one tile ahead of the one multiplied. At the top
   // of iteration t, tile t's copies must have landed (each wave waits for its
   // own, the barrier for everyone's) and the other stage is free again.
   static __device__ inline void mainloop_dma(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                              int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                             floatx16 (&acc)[TM][TN]) {
+                                             floatx16 (&acc)[TM][TN], bool side) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     dma_tile<BM>(A, g.lda, m0, kb, lds[0]);
     dma_tile<BN>(B, g.ldb, n0, kb, lds[0] + BM * CPR);
+    if constexpr (kSideOut) {
+      if (side) {
+        if (late_wave())
+          loop_side<true>(g, lds, m0, n0, kb, nkf, acc);
+        else
+          loop_side<false>(g, lds, m0, n0, kb, nkf, acc);
+        __syncthreads();
+        return;
+      }
+    }
     if (late_wave())
       loop_dma2<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
     else
@@ -795,7 +878,7 @@ struct GemmKernel {
       const int nkf = static_cast<int>((ke - kb) / BK);   // whole K-tiles
       if (nkf > 0) {
         if constexpr (A_K && B_K)
-          mainloop_dma(g, lds, m0, n0, kb, nkf, acc);
+          mainloop_dma(g, lds, m0, n0, kb, nkf, acc, SIDE && tm == side_tile_m(g, tn));
         else
           mainloop_mixed(g, lds, m0, n0, kb, nkf, acc);
       }
@@ -861,6 +944,18 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_wgrad_kernel
       g, tiles_m, tiles_n, group_m);
 }
 
+// The logits product that also writes B^T (GemmArgs::bt): a symbol of its own,
+// so that no other launch carries the side output's code.
+template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
+          int EPI>
+__global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_side_kernel(GemmArgs g,
+                                                                                int tiles_m,
+                                                                                int tiles_n,
+                                                                                int group_m) {
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, false, kEarlyBLogits, true>::run(
+      g, tiles_m, tiles_n, group_m);
+}
+
 constexpr int kWavesM = 2;
 constexpr int kWavesN = 4;
 
@@ -889,6 +984,16 @@ hipError_t launch_tiles(const GemmArgs& g, hipStream_t s) {
       return hipGetLastError();
     }
   }
+  if constexpr (A_K && B_K && BM == kGemmBM && WM_ == kWavesM && WN_ == kWavesN &&
+                (EPI == kEpiStore || EPI == kEpiStoreStats) && !PRE_OLD) {
+    if (g.bt) {
+      hipLaunchKernelGGL((gemm_bf16_side_kernel<BM, kGemmBN, BK, ST, WM_, WN_, A_K, B_K, EPI>), grid,
+                         block, 0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n),
+                         group_m);
+      return hipGetLastError();
+    }
+  }
+  if (g.bt) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, kGemmBN, BK, ST, WM_, WN_, A_K, B_K, EPI, PRE_OLD>), grid, block,
                      0, s, g, static_cast<int>(tiles_m), static_cast<int>(tiles_n), group_m);
   return hipGetLastError();
@@ -945,6 +1050,15 @@ hipError_t launch_layout(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+  // B^T is written only by the 256 x 256 tiles' whole-K-tile loop with a
+  // store epilogue: refuse every other launch rather than leave it unwritten.
+  if (g.bt) {
+    const bool ok = g.a_kcontig && g.b_kcontig && !g.wgrad && g.splitk == 1 &&
+                    (g.epilogue == kEpiStore || g.epilogue == kEpiStoreStats) &&
+                    g.M >= kGemmBM && g.N % kGemmBN == 0 &&
+                    g.K % Pipe<true, true>::BK == 0 && g.ldbt >= g.N;
+    if (!ok) return hipErrorInvalidValue;
+  }
   // The two layouts the pass uses: both operands K-contiguous (logits, and
   // the weight gradient after its transposes), and B N-contiguous
   // (grad_input's weight operand).

@@ -144,6 +144,13 @@ struct GemmArgs {
   float2* stat_part = nullptr;
   int64_t stat_ld = 0;
   float stat_k = 0.f;
+  // Both operands K-contiguous, bf16: when set, one workgroup per N-tile
+  // (its M-tile rotating with the N-tile, so the writers spread over the
+  // XCDs) also writes B transposed, bt[k * ldbt + n] = B(n, k), from the B
+  // tiles it holds in LDS. Needs every such block interior: N a multiple of
+  // the N tile, K of the K tile, M at least one M tile.
+  void* bt = nullptr;
+  int64_t ldbt = 0;
 };
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);

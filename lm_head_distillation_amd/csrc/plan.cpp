@@ -5,7 +5,8 @@
 // 2 * C * V * s bytes, and only the per-row loss scales with BT. For bf16 with
 // a weight gradient a third logits-sized region holds dZ^T (written by pass 3,
 // read by the weight-gradient product), 3 * C * V * s in all, plus X_s^T and
-// the per-row statistics. The policy replaces the cdiv(V, H) heuristic that
+// the per-row statistics, and (shapes that tile evenly) W_s^T, V * H_s * s,
+// for the grad_input product. The policy replaces the cdiv(V, H) heuristic that
 // the same page (Open question 4) calls mis-tuned for JSD: it takes the
 // largest chunk that fits.
 #include "plan.h"
@@ -93,8 +94,19 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   p.gemm_stats = dtype == 1;
   p.stat_tiles = cdiv(V, kGemmBN);
   p.off_spart = L.take(p.gemm_stats ? 2 * p.C : 0, p.stat_tiles, 8);
+  p.total_min = L.off;
+  // W_s^T last, so that a workspace of total_min bytes holds everything else.
+  p.w_transposed = dtype == 1 && V % kGemmBN == 0 && H_s % kGemmBK == 0 && p.C >= kGemmBM;
+  p.off_wst = L.take(p.w_transposed ? H_s : 0, p.ldz, es);
   p.total = L.off;
+  if (p.total == kSizeOverflow) drop_w_transposed(&p);
   return p;
+}
+
+void drop_w_transposed(ChunkPlan* p) {
+  p->w_transposed = false;
+  p->off_wst = 0;
+  p->total = p->total_min;
 }
 
 JsdPlan plan_jsd(int64_t BT, int64_t V) {
@@ -156,7 +168,8 @@ int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int d
   int64_t nc = 1;
   while (nc <= BT) {
     ChunkPlan p = plan_chunks(BT, H_s, H_t, V, dtype, nc);
-    if (p.total != kSizeOverflow && p.total <= budget) return nc;
+    // The optional W_s^T region never costs a chunk.
+    if (p.total_min != kSizeOverflow && p.total_min <= budget) return nc;
     // Next nc that gives a smaller chunk.
     const int64_t C = p.C;
     if (C == 1) break;

@@ -103,10 +103,21 @@ struct ChunkPlan {
   SlicePlan slices;       // for C rows
   int splitk = 1;         // split-K factor of grad_input = dZ W_s
   int64_t k_per_split = 0;
-  // Workspace layout, byte offsets from the workspace base.
+  // bf16 with V a multiple of the GEMM N tile, H_s of its K tile and chunks of
+  // at least one M tile: W_s^T [H_s, ldz] has a region of its own. The first
+  // chunk's student logits product writes it from the W_s tiles it holds in
+  // LDS, and grad_input = dZ W_s then reads both operands K-contiguous.
+  bool w_transposed = false;
+  // Workspace layout, byte offsets from the workspace base. total_min leaves
+  // out the W_s^T region (the last one): a workspace of at least total_min but
+  // under total bytes runs without it.
   size_t off_zs = 0, off_zt = 0, off_row_loss = 0, off_stats = 0, off_lg = 0, off_peak = 0,
-         off_ref = 0, off_lpart = 0, off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0, total = 0;
+         off_ref = 0, off_lpart = 0, off_partial = 0, off_xt = 0, off_spart = 0, off_dzt = 0,
+         off_wst = 0, total_min = 0, total = 0;
 };
+
+// Turns the W_s^T region off: grad_input reads W_s as given.
+void drop_w_transposed(ChunkPlan* p);
 
 // Chunk plan for num_chunks >= 1 (C = ceil(BT / num_chunks)).
 ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
@@ -122,7 +133,8 @@ struct JsdPlan {
 
 JsdPlan plan_jsd(int64_t BT, int64_t V);
 
-// Smallest num_chunks whose workspace fits the budget; 0 if none does.
+// Smallest num_chunks whose workspace (less the optional W_s^T region) fits
+// the budget; 0 if none does.
 int64_t policy_num_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype,
                           size_t budget);
 

@@ -84,6 +84,8 @@ int check_forward_backward(const void* X_s, const void* W_s, const void* X_t, co
     if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
   }
   *plan = plan_chunks(BT, H_s, H_t, V, dtype, nc);
+  // W_s^T only serves grad_input, and only when the workspace has room for it.
+  if (plan->w_transposed && (!grad_X_s || workspace_bytes < plan->total)) drop_w_transposed(plan);
   return check_workspace_total(workspace, workspace_bytes, plan->total);
 }
 

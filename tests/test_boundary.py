@@ -85,6 +85,21 @@ def cdiv(a, b):
     return -(-a // b)
 
 
+def test_policy_ignores_the_w_transposed_region(lib):
+    # 8192 x 4096 x 128256 tiles evenly: W_s^T (V * H_s * 2 bytes) is counted
+    # in the workspace size but never makes the policy pick more chunks.
+    BT, H, V = 8192, 4096, 128256
+    wst = a256(V * H * 2)
+    one = lib.fljsd_workspace_size(BT, H, H, V, BF16, 1)
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one) == 1
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one - wst) == 1
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one - wst - 1) == 2
+    # Chunks of fewer than 256 rows take no W_s^T region.
+    small = lib.fljsd_workspace_size(BT, H, H, V, BF16, 64)        # 128-row chunks
+    assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, small) == 64
+    assert small < wst
+
+
 def a256(x):
     return (x + 255) // 256 * 256
 
@@ -117,15 +132,21 @@ def test_workspace_size_rejects_bad_arguments(lib):
 
 def test_large_shapes_workspace(lib):
     # 8192 x 4096 x 128256 bf16 in one chunk: both logits chunks dominate; the
-    # transposed X_s chunk for the grad_W product adds C * H_s * 2 bytes.
+    # transposed X_s chunk for the grad_W product adds C * H_s * 2 bytes, and
+    # (V a multiple of 256, H_s of 64) W_s^T for the grad_input product
+    # V * H_s * 2.
     one = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 1)
     xt = 8192 * 4096 * 2                   # X_s^T
     dzt = 128256 * 8192 * 2                # dZ^T, written by the gradient pass
+    wst = 4096 * 128256 * 2                # W_s^T, written by the first logits product
     spart = 2 * 8192 * 501 * 8             # the logits GEMMs' row-statistic partials
-    base = 2 * 8192 * 128256 * 2 + xt + dzt + spart
+    base = 2 * 8192 * 128256 * 2 + xt + dzt + wst + spart
     assert base <= one < base + 64 * 2**20
     eight = lib.fljsd_workspace_size(8192, 4096, 4096, 128256, BF16, 8)
-    assert eight < one / 4
+    assert eight < one / 3
+    # A vocabulary that does not tile by 256 takes no W_s^T region.
+    odd = lib.fljsd_workspace_size(8192, 4096, 4096, 128256 + 8, BF16, 1)
+    assert odd < one - wst + 64 * 2**20
 
 
 def test_policy_smallest_count_that_fits(lib):

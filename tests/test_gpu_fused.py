@@ -264,6 +264,49 @@ def test_shapes(fl, dtype, BT, H_s, H_t, V, nc):
         _compare(dtype, got, _oracle_of(inp, dtype, beta, T, "batchmean"))
 
 
+# bf16 shapes whose vocabulary tiles by 256, H_s by 64, with chunks of at
+# least 256 rows: the first chunk's student logits product also writes W_s^T,
+# and grad_input reads both operands along V.
+@pytest.mark.parametrize("BT,H_s,H_t,V,nc", [
+    (256, 64, 64, 768, 1),        # one 256-row chunk, one M-tile
+    (600, 128, 128, 2560, 2),     # split-K grad_input over K-contiguous operands
+    (1025, 192, 320, 1024, 4),    # H_t differs; last chunk 254 rows (ragged M-tile)
+    (51010, 64, 64, 256, 200),    # 256-row chunks; last chunk 66 rows (128-row tiles)
+    (51004, 64, 64, 256, 200),    # last chunk 60 rows (64-row tiles)
+])
+def test_w_transposed_shapes(fl, BT, H_s, H_t, V, nc):
+    inp = _adhoc(13, BT, H_s, H_t, V, "bf16")
+    dev = _device_inputs(inp, "bf16")
+    for beta, T in ((0.5, 1.0), (0.0, 2.0), (1.0, 1.5)):
+        got = _run(fl, dev, beta, T, "batchmean", nc)
+        _compare("bf16", got, _oracle_of(inp, "bf16", beta, T, "batchmean"))
+
+
+def test_w_transposed_region_is_optional(fl):
+    """A workspace short of exactly the W_s^T region runs grad_input on W_s as
+    given; so does a call without grad_input. Same loss and grad_W bits, and
+    grad_input within rounding (the two layouts feed the same products)."""
+    BT, H, V, nc = 600, 128, 2560, 2
+    inp = _adhoc(14, BT, H, H, V, "bf16")
+    dev = _device_inputs(inp, "bf16")
+    full = fl.fljsd_workspace_size(BT, H, H, V, fl.BF16, nc)
+    wst = (V * H * 2 + 255) // 256 * 256
+    assert fl.fljsd_workspace_size(BT, H, H, V + 8, fl.BF16, nc) < full   # V + 8: no region
+    ws_full = torch.empty(full, dtype=torch.uint8, device="cuda")
+    ws_short = torch.empty(full - wst, dtype=torch.uint8, device="cuda")
+    a = _run(fl, dev, 0.5, 1.0, "batchmean", nc, workspace=ws_full)
+    b = _run(fl, dev, 0.5, 1.0, "batchmean", nc, workspace=ws_short)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2], b[2])
+    d = (a[1].float() - b[1].float()).abs().max().item()
+    print(f"grad_input max |W_s^T path - W_s path| = {d:.3e} (bit-equal: {torch.equal(a[1], b[1])})",
+          flush=True)
+    _compare("bf16", b, _oracle_of(inp, "bf16", 0.5, 1.0, "batchmean"))
+    _compare("bf16", a, _oracle_of(inp, "bf16", 0.5, 1.0, "batchmean"))
+    with pytest.raises(fl.FljsdError):
+        fl.fljsd_forward_backward(*dev, 0.5, 1.0, "batchmean", nc,
+                                  workspace=ws_short[:full - wst - 256])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_optional_gradients_and_determinism(fl, dtype):
     inp = _adhoc(8, 200, 128, 128, 4000, dtype)
