@@ -105,10 +105,11 @@ typedef enum fljsd_reduction {
  *   place, PR #1352 Details), per-row loss, row statistics (for bf16, per-tile
  *   partials written by the logits products), split-K partial sums, and for
  *   bf16 the transposed dZ and X_s chunk the weight-gradient product reads.
- *   For bf16 with V a multiple of 256, H_s a multiple of 64 and chunks of at
- *   least 256 rows, the size also counts W_s^T (V * H_s * 2 bytes), which the
- *   first chunk's student logits product writes so that grad_input reads both
- *   of its operands along the reduction index. A workspace that is short of
+ *   For bf16 with V a multiple of 256, H_s a multiple of 64, BT above 4096
+ *   and chunks of at least 512 rows, the size also counts W_s^T (V * H_s * 2
+ *   bytes), which the first chunk's student logits product writes so that
+ *   grad_input reads both of its operands along the reduction index (the
+ *   write costs a fixed time, the faster grad_input gains per row). A workspace that is short of
  *   exactly that region still runs, with grad_input reading W_s as given
  *   (same results, a slower product); the region is also unused when
  *   grad_X_s is NULL. Its contents on entry do not matter.

@@ -96,7 +96,8 @@ ChunkPlan plan_chunks(int64_t BT, int64_t H_s, int64_t H_t, int64_t V, int dtype
   p.off_spart = L.take(p.gemm_stats ? 2 * p.C : 0, p.stat_tiles, 8);
   p.total_min = L.off;
   // W_s^T last, so that a workspace of total_min bytes holds everything else.
-  p.w_transposed = dtype == 1 && V % kGemmBN == 0 && H_s % kGemmBK == 0 && p.C >= kGemmBM;
+  p.w_transposed = dtype == 1 && V % kGemmBN == 0 && H_s % kGemmBK == 0 &&
+                   BT > kWtMinRows && p.C >= kWtMinChunk;
   p.off_wst = L.take(p.w_transposed ? H_s : 0, p.ldz, es);
   p.total = L.off;
   if (p.total == kSizeOverflow) drop_w_transposed(&p);

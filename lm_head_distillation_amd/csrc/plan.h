@@ -13,6 +13,13 @@ namespace fljsd {
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 64;
+// Writing W_s^T costs the first logits product a fixed ~0.4 ms at V = 128256,
+// H_s = 4096, and each grad_input row gains ~0.08 us: measured at H_s = 4096
+// (one chunk) +0.13 ms at 2048 rows, +0.1 at 4096, -0.2 at 6144, -0.3 at
+// 8192, -0.9 at 16384; neutral at 256-row chunks, where every workgroup of
+// the first product writes.
+constexpr int64_t kWtMinRows = 4096;
+constexpr int64_t kWtMinChunk = 512;
 // Tile shape of the fp32 GEMMs.
 constexpr int kGemmF32BM = 64;
 constexpr int kGemmF32BN = 64;
@@ -103,10 +110,11 @@ struct ChunkPlan {
   SlicePlan slices;       // for C rows
   int splitk = 1;         // split-K factor of grad_input = dZ W_s
   int64_t k_per_split = 0;
-  // bf16 with V a multiple of the GEMM N tile, H_s of its K tile and chunks of
-  // at least one M tile: W_s^T [H_s, ldz] has a region of its own. The first
-  // chunk's student logits product writes it from the W_s tiles it holds in
-  // LDS, and grad_input = dZ W_s then reads both operands K-contiguous.
+  // bf16 with V a multiple of the GEMM N tile, H_s of its K tile, more than
+  // kWtMinRows rows in all and chunks of at least kWtMinChunk rows: W_s^T
+  // [H_s, ldz] has a region of its own. The first chunk's student logits
+  // product writes it from the W_s tiles it holds in LDS, and grad_input =
+  // dZ W_s then reads both operands K-contiguous.
   bool w_transposed = false;
   // Workspace layout, byte offsets from the workspace base. total_min leaves
   // out the W_s^T region (the last one): a workspace of at least total_min but
