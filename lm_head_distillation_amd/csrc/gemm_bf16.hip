@@ -1,4 +1,5 @@
-// bf16 GEMMs on CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16), fp32
+// bf16 GEMMs on CDNA4 matrix cores (v_mfma_f32_16x16x32_bf16 on 256-row
+// tiles, v_mfma_f32_32x32x16_bf16 on the skinny ones), fp32
 // accumulation, one rounding to bf16 at the end (Liger-Kernel PR #1352,
 // Details: the GEMM keeps the input dtype; PR #1429, Summary: the product and
 // beta*C are added in fp32 and rounded once).
@@ -6,6 +7,7 @@
 // One kernel template serves the pass's three products:
 //   logits       Z[C,V]    = X[C,H] W[V,H]^T       A and B K-contiguous
 //   grad_input   gX[C,H]   = dZ[C,V] W[V,H]        A K-contiguous, B N-contiguous
+//                (or B = W^T, K-contiguous, when the logits product wrote it)
 //   grad_weight  gW[V,H] (+)= dZ^T[V,C] X^T[H,C]^T  A and B K-contiguous (the
 //                pass transposes dZ and X first; its own kernel symbol)
 // LDS always holds both operands K-contiguous ([row][k], 16-byte chunks
@@ -21,9 +23,11 @@
 // keeps the matrix core busy while the other waits for its loads to be
 // accepted; on 256 x 256 tiles the later of the two issues fewer of them.
 // Edge blocks and a partial last K-tile take a bounds-checked
-// register path. Within a stage the source reads each 16-wide K step's
-// fragments ahead of the previous step's MFMAs; the compiler moves the reads
-// next to their MFMAs, and the SIMD's other wave covers the LDS latency.
+// register path. Within a stage the source reads each K step's fragments
+// ahead of the previous step's MFMAs (16 x 16 tiles: the next step's B
+// fragments ahead, each A fragment again once its row of products has
+// issued); the compiler moves the reads next to their MFMAs, and the SIMD's
+// other wave covers the LDS latency.
 // Workgroups are renumbered so the tiles
 // one XCD runs together share operand panels in that XCD's L2. Epilogues:
 // store (bf16), fp32 store (split-K partials, fp32 weight gradient), and
@@ -43,6 +47,30 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Matrix-core instruction: v_mfma_f32_16x16x32_bf16 (16 x 16 outputs, 32-deep
+// products) or v_mfma_f32_32x32x16_bf16. Both have the same nominal rate, but
+// in a register-only loop with random operands on every CU the 16 x 16 form
+// sustains 91% of it against 80% for the 32 x 32 form. The 256-row tiles use
+// the 16 x 16 form (the pass at 8192 x 4096 x 128256: 31.8 -> 30.2 ms); the
+// skinny tiles of small chunks, which stream the weights, keep 32 x 32 (16 x
+// 16 made them 10-15% slower).
+template <int MS> struct Mfma;
+template <> struct Mfma<32> {
+  using Acc = floatx16;
+  static constexpr int K = 16;
+  static __device__ inline Acc run(bf16x8 a, bf16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<16> {
+  using Acc = floatx4;
+  static constexpr int K = 32;
+  static __device__ inline Acc run(bf16x8 a, bf16x8 b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;  // MI355X: workgroups go round-robin to 8 XCDs, each with its own L2
@@ -134,13 +162,19 @@ struct GemmKernel {
   static constexpr int CPR = BK / 8;               // 16-byte chunks per LDS row
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = BN / WAVES_N;
-  static constexpr int TM = WM / 32;
-  static constexpr int TN = WN / 32;
+  // Matrix-core tiles of MS x MS outputs; a lane holds NACC accumulators of
+  // each, in groups of four consecutive rows (or, transposed, columns).
+  static constexpr int MS = BM >= 256 ? 16 : 32;
+  using Acc = typename Mfma<MS>::Acc;
+  static constexpr int NACC = MS * MS / 64;
+  static constexpr int KSTEP = Mfma<MS>::K;
+  static constexpr int TM = WM / MS;
+  static constexpr int TN = WN / MS;
   static constexpr int LDS_STAGE = (BM + BN) * CPR;   // uint4 per stage
   static_assert(CPR == 8, "K-tile of 64");
-  static_assert(TM >= 1 && TN >= 1 && WM % 32 == 0 && WN % 32 == 0, "wave tile");
+  static_assert(TM >= 1 && TN >= 1 && WM % MS == 0 && WN % MS == 0, "wave tile");
   static_assert(STAGES == 2, "two LDS stages of 64-wide K-tiles");
-  // The staged epilogues compute the transposed 32x32 products (B's fragment
+  // The staged epilogues compute the transposed products (B's fragment
   // first), which leaves four consecutive output columns of one row in each
   // group of four accumulator registers: a lane's four columns go to LDS as
   // one 8-byte (bf16) or 16-byte (fp32) write.
@@ -319,20 +353,31 @@ struct GemmKernel {
     }
   }
 
-  // Fragments of one 16-wide K step for this wave.
+  // Fragments of one K step (KSTEP deep) for this wave: lane l reads row
+  // l % MS of each tile, 16 bytes at K offset 8 (l / MS).
+  static __device__ inline bf16x8 frag_a(const uint4* cur, int ks, int lane, int wave_m, int i) {
+    const int ch = ks * (KSTEP / 8) + lane / MS;
+    const int r = wave_m * WM + i * MS + lane % MS;
+    return __builtin_bit_cast(bf16x8, cur[r * CPR + swz<CPR>(r, ch)]);
+  }
+  static __device__ inline bf16x8 frag_b(const uint4* cur, int ks, int lane, int wave_n, int j) {
+    const int ch = ks * (KSTEP / 8) + lane / MS;
+    const int r = wave_n * WN + j * MS + lane % MS;
+    return __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz<CPR>(r, ch)]);
+  }
   static __device__ inline void read_frags(const uint4* cur, int ks, int lane, int wave_m,
                                            int wave_n, bf16x8* fa, bf16x8* fb) {
-    const int ch = ks * 2 + (lane >> 5);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = wave_m * WM + i * 32 + (lane & 31);
-      fa[i] = __builtin_bit_cast(bf16x8, cur[r * CPR + swz<CPR>(r, ch)]);
-    }
+    for (int i = 0; i < TM; ++i) fa[i] = frag_a(cur, ks, lane, wave_m, i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int r = wave_n * WN + j * 32 + (lane & 31);
-      fb[j] = __builtin_bit_cast(bf16x8, cur[(BM + r) * CPR + swz<CPR>(r, ch)]);
-    }
+    for (int j = 0; j < TN; ++j) fb[j] = frag_b(cur, ks, lane, wave_n, j);
+  }
+  // Accumulator group q (four registers) of lane l covers four consecutive
+  // rows (columns, transposed) of its tile starting at quad_col(l, q).
+  static __device__ inline int quad_col(int lane, int q) { return 4 * (lane / MS) + (256 / MS) * q; }
+  static __device__ inline Acc mma(bf16x8 a, bf16x8 b, Acc c) {
+    // SWAP_D: the transposed product (B's fragment first).
+    return SWAP_D ? Mfma<MS>::run(b, a, c) : Mfma<MS>::run(a, b, c);
   }
 
   // MFMAs over one LDS stage, the next K step's fragments requested before
@@ -340,30 +385,54 @@ struct GemmKernel {
   // next to its MFMAs). hook(ks) runs before step ks's MFMAs (the main loops
   // issue the next tile's global loads from it).
   template <class Hook>
-  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN],
+  static __device__ inline void compute_stage(const uint4* cur, Acc (&acc)[TM][TN],
                                               Hook&& hook) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wave_m = wave % WAVES_M;
     const int wave_n = wave / WAVES_M;
-    constexpr int KS = BK / 16;
-    bf16x8 fa[2][TM], fb[2][TN];
-    read_frags(cur, 0, lane, wave_m, wave_n, fa[0], fb[0]);
+    constexpr int KS = BK / KSTEP;
+    if constexpr (MS == 32) {
+      bf16x8 fa[2][TM], fb[2][TN];
+      read_frags(cur, 0, lane, wave_m, wave_n, fa[0], fb[0]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + 1 < KS) read_frags(cur, ks + 1, lane, wave_m, wave_n, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
-      hook(ks);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) read_frags(cur, ks + 1, lane, wave_m, wave_n, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        hook(ks);
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = SWAP_D ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[ks & 1][j], fa[ks & 1][i],
-                                                                       acc[i][j], 0, 0, 0)
-                             : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][i], fb[ks & 1][j],
-                                                                       acc[i][j], 0, 0, 0);
+          for (int j = 0; j < TN; ++j) acc[i][j] = mma(fa[ks & 1][i], fb[ks & 1][j], acc[i][j]);
+      }
+    } else {
+      // Twice the fragments per K step: the next step's B fragments are read
+      // ahead into their own registers, each A fragment is re-read as soon as
+      // its row of products has issued.
+      bf16x8 fa[TM], fb[TN];
+      read_frags(cur, 0, lane, wave_m, wave_n, fa, fb);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bool more = ks + 1 < KS;
+        bf16x8 nb[TN];
+        if (more) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) nb[j] = frag_b(cur, ks + 1, lane, wave_n, j);
+        }
+        hook(ks);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j] = mma(fa[i], fb[j], acc[i][j]);
+          if (more) fa[i] = frag_a(cur, ks + 1, lane, wave_m, i);
+        }
+        if (more) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[j] = nb[j];
+        }
+      }
     }
   }
-  static __device__ inline void compute_stage(const uint4* cur, floatx16 (&acc)[TM][TN]) {
+  static __device__ inline void compute_stage(const uint4* cur, Acc (&acc)[TM][TN]) {
     compute_stage(cur, acc, [](int) {});
   }
 
@@ -373,7 +442,7 @@ struct GemmKernel {
   // waits for its loads to be accepted by the memory pipeline, the other
   // keeps the SIMD's matrix core busy. Measured on the 8192 x 128256 x 4096
   // logits product: 9% faster than every wave issuing at step 0.
-  static constexpr int kLateStep = BK / 32;
+  static constexpr int kLateStep = BK / KSTEP / 2;
   static __device__ inline bool late_wave() { return (threadIdx.x >> 6) >= NW / 2; }
 
   // EARLY_B >= 0 (256 x 256 tiles, 8 waves): the early waves copy all of A
@@ -424,7 +493,7 @@ struct GemmKernel {
   template <int STEP>
   static __device__ inline void loop_dma2(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
                                           int64_t n0, int64_t kb, int nkf,
-                                          floatx16 (&acc)[TM][TN]) {
+                                          Acc (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     for (int t = 0; t < nkf; ++t) {
@@ -463,7 +532,7 @@ struct GemmKernel {
   template <bool WRITER>
   static __device__ inline void loop_side(const GemmArgs& g, uint4 (*lds)[LDS_STAGE], int64_t m0,
                                           int64_t n0, int64_t kb, int nkf,
-                                          floatx16 (&acc)[TM][TN]) {
+                                          Acc (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     const int wg = (threadIdx.x >> 6) % (NW / 2);
@@ -489,7 +558,7 @@ struct GemmKernel {
   // own, the barrier for everyone's) and the other stage is free again.
   static __device__ inline void mainloop_dma(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                              int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                             floatx16 (&acc)[TM][TN], bool side) {
+                                             Acc (&acc)[TM][TN], bool side) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     dma_tile<BM>(A, g.lda, m0, kb, lds[0]);
@@ -519,7 +588,7 @@ struct GemmKernel {
   template <int STEP>
   static __device__ inline void loop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                            int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                           floatx16 (&acc)[TM][TN]) {
+                                           Acc (&acc)[TM][TN]) {
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
     uint4 ra[A_K ? 1 : regs(BM, false)], rb[B_K ? 1 : regs(BN, false)];
@@ -567,7 +636,7 @@ struct GemmKernel {
 
   static __device__ inline void mainloop_mixed(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                                int64_t m0, int64_t n0, int64_t kb, int nkf,
-                                               floatx16 (&acc)[TM][TN]) {
+                                               Acc (&acc)[TM][TN]) {
     if (late_wave())
       loop_mixed<kLateStep>(g, lds, m0, n0, kb, nkf, acc);
     else
@@ -579,7 +648,7 @@ struct GemmKernel {
   // K-tile; entered and left with every stage free.
   static __device__ inline void mainloop_checked(const GemmArgs& g, uint4 (*lds)[LDS_STAGE],
                                                  int64_t m0, int64_t n0, int64_t kb, int64_t ke,
-                                                 int t0, int t1, floatx16 (&acc)[TM][TN]) {
+                                                 int t0, int t1, Acc (&acc)[TM][TN]) {
     if (t0 >= t1) return;
     const uint16_t* A = static_cast<const uint16_t*>(g.A);
     const uint16_t* B = static_cast<const uint16_t*>(g.B);
@@ -609,8 +678,8 @@ struct GemmKernel {
 
   // bf16 store through LDS. The tile is written to LDS in 8-byte quads (a
   // lane's four consecutive columns in the transposed accumulator layout),
-  // quad slot s of row r at s ^ (r % 16) so that the 16 rows one write
-  // instruction covers per half-wave land in distinct banks. Then each 32-lane
+  // quad slot s of row r at s ^ (r % 16) so that the 16 rows a write
+  // instruction covers land in distinct banks. Then each 32-lane
   // half-wave reads one 512-byte row back in 16-byte chunks and stores it to
   // C with 16-byte writes. STATS: the same half-wave reduces the row's
   // rounded values to (max, sum 2^((z - max) k)) over the tile's valid
@@ -618,7 +687,7 @@ struct GemmKernel {
   template <bool STATS>
   static __device__ inline void epilogue_staged(const GemmArgs& g, int64_t m0, int64_t n0, int tn,
                                                 int lane, int wave_m, int wave_n,
-                                                floatx16 (&acc)[TM][TN], uint4* lds) {
+                                                Acc (&acc)[TM][TN], uint4* lds) {
     constexpr int QPR = BN / 4;   // quads per row
     constexpr int CPR16 = BN / 8; // 16-byte chunks per row
     static_assert(CPR16 == 32, "one 32-lane half-wave per row");
@@ -626,12 +695,12 @@ struct GemmKernel {
     __syncthreads();   // the stage buffers are free
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int row = wave_m * WM + i * 32 + (lane & 31);
+      const int row = wave_m * WM + i * MS + lane % MS;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5);
+        for (int q = 0; q < NACC / 4; ++q) {
+          const int col = wave_n * WN + j * MS + quad_col(lane, q);
           const int slot = (col >> 2) ^ (row & 15);
           quads[row * QPR + slot] =
               make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
@@ -699,7 +768,7 @@ struct GemmKernel {
   static constexpr int kSub = WAVES_M > 1 ? 2 : 1;
   static constexpr int kPartRows = WM / kSub;
   static constexpr int kPartPasses = kPartRows / kRowsPerPass;
-  static_assert(TM % kSub == 0 && kPartRows % kRowsPerPass == 0, "parts of whole 32-row tiles");
+  static_assert(TM % kSub == 0 && kPartRows % kRowsPerPass == 0, "parts of whole MS-row tiles");
 
   // Old values of the part starting at tile row r0 (zero outside C), as
   // 16-byte vectors: one per pass for bf16, two for fp32.
@@ -744,7 +813,7 @@ struct GemmKernel {
   static __device__ inline void epilogue_accumulate_staged(const GemmArgs& g, int64_t m0,
                                                            int64_t n0, int lane, int wave_m,
                                                            int wave_n,
-                                                           floatx16 (&acc)[TM][TN], uint4* lds,
+                                                           Acc (&acc)[TM][TN], uint4* lds,
                                                            const uint4 (*pre)[sizeof(Out) / 2]) {
     static_assert(BN == 256 && kPartRows * BN * 4 <= STAGES * LDS_STAGE * 16 &&
                       kPartRows % (NT / 32) == 0,
@@ -754,7 +823,7 @@ struct GemmKernel {
     constexpr int C16 = BN / 4;                  // fp32 16-byte chunks per row
     constexpr int ROWS_PER_PASS = kRowsPerPass;  // rows in flight per pass (one per half-wave)
     constexpr int PASSES = kPartPasses;
-    constexpr int TMP = TM / kSub;               // 32-row tiles of a wave per part
+    constexpr int TMP = TM / kSub;               // MS-row tiles of a wave per part
     Out* C = static_cast<Out*>(g.C);
     const bool vec = (g.ldc & (F32 ? 3 : 7)) == 0;
     const int c8 = threadIdx.x & 31;             // 8-column group of the row
@@ -781,12 +850,12 @@ struct GemmKernel {
 #pragma unroll
         for (int ii = 0; ii < TMP; ++ii) {
           const int i = sub * TMP + ii;
-          const int row = ii * 32 + (lane & 31);  // within the part
+          const int row = ii * MS + lane % MS;  // within the part
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int chunk = (wave_n * WN + j * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            for (int q = 0; q < NACC / 4; ++q) {
+              const int chunk = (wave_n * WN + j * MS + quad_col(lane, q)) >> 2;
               lds[row * C16 + (chunk ^ (row & 31))] =
                   make_uint4(__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
                              __float_as_uint(acc[i][j][4 * q + 2]),
@@ -857,13 +926,13 @@ struct GemmKernel {
     const int64_t ke = min(g.K, kb + g.k_per_split);
     const int nk = static_cast<int>((ke - kb + BK - 1) / BK);
 
-    floatx16 acc[TM][TN];
+    Acc acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
 
     // PRE_OLD (read-add-write with one wave row): the old values are loaded
     // before the main loop, in flight with the first tile's copies, so the
@@ -893,20 +962,20 @@ struct GemmKernel {
       epilogue_accumulate_staged<AccOut, kPrefetchOld>(g, m0, n0, lane, wave_m, wave_n, acc,
                                                        &lds[0][0], pre_old);
     } else {
-      // fp32 store (split-K partials, plane `split`). Accumulator register r
-      // of lane l in a 32x32 tile holds row 8*(r/4) + 4*(l/32) + r%4, column
-      // l%32.
+      // fp32 store (split-K partials, plane `split`), untransposed layout:
+      // accumulator r of lane l holds row quad_col(l, r / 4) + r % 4, column
+      // l % MS of its tile.
       static_assert(EPI == kEpiPartialF32, "epilogue");
       float* C = static_cast<float*>(g.C) + static_cast<int64_t>(split) * g.M * g.ldc;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const int64_t n = n0 + wave_n * WN + j * 32 + (lane & 31);
+          const int64_t n = n0 + wave_n * WN + j * MS + lane % MS;
           if (n >= g.N) continue;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t m = m0 + wave_m * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          for (int r = 0; r < NACC; ++r) {
+            const int64_t m = m0 + wave_m * WM + i * MS + quad_col(lane, r >> 2) + (r & 3);
             if (m < g.M) C[m * g.ldc + n] = acc[i][j][r];
           }
         }
