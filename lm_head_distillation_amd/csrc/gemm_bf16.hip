@@ -985,11 +985,14 @@ struct GemmKernel {
 };
 
 // Copy split of the 256 x 256 tiles' main loop per product (see kSplitCopies),
-// measured on the 8192 x 128256 x 4096 shapes: the logits product 7.15 ->
-// 7.03 ms with 12 / 4 copies per early / late wave, grad_W 7.39 -> 7.32 ms
-// with 9 / 7 (each best among 8 / 8 .. 14 / 2 and the even split).
-constexpr int kEarlyBLogits = 4;
+// measured inside the 8192 x 4096 x 128256 pass (each the best of 8 / 8 ..
+// 14 / 2 copies per early / late wave): logits 10 / 6 (2 x 7.07 ms against
+// 7.21 at 12 / 4), grad_input 9 / 7 (6.30 against 6.50), grad_W 9 / 7.
+constexpr int kEarlyBLogits = 2;
+constexpr int kEarlyBOther = 1;
 constexpr int kEarlyBWgrad = 1;
+template <int EPI>
+constexpr int early_b() { return EPI == kEpiStoreStats ? kEarlyBLogits : kEarlyBOther; }
 
 template <int BM, int BN, int BK, int STAGES, int WAVES_M, int WAVES_N, bool A_K, bool B_K,
           int EPI, bool PRE_OLD = false>
@@ -997,7 +1000,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_kernel(GemmA
                                                                            int tiles_m,
                                                                            int tiles_n,
                                                                            int group_m) {
-  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD, kEarlyBLogits>::run(
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, PRE_OLD, early_b<EPI>()>::run(
       g, tiles_m, tiles_n, group_m);
 }
 
@@ -1021,7 +1024,7 @@ __global__ __launch_bounds__(WAVES_M * WAVES_N * 64) void gemm_bf16_side_kernel(
                                                                                 int tiles_m,
                                                                                 int tiles_n,
                                                                                 int group_m) {
-  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, false, kEarlyBLogits, true>::run(
+  GemmKernel<BM, BN, BK, STAGES, WAVES_M, WAVES_N, A_K, B_K, EPI, false, early_b<EPI>(), true>::run(
       g, tiles_m, tiles_n, group_m);
 }
 
