@@ -911,6 +911,9 @@ struct GemmKernel {
   // stack and read them from scratch memory inside the loops.
   static __device__ __attribute__((always_inline)) void run(const GemmArgs& g, int tiles_m, int tiles_n,
                                                            int group_m) {
+    // The only __shared__ object of these kernels: with a second one the
+    // compiler's LDS alias scopes make it wait for the direct copies in flight
+    // before the main loop's fragment reads (measured: logits +0.7 ms).
     __shared__ uint4 lds[STAGES][LDS_STAGE];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
