@@ -713,8 +713,56 @@ struct GemmKernel {
     const bool vec = (g.ldc & 7) == 0;
     const int c = threadIdx.x & 31;                 // 16-byte chunk of the row
     const int64_t n = n0 + 8 * c;
-#pragma unroll 4
-    for (int row = threadIdx.x >> 5; row < BM; row += NT / 32) {
+    // Interior tiles: straight-line code over kRowsAtOnce rows at a time, so
+    // that the rows' LDS reads, stores and reduction chains overlap (the
+    // general loop below, with its per-element bounds, is not unrolled).
+    constexpr int kRowStep = NT / 32;
+    constexpr int kRowsAtOnce = 4;
+    if (m0 + BM <= g.M && n0 + BN <= g.N && vec) {
+      static_assert(BM % (kRowStep * kRowsAtOnce) == 0, "whole groups of rows");
+      for (int row0 = threadIdx.x >> 5; row0 < BM; row0 += kRowStep * kRowsAtOnce) {
+        uint4 v[kRowsAtOnce];
+#pragma unroll
+        for (int u = 0; u < kRowsAtOnce; ++u) {
+          const int row = row0 + u * kRowStep;
+          const int f = row & 15;
+          v[u] = lds[row * CPR16 + (c ^ (f >> 1))];
+          if (f & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
+        }
+#pragma unroll
+        for (int u = 0; u < kRowsAtOnce; ++u)
+          *reinterpret_cast<uint4*>(C + (m0 + row0 + u * kRowStep) * g.ldc + n) = v[u];
+        if constexpr (STATS) {
+          float z[kRowsAtOnce][8], mx[kRowsAtOnce], d[kRowsAtOnce];
+#pragma unroll
+          for (int u = 0; u < kRowsAtOnce; ++u) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[u][e] = __uint_as_float((w[e >> 1] >> (16 * (e & 1))) << 16);
+            mx[u] = z[u][0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx[u] = fmaxf(mx[u], z[u][e]);
+          }
+#pragma unroll
+          for (int u = 0; u < kRowsAtOnce; ++u) mx[u] = half_wave_max(mx[u]);
+#pragma unroll
+          for (int u = 0; u < kRowsAtOnce; ++u) {
+            d[u] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[u] += __builtin_amdgcn_exp2f((z[u][e] - mx[u]) * g.stat_k);
+          }
+#pragma unroll
+          for (int u = 0; u < kRowsAtOnce; ++u) d[u] = half_wave_sum(d[u]);
+          if (c == 0) {
+#pragma unroll
+            for (int u = 0; u < kRowsAtOnce; ++u)
+              g.stat_part[(m0 + row0 + u * kRowStep) * g.stat_ld + tn] = make_float2(mx[u], d[u]);
+          }
+        }
+      }
+      return;
+    }
+    for (int row = threadIdx.x >> 5; row < BM; row += kRowStep) {
       const int f = row & 15;
       uint4 v = lds[row * CPR16 + (c ^ (f >> 1))];
       if (f & 1) v = make_uint4(v.z, v.w, v.x, v.y);
