@@ -280,7 +280,10 @@ int fljsd_tvd(const void* p, const void* q, int64_t BT, int64_t V, int64_t ld,
  *             for the workspace size).
  * Outputs (every element written): loss fp32 (1 or BT values); grad_X
  *   [BT, H] and grad_W [V, H] in dtype, each optional (NULL skips it).
- * Workspace: at least fljsd_flce_workspace_size(BT, H, V, dtype, num_chunks).
+ * Workspace: at least fljsd_flce_workspace_size(BT, H, V, dtype, num_chunks),
+ *   which counts, for the shapes named under fljsd_forward_backward, a W^T
+ *   region (V * H * 2 bytes) for grad_X; a workspace short of exactly that
+ *   region runs grad_X on W as given (same results).
  * Errors: FLJSD_EINVAL (NULL required pointer, sizes <= 0, label_smoothing
  *   outside [0, 1] or nan, num_chunks < 0), FLJSD_EDTYPE, FLJSD_EALIGN,
  *   FLJSD_EWORKSPACE, FLJSD_EDEVICE, FLJSD_EHIP.
@@ -314,8 +317,8 @@ int fljsd_flce_forward_backward_ex(const void* X, const void* W, const int64_t* 
                                    void* stream);
 
 /* Workspace bytes of fljsd_flce_forward_backward (0 for invalid arguments),
- * and the smallest chunk count whose workspace fits `budget_bytes` (or a
- * negative status code). Host-only. */
+ * and the smallest chunk count whose workspace, less the optional W^T
+ * region, fits `budget_bytes` (or a negative status code). Host-only. */
 size_t fljsd_flce_workspace_size(int64_t BT, int64_t H, int64_t V, int dtype, int num_chunks);
 int fljsd_flce_plan_num_chunks(int64_t BT, int64_t H, int64_t V, int dtype,
                                size_t budget_bytes);

@@ -725,7 +725,10 @@ FLJSD_EXPORT int fljsd_flce_forward_backward_ex(const void* X, const void* W,
   for (int64_t ci = 0; ci < plan.n_chunks; ++ci) {
     const int64_t r0 = ci * plan.C;
     const int64_t rows = std::min(plan.C, BT - r0);
-    rc = run_logits_gemm(dtype, Xc + r0 * H * es, W, Z, rows, V, H, plan.ldz, s);
+    // W^T for grad_input, written once, by the first chunk's product.
+    void* wt = (grad_X && plan.w_transposed) ? ws + plan.off_wt : nullptr;
+    rc = run_logits_gemm(dtype, Xc + r0 * H * es, W, Z, rows, V, H, plan.ldz, s, nullptr, 0, 0.f,
+                         ci == 0 ? wt : nullptr, plan.ldz);
     if (rc != FLJSD_OK) return rc;
     ca.rows = rows;
     ca.labels = labels + r0;
@@ -742,7 +745,7 @@ FLJSD_EXPORT int fljsd_flce_forward_backward_ex(const void* X, const void* W,
     if (grad_X) {
       rc = run_grad_input(dtype, Z, plan.ldz, W, rows, H, V,
                           static_cast<char*>(grad_X) + r0 * H * es, plan.splitk,
-                          plan.k_per_split, ws + plan.off_partial, s);
+                          plan.k_per_split, ws + plan.off_partial, s, wt, plan.ldz);
       if (rc != FLJSD_OK) return rc;
     }
     if (grad_W) {

@@ -148,15 +148,27 @@ CePlan plan_ce_chunks(int64_t BT, int64_t H, int64_t V, int dtype, int64_t num_c
   p.off_zy = L.take(p.C, 1, 4);
   p.off_scale = L.take(16, 1, 1);
   p.off_partial = L.take(p.splitk > 1 ? p.splitk * p.C : 0, H, 4);
+  p.total_min = L.off;
+  // W^T last (the same rule and reason as the JSD pass's W_s^T region).
+  p.w_transposed = dtype == 1 && V % kGemmBN == 0 && H % kGemmBK == 0 && BT > kWtMinRows &&
+                   p.C >= kWtMinChunk;
+  p.off_wt = L.take(p.w_transposed ? H : 0, p.ldz, es);
   p.total = L.off;
+  if (p.total == kSizeOverflow) drop_w_transposed(&p);
   return p;
+}
+
+void drop_w_transposed(CePlan* p) {
+  p->w_transposed = false;
+  p->off_wt = 0;
+  p->total = p->total_min;
 }
 
 int64_t policy_num_chunks_ce(int64_t BT, int64_t H, int64_t V, int dtype, size_t budget) {
   int64_t nc = 1;
   while (nc <= BT) {
     const CePlan p = plan_ce_chunks(BT, H, V, dtype, nc);
-    if (p.total != kSizeOverflow && p.total <= budget) return nc;
+    if (p.total_min != kSizeOverflow && p.total_min <= budget) return nc;
     if (p.C == 1) break;
     nc = cdiv(BT, p.C - 1);
   }

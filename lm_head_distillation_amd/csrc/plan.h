@@ -153,11 +153,14 @@ struct CePlan {
   int splitk = 1;
   int64_t k_per_split = 0;
   bool transposed_grad_w = false;
+  bool w_transposed = false;   // W^T [H, ldz] for grad_input, as in ChunkPlan
   size_t off_z = 0, off_zt = 0, off_xt = 0, off_row_loss = 0, off_stats = 0, off_zy = 0,
-         off_scale = 0, off_partial = 0, total = 0;
+         off_scale = 0, off_partial = 0, off_wt = 0, total_min = 0, total = 0;
 };
+void drop_w_transposed(CePlan* p);
 
 CePlan plan_ce_chunks(int64_t BT, int64_t H, int64_t V, int dtype, int64_t num_chunks);
+// Smallest num_chunks whose workspace (less the optional W^T region) fits.
 int64_t policy_num_chunks_ce(int64_t BT, int64_t H, int64_t V, int dtype, size_t budget);
 
 }  // namespace fljsd

@@ -165,6 +165,7 @@ int check_flce(const void* X, const void* W, const int64_t* labels, int64_t BT, 
     if (nc <= 0) return fail(FLJSD_EWORKSPACE, "no chunk count fits the workspace");
   }
   *plan = plan_ce_chunks(BT, H, V, dtype, nc);
+  if (plan->w_transposed && (!grad_X || workspace_bytes < plan->total)) drop_w_transposed(plan);
   return check_workspace_total(workspace, workspace_bytes, plan->total);
 }
 

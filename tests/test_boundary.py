@@ -94,7 +94,7 @@ def test_policy_ignores_the_w_transposed_region(lib):
     assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one) == 1
     assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one - wst) == 1
     assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, one - wst - 1) == 2
-    # Chunks of fewer than 256 rows take no W_s^T region.
+    # Chunks of fewer than 512 rows take no W_s^T region.
     small = lib.fljsd_workspace_size(BT, H, H, V, BF16, 64)        # 128-row chunks
     assert lib.fljsd_plan_num_chunks(BT, H, H, V, BF16, small) == 64
     assert small < wst
@@ -371,13 +371,19 @@ def test_flce_ex_rejects(lib, over, code):
 def test_flce_workspace_and_policy(lib):
     BT, H, V = 8192, 4096, 128256
     one = lib.fljsd_flce_workspace_size(BT, H, V, BF16, 1)
-    # logits chunk + dZ^T + X^T dominate
-    assert BT * V * 2 * 2 + BT * H * 2 <= one < BT * V * 2 * 2 + BT * H * 2 + 64 * 2**20
+    # logits chunk + dZ^T + X^T dominate, plus W^T (V * H * 2) for grad_X
+    wt = a256(V * H * 2)
+    base = BT * V * 2 * 2 + BT * H * 2 + wt
+    assert base <= one < base + 64 * 2**20
     assert lib.fljsd_flce_workspace_size(BT, H, V, 7, 1) == 0
     assert lib.fljsd_flce_workspace_size(BT, H, V, BF16, 0) == 0
     assert lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, one) == 1
+    assert lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, one - wt) == 1   # W^T costs no chunk
     nc = lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, one // 3)
-    assert nc > 1 and lib.fljsd_flce_workspace_size(BT, H, V, BF16, nc) <= one // 3
+    assert nc > 1 and lib.fljsd_flce_workspace_size(BT, H, V, BF16, nc) - wt <= one // 3
+    # No region at 4096 rows.
+    assert (lib.fljsd_flce_workspace_size(4104, H, V, BF16, 1)
+            - lib.fljsd_flce_workspace_size(4096, H, V, BF16, 1)) >= wt
     assert lib.fljsd_flce_plan_num_chunks(BT, H, V, BF16, 100) == EWORKSPACE
 
 

@@ -87,6 +87,32 @@ def test_shapes(fl, dtype, BT, H, V, nc):
     _check(dtype, got, ref, f"{BT}x{H}x{V} nc={nc}")
 
 
+# bf16 shapes with more than 4096 rows, V a multiple of 256 and H of 64, chunks
+# of at least 512 rows: the first chunk's logits product also writes W^T and
+# grad_X reads both operands along V.
+@pytest.mark.parametrize("BT,H,V,nc", [(4160, 64, 768, 1), (4608, 128, 2560, 9), (4601, 192, 1024, 4)])
+def test_w_transposed_shapes(fl, BT, H, V, nc):
+    X, W, y = _case(612, BT, H, V, "bf16")
+    got = _run(fl, X, W, y, "bf16", -100, 0.05, "mean", nc)
+    ref = oracle.fused_linear_cross_entropy(to_f64(X, "bf16"), to_f64(W, "bf16"), y, -100, 0.05, "mean")
+    _check("bf16", got, ref, f"{BT}x{H}x{V} nc={nc}")
+
+
+def test_w_transposed_region_is_optional(fl):
+    """A workspace short of exactly the W^T region runs grad_X on W as given:
+    the same LDS contents and MFMA sequence, so the same bits."""
+    BT, H, V, nc = 4160, 128, 2560, 2
+    X, W, y = _case(613, BT, H, V, "bf16")
+    full = fl.fljsd_flce_workspace_size(BT, H, V, fl.BF16, nc)
+    wt = (V * H * 2 + 255) // 256 * 256
+    ws_full = torch.empty(full, dtype=torch.uint8, device="cuda")
+    ws_short = torch.empty(full - wt, dtype=torch.uint8, device="cuda")
+    a = _run(fl, X, W, y, "bf16", -100, 0.05, "mean", nc, workspace=ws_full)
+    b = _run(fl, X, W, y, "bf16", -100, 0.05, "mean", nc, workspace=ws_short)
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+
+
 def test_all_rows_ignored(fl):
     X, W, _ = _case(604, 16, 64, 300, "bf16")
     y = np.full(16, -100, dtype=np.int64)
