@@ -76,7 +76,26 @@ def _fused_cases(n=24, seed=20261202):
     return cases
 
 
-@pytest.mark.parametrize("case", _fused_cases(), ids=lambda c: f"case{c[0]}")
+def _fused_wt_cases(n=6, seed=20261203):
+    """bf16 shapes past 4096 rows whose vocabulary tiles by 256 and H_s by 64:
+    with chunks of at least 512 rows the pass writes W_s^T and grad_input
+    reads it (every option, reduction and chunk count mixed in)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        BT = int(rng.integers(4097, 6200))
+        H_s = 64 * int(rng.integers(1, 5))
+        H_t = H_s if rng.random() < 0.5 else 8 * int(rng.integers(1, 40))
+        V = 256 * int(rng.integers(1, 12))
+        nc = int(rng.choice([0, 1, 2, 5, 9]))
+        T = float(np.float32(rng.uniform(0.8, 3.0)))
+        red = REDUCTIONS[int(rng.integers(0, 4))]
+        opt = ["plain", "f32_gw", "accumulate"][int(rng.integers(0, 3))]
+        cases.append((100 + i, "bf16", BT, H_s, H_t, V, nc, _beta(rng), T, red, opt))
+    return cases
+
+
+@pytest.mark.parametrize("case", _fused_cases() + _fused_wt_cases(), ids=lambda c: f"case{c[0]}")
 def test_fused_pass_random(fl, case):
     i, dtype, BT, H_s, H_t, V, nc, beta, T, red, opt = case
     print(f"case {i}: {dtype} BT={BT} H_s={H_s} H_t={H_t} V={V} nc={nc} beta={beta} T={T} "
