@@ -729,9 +729,11 @@ struct GemmKernel {
           v[u] = lds[row * CPR16 + (c ^ (f >> 1))];
           if (f & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
         }
+        // Non-temporal: the logits are read next by the loss passes, not by
+        // this product (pass 2 0.71 -> 0.645 ms, logits -0.05 ms).
 #pragma unroll
         for (int u = 0; u < kRowsAtOnce; ++u)
-          *reinterpret_cast<uint4*>(C + (m0 + row0 + u * kRowStep) * g.ldc + n) = v[u];
+          st_stream(C + (m0 + row0 + u * kRowStep) * g.ldc + n, v[u]);
         if constexpr (STATS) {
           float z[kRowsAtOnce][8], mx[kRowsAtOnce], d[kRowsAtOnce];
 #pragma unroll
