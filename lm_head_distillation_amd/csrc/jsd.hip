@@ -22,7 +22,7 @@
 // D = ln P - ln Q = (a_t - a_s) ln 2:
 //   generalized: r = ln(beta e^D + 1 - beta), for fp32 logits from mix_log
 //                (full relative accuracy at every D and beta; bf16 logits:
-//                the direct form described at jsd_terms),
+//                the base-2 form described at gen_terms),
 //                ln(P/M) = D - r, ln(Q/M) = -r,
 //                l = beta P (D - r) - (1-beta) Q r,   g = -(1-beta) Q r,
 //                dA = g - Q G with G = sum_v g (dX_sum); for fp32 logits
@@ -32,9 +32,11 @@
 //                terms
 //   forward KL:  l = P D - P + Q,  dA = Q - P          (sum_v P = 1 exactly)
 //   reverse KL:  l = P - Q - Q D,  G = sum_v l,  dA = -Q D - Q G
-// and an exact tie gives l = g = 0 (PR #1374 "Fix TVD gradient at p == q":
-// one predicate and one select per element): P == Q for fp32 logits, equal
-// log2 probabilities a_s == a_t for bf16 logits (then P == Q too).
+// and an exact tie gives l = g = 0 (PR #1374 "Fix TVD gradient at p == q"):
+// P == Q for fp32 logits, by one predicate and one select per element; for
+// bf16 logits equal log2 probabilities a_s == a_t (then P == Q too), where
+// the generalized terms vanish by themselves (gen_terms) and the KL branches
+// take the fp32 test.
 // The KL terms carry "- P + Q" (which sums to zero over a row) so that each
 // term is O(D^2) and non-negative: the plain P D terms are O(D) and cancel
 // across the row, which turns the fp32 rounding of the row normalizers into a
@@ -64,32 +66,13 @@ constexpr int kWaves = kThreads / 64;
 
 // Per-element terms of the divergence; see the file comment. Inputs are the
 // log2 probabilities a_s, a_t. Outputs: Q and P, the loss term l, the
-// gradient term g (dA = g - Q G) and gacc, the term summed into G.
-//
-// DIRECT (bf16 logits): the generalized branch takes r from jsd_r_direct
-// (one hardware exponential and one log2, or a degree-4 polynomial near
-// D = 0) instead of the expm1 and log1p series, whose extra accuracy (a few
-// ulp of r against ~1e-7 relative) is kept for fp32 logits: a bf16 logit's
-// own rounding moves D by up to 2^-9 |z| / T.
-template <int MODE, bool DIRECT = false>
+// gradient term g (dA = g - Q G) and gacc, the term summed into G. bf16
+// logits take the generalized branch from gen_terms instead.
+template <int MODE>
 __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float& P, float& l,
                                  float& g, float& gacc, const BetaWeights* bw = nullptr) {
   Q = hw_exp2(as);
   P = hw_exp2(at);
-  if constexpr (DIRECT && MODE == kModeGeneralized) {
-    // A tie (equal log-probabilities, so P == Q; masked columns, both -inf,
-    // included) selects zeros over whatever the terms evaluated to.
-    // (Evaluating a tie at D = 0 instead, with no branch, measured 7% slower.)
-    const float t = at - as;
-    const float D = t * kLn2;
-    float r, dmr;
-    jsd_r_direct(D, t, beta, r, dmr);
-    const bool tie = as == at;
-    l = tie ? 0.f : beta * P * dmr - (1.f - beta) * Q * r;
-    g = tie ? 0.f : -(1.f - beta) * Q * r;
-    gacc = g;
-    return;
-  }
   if (P == Q) {  // exact tie: no loss, no gradient term
     l = 0.f;
     g = 0.f;
@@ -130,6 +113,70 @@ __device__ inline void jsd_terms(float as, float at, float beta, float& Q, float
 __device__ inline float gsum_plain(float gsum, float as, float at, float Q, float beta, float cg) {
   const float u = fmaf(beta, hw_exp2(fminf(at - as, 64.f)), 1.f - beta);
   return fmaf(as == at ? 0.f : Q, hw_log2(u) * cg, gsum);
+}
+
+// bf16 logits, generalized branch: the terms of one element, shared by every
+// pass that evaluates them (pass 2's loss, pass 3's dZ with or without the
+// transposed copy, pass 3's loss), so that no result depends on which
+// outputs were asked for. In base 2,
+// with t = a_t - a_s = D / ln 2, r2 = r / ln 2 for r = ln(beta e^D + 1 - beta):
+//  - below |D| = 1/16, r's Taylor series to degree 4 (r is the cumulant
+//    generating function of a Bernoulli(beta) variable, so the coefficient of
+//    D^n / n! is its n-th cumulant; truncation below 1.3e-7 relative there),
+//    which keeps a small r accurate relative to itself;
+//  - beyond, log2(beta 2^t + 1 - beta), 2^t taken at min(t, 64) and the rest
+//    of t added back (past 64 the 1 - beta term is below 2^-64 of the
+//    other); both terms are positive, so nothing cancels.
+// dmr2 = t - r2 = (D - r) / ln 2. A tie (t == 0, finite logits) takes the
+// series branch and gives r2 = dmr2 = 0, so both terms vanish with no select;
+// masked columns (-inf in both rows) give NaN and the callers leave them out.
+// Outputs: dz = grad_scale (g - Q G) with g = -(1 - beta) Q r, from
+// nG = -G grad_scale and cg = -(1 - beta) ln 2 grad_scale; and the loss
+// term over ln 2, l2 = (beta P (D - r) - (1 - beta) Q r) / ln 2.
+struct GenBeta {
+  float beta, cb, c2, c3, c4, cg;
+};
+__device__ inline GenBeta gen_beta(float beta, float grad_scale) {
+  const float v = beta * (1.f - beta);  // the Bernoulli variance
+  return {beta,
+          1.f - beta,
+          v * (0.5f * kLn2),
+          v * (1.f - 2.f * beta) * (kLn2 * kLn2 / 6.f),
+          v * (1.f - 6.f * v) * (kLn2 * kLn2 * kLn2 / 24.f),
+          -(1.f - beta) * kLn2 * grad_scale};
+}
+struct GenRow {
+  float ms, ls, mt, lt, nG;
+};
+__device__ inline GenRow gen_row(const float4& L, float G, float grad_scale) {
+  return {L.x, -L.y, L.z, -L.w, -G * grad_scale};
+}
+// a_s = (z_s - m_s) k - log2 d_s, one FMA after an exact subtraction (two
+// bf16 values): an element at its row's maximum gets exactly -log2 d, and
+// rows that differ by a constant shift give equal log2 probabilities.
+__device__ inline float gen_as(float z, float k, const GenRow& rw) {
+  return fmaf(z - rw.ms, k, rw.ls);
+}
+__device__ inline float gen_at(float z, float k, const GenRow& rw) {
+  return fmaf(z - rw.mt, k, rw.lt);
+}
+constexpr float kGenSmallT = 0.0625f / kLn2;  // |D| = 1/16
+__device__ inline void gen_terms(float as, float at, float nG, const GenBeta& c, float& dz,
+                                 float& l2) {
+  const float Q = hw_exp2(as), P = hw_exp2(at);
+  const float t = at - as;
+  const float tc = fminf(t, 64.f);
+  const float rl = hw_log2(fmaf(c.beta, hw_exp2(tc), c.cb)) + (t - tc);
+  float p = fmaf(c.c4, t, c.c3);
+  p = fmaf(p, t, c.c2);
+  p = fmaf(p, t, c.beta);
+  const float rs = p * t;
+  // Both branches evaluated, then selected (no divergent branch per element).
+  const float r2 = fabsf(t) < kGenSmallT ? rs : rl;
+  const float dmr2 = t - r2;
+  const float Qr = Q * r2;
+  l2 = fmaf(c.beta * P, dmr2, -c.cb * Qr);
+  dz = fmaf(Q, nG, c.cg * Qr);
 }
 
 // Row statistics from the S pass-1 partials, merged in slice order by one
@@ -314,6 +361,11 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
   const float k = a.k2;
   const BetaWeights bw = beta_weights(a.beta);
   const float cg = -(1.f - a.beta) * kLn2;
+  // bf16 generalized: the terms of gen_terms (loss over ln 2, rescaled below)
+  // and G from gsum_plain.
+  constexpr bool kGen16 = sizeof(T) == 2 && MODE == kModeGeneralized;
+  const GenBeta gb = gen_beta(a.beta, 0.f);
+  const GenRow rw = gen_row(L, 0.f, 0.f);
   // fp32 forward KL also sums Q and P over the elements below the student's
   // maximum and counts the elements at it, for pass 3's peak rewrite.
   constexpr bool kPeak = sizeof(T) == 4 && MODE == kModeForwardKL;
@@ -324,18 +376,24 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
     load8(zs, v, n, a.vec_ok, ys);
     load8(zt, v, n, a.vec_ok, yt);
     // Columns past the row end load as -inf in both rows: Q = P = 0, an exact
-    // tie, which adds exactly 0 to every sum, so no per-element mask is needed.
+    // tie, which adds exactly 0 to every sum of jsd_terms and gsum_plain
+    // (gen_terms' loss term is NaN there and is masked).
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if constexpr (kGen16) {
+        const float as = gen_as(ys[i], k, rw), at = gen_at(yt[i], k, rw);
+        float dz, l2;
+        gen_terms(as, at, 0.f, gb, dz, l2);
+        lsum += i < n ? l2 : 0.f;
+        gsum = gsum_plain(gsum, as, at, hw_exp2(as), a.beta, cg);
+        continue;
+      }
       float Q, P, l, g, gacc;
       const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
-      jsd_terms<MODE, sizeof(T) == 2>(as, at, a.beta, Q, P, l, g, gacc, &bw);
+      jsd_terms<MODE>(as, at, a.beta, Q, P, l, g, gacc, &bw);
       if constexpr (kShift) gacc = shifted_g<MODE>(rs, ys[i], yt[i], at - as, Q, P, k, a.beta);
       lsum += l;
-      if constexpr (sizeof(T) == 2 && MODE == kModeGeneralized)
-        gsum = gsum_plain(gsum, as, at, Q, a.beta, cg);
-      else
-        gsum += gacc;
+      gsum += gacc;
       if constexpr (kPeak) {
         const bool rest = ys[i] < L.x;
         qrest += rest ? Q : 0.f;
@@ -344,6 +402,7 @@ __global__ __launch_bounds__(kThreads) void jsd_loss_kernel(JsdArgs a) {
       }
     }
   }
+  if constexpr (kGen16) lsum *= kLn2;
   lsum = wave_sum(lsum);
   gsum = wave_sum(gsum);
   __shared__ float2 sh[kWaves];
@@ -426,6 +485,9 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
   }
   __syncthreads();
   const float G = sh_G;
+  constexpr bool kGen16 = sizeof(T) == 2 && MODE == kModeGeneralized;
+  const GenBeta gb = gen_beta(a.beta, a.grad_scale);
+  const GenRow rw = gen_row(L, G, a.grad_scale);
   // Peak rewrite (fp32 forward KL): when the student's row has one dominant
   // element p with Q_p near 1, Q_p - P_p computed from the rounded Q_p and P_p
   // keeps only ~1e-7 / |Q_p - P_p| relative accuracy. Summing the other
@@ -444,9 +506,14 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_kernel(JsdArgs a) {
     load8(zt, v, n, a.vec_ok, yt);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      if constexpr (kGen16) {
+        float l2;
+        gen_terms(gen_as(ys[i], k, rw), gen_at(yt[i], k, rw), rw.nG, gb, out[i], l2);
+        continue;
+      }
       float Q, P, l, g, gacc;
       const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
-      jsd_terms<MODE, sizeof(T) == 2>(as, at, a.beta, Q, P, l, g, gacc, &bw);
+      jsd_terms<MODE>(as, at, a.beta, Q, P, l, g, gacc, &bw);
       if constexpr (kShift) g = shifted_g<MODE>(rs, ys[i], yt[i], at - as, Q, P, k, a.beta);
       float dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
       if (rewrite && ys[i] == L.x) dA = pk.y - pk.x;
@@ -552,17 +619,6 @@ hipError_t launch_loss_t(const JsdArgs& a, hipStream_t s, dim3 grid) {
   return hipGetLastError();
 }
 
-// bf16 terms of the fused pass with the loss moved into pass 3: a tie is
-// equality of the two log2-probabilities (then P == Q, and masked columns,
-// where both are -inf, count as ties too). Returns g, the term of
-// dA = g - Q G (generalized), and Q, r and D - r for the loss.
-__device__ inline float g_direct(float as, float at, float beta, float& Q, float& r, float& dmr) {
-  Q = hw_exp2(as);
-  const float t = at - as;
-  jsd_r_direct(t * kLn2, t, beta, r, dmr);
-  return as == at ? 0.f : -(1.f - beta) * Q * r;
-}
-
 // Pass 2 when pass 3 computes the loss (bf16, generalized branch): only the
 // cross-column sum G = sum_v g per (row, slice), into lg[.].y (lg[.].x = 0);
 // the loss, which needs the accurate small-t form of r, is summed in pass 3.
@@ -576,6 +632,7 @@ __global__ __launch_bounds__(kThreads) void jsd_gsum_kernel(JsdArgs a) {
   const float4 L = row_log_norms(a, row);
   const float k = a.k2;
   const float cg = -(1.f - a.beta) * kLn2;
+  const GenRow rw = gen_row(L, 0.f, 0.f);  // a_s, a_t as in jsd_loss_kernel
   float gsum = 0.f;
   for (int64_t v = v0 + threadIdx.x * 8; v < v1; v += kThreads * 8) {
     const int n = static_cast<int>(min<int64_t>(8, v1 - v));
@@ -585,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void jsd_gsum_kernel(JsdArgs a) {
     // Columns past the row end load as -inf in both rows: a tie, adding 0.
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
+      const float as = gen_as(ys[i], k, rw), at = gen_at(yt[i], k, rw);
       gsum = gsum_plain(gsum, as, at, hw_exp2(as), a.beta, cg);
     }
   }
@@ -675,8 +732,12 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
     }
   };
   float lsum[2] = {0.f, 0.f};
-  // The dZ of 8 logits of one row, and its loss terms into *ls.
-  auto elem8 = [&](const uint4& qs, const uint4& qt, const float4& L, float G, float& ls) {
+  constexpr bool kGen = MODE == kModeGeneralized;
+  const GenBeta gb = gen_beta(beta, a.grad_scale);
+  // The dZ of 8 logits of one row, and its loss terms into *ls (for the
+  // generalized branch, over ln 2).
+  auto elem8 = [&](const uint4& qs, const uint4& qt, const float4& L, float G, const GenRow& rw,
+                   float& ls) {
     const uint32_t ws[4] = {qs.x, qs.y, qs.z, qs.w};
     const uint32_t wt[4] = {qt.x, qt.y, qt.z, qt.w};
     float out[8];
@@ -684,19 +745,15 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
     for (int i = 0; i < 8; ++i) {
       const float zsv = (i & 1) ? bf16_hi(ws[i >> 1]) : bf16_lo(ws[i >> 1]);
       const float ztv = (i & 1) ? bf16_hi(wt[i >> 1]) : bf16_lo(wt[i >> 1]);
-      const float as = (zsv - L.x) * k - L.y, at = (ztv - L.z) * k - L.w;
-      float dA, l = 0.f;
-      if constexpr (LOSS && MODE == kModeGeneralized) {
-        float Q, r, dmr;
-        const float g = g_direct(as, at, beta, Q, r, dmr);
-        dA = g - Q * G;
-        l = as == at ? 0.f : beta * hw_exp2(at) * dmr - (1.f - beta) * Q * r;
+      float l = 0.f;
+      if constexpr (kGen) {
+        gen_terms(gen_as(zsv, k, rw), gen_at(ztv, k, rw), rw.nG, gb, out[i], l);
       } else {
+        const float as = (zsv - L.x) * k - L.y, at = (ztv - L.z) * k - L.w;
         float Q, P, g, gacc;
-        jsd_terms<MODE, true>(as, at, beta, Q, P, l, g, gacc);
-        dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+        jsd_terms<MODE>(as, at, beta, Q, P, l, g, gacc);
+        out[i] = ((MODE == kModeForwardKL) ? (Q - P) : (g - Q * G)) * a.grad_scale;
       }
-      out[i] = dA * a.grad_scale;
       if constexpr (LOSS) ls += l;
     }
     return make_uint4(pack_bf16x2(out[0], out[1]), pack_bf16x2(out[2], out[3]),
@@ -711,23 +768,25 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
     const int64_t off1 = off0 + 32 * a.ld;
     const float4 L0 = sh_L[rl0], L1 = sh_L[rl0 + 32];
     const float G0 = sh_G[rl0], G1 = sh_G[rl0 + 32];
+    const GenRow R0 = gen_row(L0, G0, a.grad_scale), R1 = gen_row(L1, G1, a.grad_scale);
     const int j = t % 8;
     uint16_t* d0 = dzt + (c_begin + rl0) * ldt + r0 + 8 * j;   // column c_begin + t/8
     uint16_t* d1 = d0 + 32 * ldt;                              // column c_begin + t/8 + 32
     const int ntile = static_cast<int>(span / 64);
-    uint4 s0 = ld_stream(zs + off0), s1 = ld_stream(zs + off1);
-    uint4 u0 = ld_stream(zt + off0), u1 = ld_stream(zt + off1);
-    for (int it = 0; it < ntile; ++it) {
+    // q = (student row 0, student row 1, teacher row 0, teacher row 1) of
+    // one tile. Two register sets alternate: the next tile's loads go to the
+    // set not being computed, so nothing is copied between them.
+    auto load_tile = [&](int it, uint4 (&q)[4]) {
       const int64_t c = static_cast<int64_t>(it) * 64;
-      uint4 ns0 = s0, ns1 = s1, nu0 = u0, nu1 = u1;
-      if (it + 1 < ntile) {
-        ns0 = ld_stream(zs + off0 + c + 64);
-        ns1 = ld_stream(zs + off1 + c + 64);
-        nu0 = ld_stream(zt + off0 + c + 64);
-        nu1 = ld_stream(zt + off1 + c + 64);
-      }
-      const uint4 p0 = elem8(s0, u0, L0, G0, lsum[0]);
-      const uint4 p1 = elem8(s1, u1, L1, G1, lsum[1]);
+      q[0] = ld_stream(zs + off0 + c);
+      q[1] = ld_stream(zs + off1 + c);
+      q[2] = ld_stream(zt + off0 + c);
+      q[3] = ld_stream(zt + off1 + c);
+    };
+    auto do_tile = [&](int it, const uint4 (&q)[4]) {
+      const int64_t c = static_cast<int64_t>(it) * 64;
+      const uint4 p0 = elem8(q[0], q[2], L0, G0, R0, lsum[0]);
+      const uint4 p1 = elem8(q[1], q[3], L1, G1, R1, lsum[1]);
       st_stream(gr + off0 + c, p0);
       st_stream(gr + off1 + c, p1);
       tile[it & 1][rl0][chunk ^ ((rl0 >> 3) & 7)] = p0;
@@ -747,10 +806,15 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
                   make_uint4(e[0] | (uint32_t(e[1]) << 16), e[2] | (uint32_t(e[3]) << 16),
                              e[4] | (uint32_t(e[5]) << 16), e[6] | (uint32_t(e[7]) << 16)));
       }
-      s0 = ns0;
-      s1 = ns1;
-      u0 = nu0;
-      u1 = nu1;
+    };
+    uint4 qa[4], qb[4];
+    load_tile(0, qa);
+    for (int it = 0; it < ntile; it += 2) {
+      if (it + 1 < ntile) load_tile(it + 1, qb);
+      do_tile(it, qa);
+      if (it + 1 >= ntile) break;
+      if (it + 2 < ntile) load_tile(it + 2, qa);
+      do_tile(it + 1, qb);
     }
   }
   uint4 cs[2], ct[2], ns[2], nt[2];
@@ -783,23 +847,20 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
           load8(zs + row * a.ld, v, n, a.vec_ok, ys);
           load8(zt + row * a.ld, v, n, a.vec_ok, yt);
         }
+        const GenRow rw = gen_row(L, G, a.grad_scale);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
-          float dA, l = 0.f;
-          if constexpr (LOSS && MODE == kModeGeneralized) {
-            float Q, r, dmr;
-            const float g = g_direct(as, at, beta, Q, r, dmr);
-            dA = g - Q * G;
-            const float P = hw_exp2(at);
-            l = as == at ? 0.f : beta * P * dmr - (1.f - beta) * Q * r;
+          float l = 0.f;
+          if constexpr (kGen) {
+            gen_terms(gen_as(ys[i], k, rw), gen_at(yt[i], k, rw), rw.nG, gb, out[i], l);
           } else {
+            const float as = (ys[i] - L.x) * k - L.y, at = (yt[i] - L.z) * k - L.w;
             float Q, P, g, gacc;
-            jsd_terms<MODE, true>(as, at, beta, Q, P, l, g, gacc);
-            dA = (MODE == kModeForwardKL) ? (Q - P) : (g - Q * G);
+            jsd_terms<MODE>(as, at, beta, Q, P, l, g, gacc);
+            out[i] = ((MODE == kModeForwardKL) ? (Q - P) : (g - Q * G)) * a.grad_scale;
           }
-          out[i] = dA * a.grad_scale;
-          // Columns past the row end load as -inf: no loss term.
+          // Columns past the row end load as -inf: no loss term (the
+          // generalized one is NaN there).
           if constexpr (LOSS) lsum[h] += i < n ? l : 0.f;
         }
         packed = pack8_bf16(out, n);
@@ -846,7 +907,7 @@ __global__ __launch_bounds__(kThreads) void jsd_grad_t_kernel(JsdArgs a, uint16_
     // per lane pattern, and write this workgroup's partial of each row.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float x = lsum[h];
+      float x = kGen ? lsum[h] * kLn2 : lsum[h];
       x += __shfl_xor(x, 1, 64);
       x += __shfl_xor(x, 2, 64);
       x += __shfl_xor(x, 4, 64);
