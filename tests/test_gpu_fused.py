@@ -140,6 +140,35 @@ def test_ties_self_distillation(fl):
     assert torch.count_nonzero(gW).item() == 0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta,T", [(0.5, 1.0), (0.1, 2.0), (0.0, 1.0), (1.0, 0.7)])
+def test_shifted_teacher_rows(fl, dtype, beta, T):
+    """Teacher logits equal to the student's plus a constant per row, exactly:
+    integer features and weights make every logit a small integer (exact in
+    bf16), and the teacher's extra feature column, against an all-ones weight
+    column, adds the row's constant (seven zero columns more keep H_t a whole
+    number of 16-byte vectors). The softmax ignores a shift of its row,
+    so the two distributions are equal element by element (exact ties, PR
+    #1374) and the loss and every gradient element are exactly 0, across
+    several vocabulary tiles and the merge of their row statistics."""
+    rng = np.random.default_rng(41)
+    BT, H, V = 300, 64, 1000
+    X_s = rng.integers(-1, 2, size=(BT, H)).astype(np.float32)
+    W_s = rng.integers(-1, 2, size=(V, H)).astype(np.float32)
+    shift = rng.integers(-60, 61, size=(BT, 1)).astype(np.float32)
+    X_t = np.concatenate([X_s, shift, np.zeros((BT, 7), np.float32)], axis=1)
+    W_t = np.concatenate([W_s, np.ones((V, 1), np.float32), np.zeros((V, 7), np.float32)], axis=1)
+    arrays = (X_s, W_s, X_t, W_t)
+    if dtype == "bf16":  # small integers: the fp32 pattern's top half is exact
+        arrays = tuple((a.view(np.uint32) >> 16).astype(np.uint16) for a in arrays)
+    dev = tuple(to_device(a, dtype) for a in arrays)
+    for reduction, nc in (("batchmean", 1), ("sum", 3), ("none", 2)):
+        loss, gX, gW = _run(fl, dev, beta, T, reduction, nc)
+        assert np.all(from_device(loss) == 0.0), f"{reduction} nc={nc}"
+        assert torch.count_nonzero(gX).item() == 0, f"{reduction} nc={nc}"
+        assert torch.count_nonzero(gW).item() == 0, f"{reduction} nc={nc}"
+
+
 def test_ties_padded_vocabulary(fl):
     """Padded vocabulary rows carry zero mass in both models: their grad_W rows
     are exactly 0, and everything else matches the oracle."""
