@@ -115,11 +115,14 @@ __device__ inline int swz(int r, int c) {
 // A lane's value after a DPP move within its 16-lane row (gfx9 encodings):
 // quad_perm [1,0,3,2] and [2,3,0,1] exchange with lane ^ 1 and lane ^ 2,
 // row_half_mirror pairs lane i with 7 - i in each group of eight, row_mirror
-// i with 15 - i in the row.
+// i with 15 - i in the row. Each reads a lane of the same row, so no lane is
+// out of range and bound_ctrl changes nothing; with it the move needs no old
+// value (no zeroed register before each move, and adds fuse into
+// v_add_f32_dpp).
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 template <int CTRL>
 __device__ inline float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Max and sum over a 32-lane half-wave, as butterflies: after each step both
@@ -680,8 +683,8 @@ struct GemmKernel {
   // lane's four consecutive columns in the transposed accumulator layout),
   // quad slot s of row r at s ^ (r % 16) so that the 16 rows a write
   // instruction covers land in distinct banks. Then each 32-lane
-  // half-wave reads one 512-byte row back in 16-byte chunks and stores it to
-  // C with 16-byte writes. STATS: the same half-wave reduces the row's
+  // half-wave reads one 512-byte row back, a 16-byte chunk per lane from its
+  // two quads' slots, and stores it to C with 16-byte writes. STATS: the same half-wave reduces the row's
   // rounded values to (max, sum 2^((z - max) k)) over the tile's valid
   // columns and writes them as the row's partial for N-tile tn.
   template <bool STATS>
@@ -724,10 +727,13 @@ struct GemmKernel {
         uint4 v[kRowsAtOnce];
 #pragma unroll
         for (int u = 0; u < kRowsAtOnce; ++u) {
+          // The chunk's two quads, each from its own slot (no swap to undo
+          // where the row's XOR is odd).
           const int row = row0 + u * kRowStep;
           const int f = row & 15;
-          v[u] = lds[row * CPR16 + (c ^ (f >> 1))];
-          if (f & 1) v[u] = make_uint4(v[u].z, v[u].w, v[u].x, v[u].y);
+          const uint2 lo = quads[row * QPR + ((2 * c) ^ f)];
+          const uint2 hi = quads[row * QPR + ((2 * c + 1) ^ f)];
+          v[u] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
         // Non-temporal: the logits are read next by the loss passes, not by
         // this product (pass 2 0.71 -> 0.645 ms, logits -0.05 ms).
@@ -766,8 +772,9 @@ struct GemmKernel {
     }
     for (int row = threadIdx.x >> 5; row < BM; row += kRowStep) {
       const int f = row & 15;
-      uint4 v = lds[row * CPR16 + (c ^ (f >> 1))];
-      if (f & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+      const uint2 lo = quads[row * QPR + ((2 * c) ^ f)];
+      const uint2 hi = quads[row * QPR + ((2 * c + 1) ^ f)];
+      const uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
       const int64_t m = m0 + row;
       if (m < g.M && n < g.N) {
         uint16_t* dst = C + m * g.ldc + n;
