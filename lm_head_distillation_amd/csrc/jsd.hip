@@ -124,11 +124,15 @@ __device__ inline float gsum_plain(float gsum, float as, float at, float Q, floa
 //    generating function of a Bernoulli(beta) variable, so the coefficient of
 //    D^n / n! is its n-th cumulant; truncation below 1.3e-7 relative there),
 //    which keeps a small r accurate relative to itself;
-//  - beyond, log2(beta 2^t + 1 - beta), 2^t taken at min(t, 64) and the rest
-//    of t added back (past 64 the 1 - beta term is below 2^-64 of the
-//    other); both terms are positive, so nothing cancels.
-// dmr2 = t - r2 = (D - r) / ln 2. A tie (t == 0, finite logits) takes the
-// series branch and gives r2 = dmr2 = 0, so both terms vanish with no select;
+//  - beyond, with e = 2^-|t| and L = log2 of two positive terms: for t < 0,
+//    r2 = L = log2(beta e + 1 - beta) and dmr2 = t - L; for t > 0,
+//    L = log2((1 - beta) e + beta), r2 = t + L and dmr2 = -L. Nothing
+//    overflows, and the smaller of r2 and dmr2 on each side never comes from
+//    a difference (with t large and beta near 1, t - r2 would leave
+//    -log2 beta ~ 1e-3 to the rounding of t).
+// dmr2 = (D - r) / ln 2 (t - r2 below 1/16). A tie (t == 0, finite logits)
+// takes the series branch and gives r2 = dmr2 = 0, so both terms vanish with
+// no select;
 // masked columns (-inf in both rows) give NaN and the callers leave them out.
 // Outputs: dz = grad_scale (g - Q G) with g = -(1 - beta) Q r, from
 // nG = -G grad_scale and cg = -(1 - beta) ln 2 grad_scale; and the loss
@@ -165,15 +169,17 @@ __device__ inline void gen_terms(float as, float at, float nG, const GenBeta& c,
                                  float& l2) {
   const float Q = hw_exp2(as), P = hw_exp2(at);
   const float t = at - as;
-  const float tc = fminf(t, 64.f);
-  const float rl = hw_log2(fmaf(c.beta, hw_exp2(tc), c.cb)) + (t - tc);
+  const bool neg = t < 0.f;
+  const float e = hw_exp2(-fabsf(t));
+  const float L = hw_log2(neg ? fmaf(c.beta, e, c.cb) : fmaf(c.cb, e, c.beta));
   float p = fmaf(c.c4, t, c.c3);
   p = fmaf(p, t, c.c2);
   p = fmaf(p, t, c.beta);
   const float rs = p * t;
   // Both branches evaluated, then selected (no divergent branch per element).
-  const float r2 = fabsf(t) < kGenSmallT ? rs : rl;
-  const float dmr2 = t - r2;
+  const bool small = fabsf(t) < kGenSmallT;
+  const float r2 = small ? rs : (neg ? L : t + L);
+  const float dmr2 = small ? t - rs : (neg ? t - L : -L);
   const float Qr = Q * r2;
   l2 = fmaf(c.beta * P, dmr2, -c.cb * Qr);
   dz = fmaf(Q, nG, c.cg * Qr);

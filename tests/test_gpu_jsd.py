@@ -197,3 +197,46 @@ def test_near_ties_bf16(fl, ulps, beta, T):
     assert rel <= 2e-4
     tol = dict(TIGHT["bf16"], elem_max=1e-3)
     assert_tensor_close(from_device(grad), ref_grad, tol, "grad")
+
+
+@pytest.mark.parametrize("beta", [0.001, 0.5, 0.999])
+@pytest.mark.parametrize("T,scale", [(0.25, 30.0), (20.0, 0.5)])
+def test_generalized_bf16_far_and_series(fl, beta, T, scale):
+    """The two forms of the bf16 generalized terms at their ends.
+
+    T = 20, logits of std 0.5: nearly every |D| is below 1/16, so nearly every
+    element takes the degree-4 series, with beta near 0 and 1 stressing its
+    cumulant coefficients. The row losses (~6e-7) are sums of second-order
+    terms, each the difference of two first-order ones, so the fp32 rounding
+    of every log2 probability (~1e-6 absolute at -13.5) reaches them at
+    ~1e-3 relative (fp32 emulation: 1.6e-3 at most, with or without an exact
+    normaliser): the loss bound is 5e-3; the gradient elements, differences
+    g - Q G of first-order terms, take the near-tie bounds.
+
+    T = 0.25, logits of std 30: most log2-probability differences pass 64,
+    where 2^t is taken at 64 and the rest of t added back, and the two
+    distributions are nearly disjoint one-hot rows. The loss then sits at the
+    binary entropy h(beta) and is held to the loss-step bound. The gradient of
+    such rows vanishes: its elements are ~1e-17 of their natural scale
+    1 / (BT T), and g - Q G, two terms of ~1e-3 Q that cancel, leaves fp32
+    noise far above that (the fp32 logit path keeps its terms relative to the
+    student's most probable element; the bf16 one does not). There the bound
+    is absolute, 1e-6 of the natural scale."""
+    BT, V = 48, 12000
+    zs, _ = _logits(61, BT, V, scale, "bf16")
+    zt, _ = _logits(62, BT, V, scale, "bf16")
+    for red in ("batchmean", "none"):
+        loss, grad, _ = _run(fl, zs, zt, V, "bf16", beta, T, red)
+        ref_loss, ref_grad = oracle.generalized_jsd(to_f64(zs, "bf16"), to_f64(zt, "bf16"), beta, T,
+                                                    red)
+        got = from_device(grad)
+        if T < 1.0:
+            assert_loss_close(from_device(loss), ref_loss, dict(TIGHT["bf16"], loss_rel=1e-4))
+            natural = (1.0 / BT if red == "batchmean" else 1.0) / T
+            err = np.max(np.abs(got - ref_grad)) / natural
+            print(f"{red}: max |dZ - ref| = {err:.2e} of 1/(BT T)", flush=True)
+            assert err <= 1e-6
+        else:
+            tol = dict(TIGHT["bf16"], loss_rel=5e-3, elem_max=1e-3)
+            assert_loss_close(from_device(loss), ref_loss, tol)
+            assert_tensor_close(got, ref_grad, tol, "grad")
