@@ -129,7 +129,10 @@ __device__ inline float gsum_plain(float gsum, float as, float at, float Q, floa
 //    L = log2((1 - beta) e + beta), r2 = t + L and dmr2 = -L. Nothing
 //    overflows, and the smaller of r2 and dmr2 on each side never comes from
 //    a difference (with t large and beta near 1, t - r2 would leave
-//    -log2 beta ~ 1e-3 to the rounding of t).
+//    -log2 beta ~ 1e-3 to the rounding of t). The argument is written
+//    1 - c (1 - e), c the weight on e's side, so that it is exactly 1 at
+//    e = 1: beta + (1 - beta) is not 1 in fp32 for most beta, and that bias,
+//    the same sign at every element, reached 1e-3 of near-uniform row losses.
 // dmr2 = (D - r) / ln 2 (t - r2 below 1/16). A tie (t == 0, finite logits)
 // takes the series branch and gives r2 = dmr2 = 0, so both terms vanish with
 // no select;
@@ -171,7 +174,7 @@ __device__ inline void gen_terms(float as, float at, float nG, const GenBeta& c,
   const float t = at - as;
   const bool neg = t < 0.f;
   const float e = hw_exp2(-fabsf(t));
-  const float L = hw_log2(neg ? fmaf(c.beta, e, c.cb) : fmaf(c.cb, e, c.beta));
+  const float L = hw_log2(fmaf(-(neg ? c.beta : c.cb), 1.f - e, 1.f));
   float p = fmaf(c.c4, t, c.c3);
   p = fmaf(p, t, c.c2);
   p = fmaf(p, t, c.beta);

@@ -207,11 +207,12 @@ def test_generalized_bf16_far_and_series(fl, beta, T, scale):
     T = 20, logits of std 0.5: nearly every |D| is below 1/16, so nearly every
     element takes the degree-4 series, with beta near 0 and 1 stressing its
     cumulant coefficients. The row losses (~6e-7) are sums of second-order
-    terms, each the difference of two first-order ones, so the fp32 rounding
-    of every log2 probability (~1e-6 absolute at -13.5) reaches them at
-    ~1e-3 relative (fp32 emulation: 1.6e-3 at most, with or without an exact
-    normaliser): the loss bound is 5e-3; the gradient elements, differences
-    g - Q G of first-order terms, take the near-tie bounds.
+    terms, each the difference of two first-order ones. At beta near 0 or 1
+    the elements past |D| = 1/16 take log2 of an argument within ~1e-4 of 1
+    on the side of the small weight, whose fp32 rounding costs that log up to
+    ~1e-3 relative, and those errors reach the row loss undiminished (fp32
+    emulation: 9e-4 at most): the loss bound is 5e-3. The gradient elements,
+    differences g - Q G of first-order terms, take the near-tie bounds.
 
     T = 0.25, logits of std 30: most log2-probability differences pass 64,
     where 2^t is taken at 64 and the rest of t added back, and the two
