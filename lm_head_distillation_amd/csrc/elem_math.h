@@ -219,7 +219,10 @@ __device__ inline BetaWeights beta_weights(float beta) {
 // t = D / ln 2. Away from D = 0, r = ln u + max(D, 0) with
 // u = c e^(-|D|) + 1 - c (c = beta for D < 0, else 1 - beta): u lies in
 // [min(beta, 1 - beta), 1], so nothing overflows, and rounding u costs r an
-// absolute ~4e-8. Near D = 0, where that would be a large relative error of a
+// absolute ~4e-8. u is evaluated as 1 - c (1 - e^(-|D|)), exactly 1 at
+// D = 0 whatever the rounding of 1 - beta (beta + (1 - beta) is not 1 in
+// fp32 for most beta, a bias of the same sign at every element otherwise).
+// Near D = 0, where rounding u would be a large relative error of a
 // small r, r is r(D)'s Taylor series instead: r is the cumulant generating
 // function of a Bernoulli(beta) variable, so the coefficient of D^n / n! is
 // that variable's n-th cumulant. The series runs to degree 4 below |D| = 1/16
@@ -227,7 +230,7 @@ __device__ inline BetaWeights beta_weights(float beta) {
 __device__ inline void jsd_r_direct(float D, float t, float beta, float& r, float& dmr) {
   const bool neg = D < 0.f;
   const float e = hw_exp2(-fabsf(t));
-  const float L1 = hw_log2(neg ? fmaf(beta, e, 1.f - beta) : fmaf(1.f - beta, e, beta)) * kLn2;
+  const float L1 = hw_log2(fmaf(-(neg ? beta : 1.f - beta), 1.f - e, 1.f)) * kLn2;
   const float v = beta * (1.f - beta);  // the Bernoulli variance
   float p = v * (1.f - 6.f * v) * (1.f / 24.f);
   p = fmaf(p, D, v * (1.f - 2.f * beta) * (1.f / 6.f));
