@@ -118,8 +118,8 @@ __device__ inline float gsum_plain(float gsum, float as, float at, float Q, floa
 // bf16 logits, generalized branch: the terms of one element, shared by every
 // pass that evaluates them (pass 2's loss, pass 3's dZ with or without the
 // transposed copy, pass 3's loss), so that no result depends on which
-// outputs were asked for. In base 2,
-// with t = a_t - a_s = D / ln 2, r2 = r / ln 2 for r = ln(beta e^D + 1 - beta):
+// outputs were asked for. In base 2, with t = a_t - a_s = D / ln 2,
+// r2 = r / ln 2 for r = ln(beta e^D + 1 - beta):
 //  - below |D| = 1/16, r's Taylor series to degree 4 (r is the cumulant
 //    generating function of a Bernoulli(beta) variable, so the coefficient of
 //    D^n / n! is its n-th cumulant; truncation below 1.3e-7 relative there),
@@ -135,8 +135,8 @@ __device__ inline float gsum_plain(float gsum, float as, float at, float Q, floa
 //    the same sign at every element, reached 1e-3 of near-uniform row losses.
 // dmr2 = (D - r) / ln 2 (t - r2 below 1/16). A tie (t == 0, finite logits)
 // takes the series branch and gives r2 = dmr2 = 0, so both terms vanish with
-// no select;
-// masked columns (-inf in both rows) give NaN and the callers leave them out.
+// no select; masked columns (-inf in both rows) give NaN and the callers
+// leave them out.
 // Outputs: dz = grad_scale (g - Q G) with g = -(1 - beta) Q r, from
 // nG = -G grad_scale and cg = -(1 - beta) ln 2 grad_scale; and the loss
 // term over ln 2, l2 = (beta P (D - r) - (1 - beta) Q r) / ln 2.
