@@ -288,17 +288,27 @@ def flce_sweep(fljsd, steps, warmup):
         for _ in range(warmup):
             step()
         torch.cuda.synchronize()
+        fljsd.fljsd_profile_enable(True)
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
+        kernels = fljsd.fljsd_profile_read()
+        fljsd.fljsd_profile_enable(False)
+        floor, hbm, mfma = pass_floor(kernels, steps)
         rec = {"BT": BT, "num_chunks": nc, "ms_per_step": round(ms, 3),
                "tokens_per_s": round(BT / ms * 1e3, 1),
                "peak_hbm_mb": round(torch.cuda.max_memory_allocated() / 2**20, 1),
+               "floor_ms": round(floor, 3), "bound": "hbm" if hbm > mfma else "mfma",
+               "roofline_frac": round(floor / ms, 4),
+               "kernel_ms_per_step": {c: round(k["ms"] / steps, 3) for c, k in kernels.items()
+                                      if k["launches"]},
                "pages_h100_ms": PAGES_FLCE_MS[BT]}
         log(f"  flce BT={BT:5d} nc={nc}: {ms:7.2f} ms/step  {rec['tokens_per_s']:>10,.0f} tokens/s  "
-            f"peak {rec['peak_hbm_mb']:.0f} MB  (pages, H100: {PAGES_FLCE_MS[BT]} ms)")
+            f"peak {rec['peak_hbm_mb']:.0f} MB  floor {floor:.2f} ms ({rec['bound']}, "
+            f"{100 * floor / ms:.0f}%)  (pages, H100: {PAGES_FLCE_MS[BT]} ms)  " +
+            " ".join(f"{c}={v:.2f}" for c, v in rec["kernel_ms_per_step"].items()))
         out.append(rec)
         del X, ws, labels
         torch.cuda.empty_cache()
